@@ -1,0 +1,401 @@
+// Index build on the GPU: the KV-outer CSR index of types.rs (alice-llm
+// 2.0.0, KvOuterIndex field docs) plus the work units that the forward walks.
+//
+//   k_index_init     zero the per-slot counters, reset the header, check cu_seqlens
+//   k_index_hist     one thread per (q, h, r): drop padding / past-lk ranks,
+//                    flag ids outside [-1, msb), count edges per (h, raw slot)
+//   k_index_scan     one workgroup per head: exclusive scans of the counts,
+//                    compaction of nonempty slots, plateaued offsets, unit
+//                    counts per slot, page-id check of touched pages
+//   k_index_scatter  one thread per kept (q, h, r): atomic cursor per slot,
+//                    key q*topk + r into the slot's segment (unordered)
+//   k_index_rank     per compact slot: rank of each key inside the segment
+//                    (keys are unique) -> edges and inv in (q, r) order, then
+//                    the slot's work units; workgroup 0 fills the header
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 4;
+
+__device__ inline int4 add4(int4 a, int4 b) {
+  return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ inline int4 sub4(int4 a, int4 b) {
+  return make_int4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+}
+
+__device__ inline int4 wave_incl_scan4(int4 v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int4 t;
+    t.x = __shfl_up(v.x, off, 64);
+    t.y = __shfl_up(v.y, off, 64);
+    t.z = __shfl_up(v.z, off, 64);
+    t.w = __shfl_up(v.w, off, 64);
+    if (lane >= off) v = add4(v, t);
+  }
+  return v;
+}
+
+// Units of a slot with c edges: k = ceil(c / cap) near-equal parts. Part i
+// spans [floor(i*c/k), floor((i+1)*c/k)), so sizes are floor(c/k) or one
+// more. A part goes to the MFMA kernel iff its size is at least thr_e.
+__device__ inline void unit_split(int c, int cap, int thr_e, int* n_wave, int* n_mfma) {
+  if (c <= 0) { *n_wave = 0; *n_mfma = 0; return; }
+  const int k = (c + cap - 1) / cap;
+  const int lo = c / k;
+  const int n_hi = c % k;
+  if (lo >= thr_e) { *n_wave = 0; *n_mfma = k; }
+  else if (lo + 1 >= thr_e) { *n_wave = k - n_hi; *n_mfma = n_hi; }
+  else { *n_wave = k; *n_mfma = 0; }
+}
+
+__global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
+  const int64_t n = (int64_t)A.hkv * A.nbs;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    P.cnt[i] = 0;
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x == 0) {
+    DevHeader* h = P.hdr;
+    h->err_key = ~0ull;
+    h->status = 0;
+    h->what_code = kWhatNone;
+    h->err_expected = 0;
+    h->err_got = 0;
+    h->total_edges = 0;
+    h->num_units_wave = 0;
+    h->num_units_mfma = 0;
+    h->num_slots = 0;
+    h->queue_mfma = 0;
+    h->done_mfma = 0;
+    h->queue_wave = 0;
+    h->done_wave = 0;
+    h->geom[0] = (int32_t)A.tq;
+    h->geom[1] = A.hkv;
+    h->geom[2] = A.topk;
+    h->geom[3] = A.batch;
+    h->geom[4] = A.max_pages;
+    h->geom[5] = A.block_size;
+    h->geom[6] = A.page_size;
+    h->geom[7] = A.qhead;
+  }
+  __syncthreads();
+  // cu_seqlens content (types.rs CuSeqlensQ::new): cu[0] == 0, non-decreasing.
+  for (int32_t b = threadIdx.x; b < A.batch; b += 256)
+    if (A.cu[b + 1] < A.cu[b]) atomicMin(&P.hdr->err_key, err_key(kRankCuContent, b + 1));
+  if (threadIdx.x == 0) {
+    if (A.cu[0] != 0) atomicMin(&P.hdr->err_key, err_key(kRankCuContent, 0));
+    if (A.cu[A.batch] != A.tq) atomicMin(&P.hdr->err_key, err_key(kRankCuTotal, 0));
+  }
+}
+
+// Thread per entry of `selected`, in memory order idx = (q*hkv + h)*topk + r.
+__global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
+  const int64_t total = A.tq * A.hkv * A.topk;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int32_t r = (int32_t)(idx % A.topk);
+  const int64_t qh = idx / A.topk;
+  const int32_t h = (int32_t)(qh % A.hkv);
+  const int64_t q = qh / A.hkv;
+  const int32_t v = A.selected[idx];
+  P.inv[((int64_t)h * A.tq + q) * A.topk + r] = -1;
+  if (v == -1) return;
+  if (v < -1 || v >= A.msb) {
+    atomicMin(&P.hdr->err_key, err_key(kRankSelected, (uint64_t)idx));
+    return;
+  }
+  const int32_t b = batch_of_dev(A.cu, A.batch, q);
+  const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
+  if ((int64_t)v * A.block_size >= lk) return;
+  atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_index_scan(IndexPtrs P, BuildArgs A) {
+  const int32_t h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ int4 s_wave[kScanThreads / 64];
+  __shared__ int4 s_carry;
+  if (tid == 0) s_carry = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  const int64_t nbs = A.nbs;
+  int32_t* cnt = P.cnt + (int64_t)h * nbs;
+  const int cap = A.cap_edges;
+  const int thr_e = (int)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
+  for (int64_t base = 0; base < nbs; base += kScanThreads * kScanItems) {
+    int c[kScanItems], nw[kScanItems], nm[kScanItems];
+    int4 mine = make_int4(0, 0, 0, 0);    // edges, nonempty slots, wave units, mfma units
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int64_t raw = base + (int64_t)tid * kScanItems + k;
+      c[k] = raw < nbs ? cnt[raw] : 0;
+      unit_split(c[k], cap, thr_e, &nw[k], &nm[k]);
+      mine = add4(mine, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
+    }
+    const int4 incl = wave_incl_scan4(mine);
+    if (lane == 63) s_wave[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+      int4 w = lane < kScanThreads / 64 ? s_wave[lane] : make_int4(0, 0, 0, 0);
+      w = wave_incl_scan4(w);
+      if (lane < kScanThreads / 64) s_wave[lane] = w;
+    }
+    __syncthreads();
+    const int4 carry = s_carry;
+    int4 run = add4(carry, sub4(incl, mine));
+    if (wid > 0) run = add4(run, s_wave[wid - 1]);
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int64_t raw = base + (int64_t)tid * kScanItems + k;
+      if (c[k] > 0) {
+        const int64_t j = run.y;
+        P.sel_slots[(int64_t)h * nbs + j] = (int32_t)raw;
+        P.sel_offsets[(int64_t)h * (nbs + 1) + j] = run.x;
+        P.slot_uw[(int64_t)h * nbs + j] = run.z;
+        P.slot_um[(int64_t)h * nbs + j] = run.w;
+        cnt[raw] = run.x;                               // scatter cursor
+        if (A.num_pages >= 0) {
+          // Pages that the kept block's valid range touches (the forward's
+          // "block_tables page id" check, moved into the build).
+          const int32_t b = (int32_t)(raw / A.msb), blk = (int32_t)(raw % A.msb);
+          const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
+          int64_t block_end = (int64_t)(blk + 1) * A.block_size;
+          block_end = block_end < lk ? block_end : lk;
+          for (int32_t pl = 0; pl < A.ppb; ++pl) {
+            if ((int64_t)blk * A.block_size + (int64_t)pl * A.page_size >= block_end) break;
+            const int64_t col = (int64_t)b * A.max_pages + (int64_t)blk * A.ppb + pl;
+            if (A.block_tables[col] >= A.num_pages)
+              atomicMin(&P.hdr->err_key, err_key(kRankPage, (uint64_t)col));
+          }
+        }
+      }
+      run = add4(run, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
+    }
+    __syncthreads();
+    if (tid == 0) s_carry = add4(carry, s_wave[kScanThreads / 64 - 1]);
+    __syncthreads();
+  }
+  const int4 tot = s_carry;
+  if (tid == 0) {
+    P.num_sel[h] = tot.y;
+    P.head_e[h] = tot.x;
+    P.head_uw[h] = tot.z;
+    P.head_um[h] = tot.w;
+  }
+  for (int64_t j = tot.y + tid; j < nbs; j += kScanThreads) P.sel_slots[(int64_t)h * nbs + j] = -1;
+  for (int64_t j = tot.y + tid; j <= nbs; j += kScanThreads)
+    P.sel_offsets[(int64_t)h * (nbs + 1) + j] = tot.x;
+}
+
+__device__ inline int64_t head_edge_base(const IndexPtrs& P, int32_t h) {
+  int64_t s = 0;
+  for (int32_t i = 0; i < h; ++i) s += P.head_e[i];
+  return s;
+}
+
+__global__ __launch_bounds__(256) void k_index_scatter(IndexPtrs P, BuildArgs A) {
+  const int64_t total = A.tq * A.hkv * A.topk;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int32_t v = A.selected[idx];
+  if (v < 0 || v >= A.msb) return;
+  const int32_t r = (int32_t)(idx % A.topk);
+  const int64_t qh = idx / A.topk;
+  const int32_t h = (int32_t)(qh % A.hkv);
+  const int64_t q = qh / A.hkv;
+  const int32_t b = batch_of_dev(A.cu, A.batch, q);
+  const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
+  if ((int64_t)v * A.block_size >= lk) return;
+  const int32_t pos = atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
+  P.keys[head_edge_base(P, h) + pos] = (int32_t)(q * A.topk + r);
+}
+
+__device__ void finalize_header(const IndexPtrs& P, const BuildArgs& A) {
+  int64_t e = 0, ns = 0;
+  int32_t uw = 0, um = 0;
+  for (int32_t h = 0; h < A.hkv; ++h) {
+    P.edge_head_base[h] = e;
+    e += P.head_e[h];
+    uw += P.head_uw[h];
+    um += P.head_um[h];
+    ns += P.num_sel[h];
+  }
+  P.edge_head_base[A.hkv] = e;
+  DevHeader* hd = P.hdr;
+  hd->total_edges = e;
+  hd->num_units_wave = uw;
+  hd->num_units_mfma = um;
+  hd->num_slots = ns;
+  const unsigned long long key = hd->err_key;
+  if (key == ~0ull) { hd->status = SA_OK; return; }
+  const uint64_t rank = key >> 56;
+  const int64_t pos = (int64_t)(key & ((1ull << 56) - 1));
+  if (rank == kRankCuContent) {
+    hd->status = SA_ERR_CU_SEQLENS;
+  } else if (rank == kRankCuTotal) {
+    hd->status = SA_ERR_SHAPE;
+    hd->what_code = kWhatCuTotal;
+    hd->err_expected = A.tq;
+    hd->err_got = A.cu[A.batch];
+  } else if (rank == kRankSelected) {
+    hd->status = SA_ERR_SELECTED_RANGE;
+    hd->err_expected = A.msb;
+    hd->err_got = A.selected[pos];
+  } else {
+    hd->status = SA_ERR_SHAPE;
+    hd->what_code = kWhatPageId;
+    hd->err_expected = A.num_pages;
+    hd->err_got = A.block_tables[pos];
+  }
+}
+
+constexpr int kRankChunk = 2048;   // keys staged in LDS per pass
+constexpr int kRankKeys = 4;       // keys held per thread per pass
+
+__device__ inline void write_edge(const IndexPtrs& P, const BuildArgs& A, int32_t h,
+                                  int64_t head_base, int32_t off0, int32_t key, int32_t rank) {
+  const int32_t q = key / A.topk, r = key % A.topk;
+  const int64_t e = head_base + off0 + rank;
+  P.edges[2 * e] = q;
+  P.edges[2 * e + 1] = r;
+  P.inv[((int64_t)h * A.tq + q) * A.topk + r] = off0 + rank;
+}
+
+// Each workgroup owns 4 consecutive compact-slot ids g = 4*blockIdx + wave
+// over all heads (h = g / nbs, j = g % nbs). Slots with <= 64 keys are ranked
+// by their wave with lane shuffles. If any of the 4 has more, the whole
+// workgroup ranks them one after another through LDS.
+__global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) finalize_header(P, A);
+  if (A.nbs == 0) return;                          // no slots at all (msb == 0)
+  __shared__ int32_t s_n[4], s_h[4], s_j[4], s_off[4];
+  __shared__ int64_t s_base[4];
+  __shared__ __align__(16) int32_t s_keys[kRankChunk];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t g = (int64_t)blockIdx.x * 4 + w;
+  if (lane == 0) {
+    const int32_t h = (int32_t)(g / A.nbs);
+    const int64_t j = g % A.nbs;
+    int32_t n = 0, off0 = 0;
+    int64_t hb = 0;
+    if (h < A.hkv && j < P.num_sel[h]) {
+      off0 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j];
+      n = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j + 1] - off0;
+      hb = head_edge_base(P, h);
+    }
+    s_n[w] = n;
+    s_h[w] = h;
+    s_j[w] = (int32_t)j;
+    s_off[w] = off0;
+    s_base[w] = hb;
+  }
+  __syncthreads();
+  const bool block_mode = s_n[0] > 64 || s_n[1] > 64 || s_n[2] > 64 || s_n[3] > 64;
+  if (!block_mode) {
+    const int32_t n = s_n[w];
+    if (n > 0) {
+      const int32_t* seg = P.keys + s_base[w] + s_off[w];
+      const int32_t key = lane < n ? seg[lane] : INT32_MAX;
+      int32_t rank = 0;
+      for (int32_t x = 0; x < n; ++x) rank += __shfl(key, x, 64) < key;
+      if (lane < n) write_edge(P, A, s_h[w], s_base[w], s_off[w], key, rank);
+    }
+  } else {
+    for (int s = 0; s < 4; ++s) {
+      const int32_t n = s_n[s];
+      if (n == 0) continue;
+      const int32_t* seg = P.keys + s_base[s] + s_off[s];
+      for (int32_t pass = 0; pass < n; pass += 256 * kRankKeys) {
+        int32_t mine[kRankKeys], rank[kRankKeys];
+#pragma unroll
+        for (int k = 0; k < kRankKeys; ++k) {
+          const int32_t i = pass + tid + 256 * k;
+          mine[k] = i < n ? seg[i] : INT32_MAX;
+          rank[k] = 0;
+        }
+        for (int32_t c0 = 0; c0 < n; c0 += kRankChunk) {
+          const int32_t m = n - c0 < kRankChunk ? n - c0 : kRankChunk;
+          const int32_t m4 = (m + 3) & ~3;
+          __syncthreads();
+          for (int32_t x = tid; x < m4; x += 256) s_keys[x] = x < m ? seg[c0 + x] : INT32_MAX;
+          __syncthreads();
+          for (int32_t x = 0; x < m4; x += 4) {
+            const int4 kk = *reinterpret_cast<const int4*>(&s_keys[x]);
+#pragma unroll
+            for (int k = 0; k < kRankKeys; ++k)
+              rank[k] += (kk.x < mine[k]) + (kk.y < mine[k]) + (kk.z < mine[k]) + (kk.w < mine[k]);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kRankKeys; ++k) {
+          const int32_t i = pass + tid + 256 * k;
+          if (i < n) write_edge(P, A, s_h[s], s_base[s], s_off[s], mine[k], rank[k]);
+        }
+      }
+    }
+  }
+  // Work units of this wave's slot, in CSR order within each kind.
+  const int32_t n = s_n[w];
+  if (n == 0) return;
+  const int32_t h = s_h[w], j = s_j[w];
+  const int32_t cap = A.cap_edges;
+  const int32_t thr_e = (int32_t)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
+  const int32_t k_units = (n + cap - 1) / cap;
+  int32_t uw = P.slot_uw[(int64_t)h * A.nbs + j], um = P.slot_um[(int64_t)h * A.nbs + j];
+  for (int32_t i = 0; i < h; ++i) {
+    uw += P.head_uw[i];
+    um += P.head_um[i];
+  }
+  const int64_t e_base = s_base[w] + s_off[w];
+  for (int32_t i0 = 0; i0 < k_units; i0 += 64) {
+    const int32_t i = i0 + lane;
+    const bool active = i < k_units;
+    int32_t s0 = 0, s1 = 0;
+    if (active) {
+      s0 = (int32_t)(((int64_t)i * n) / k_units);
+      s1 = (int32_t)(((int64_t)(i + 1) * n) / k_units);
+    }
+    const bool is_m = active && (s1 - s0) >= thr_e;
+    const bool is_w = active && !is_m;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t bm = __ballot(is_m), bw = __ballot(is_w);
+    if (is_m)
+      P.units_mfma[um + __popcll(bm & below)] =
+          make_int4(h, j, (int32_t)(e_base + s0), (int32_t)(e_base + s1));
+    if (is_w)
+      P.units_wave[uw + __popcll(bw & below)] =
+          make_int4(h, j, (int32_t)(e_base + s0), (int32_t)(e_base + s1));
+    um += __popcll(bm);
+    uw += __popcll(bw);
+  }
+}
+
+inline unsigned grid_for(int64_t n, int per) {
+  int64_t g = (n + per - 1) / per;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) {
+  const IndexPtrs P = index_ptrs(idx);
+  const int64_t slots = (int64_t)a.hkv * a.nbs;
+  int64_t init_grid = (slots + 255) / 256;
+  if (init_grid > 2048) init_grid = 2048;
+  if (init_grid < 1) init_grid = 1;
+  hipLaunchKernelGGL(k_index_init, dim3((unsigned)init_grid), dim3(256), 0, s, P, a);
+  const int64_t entries = a.tq * a.hkv * a.topk;
+  hipLaunchKernelGGL(k_index_hist, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
+  hipLaunchKernelGGL(k_index_scan, dim3((unsigned)a.hkv), dim3(kScanThreads), 0, s, P, a);
+  hipLaunchKernelGGL(k_index_scatter, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
+  hipLaunchKernelGGL(k_index_rank, dim3(grid_for(slots, 4)), dim3(256), 0, s, P, a);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,166 @@
+// Internal definitions shared by the library's translation units (not part
+// of the public ABI): the device-side index header, kernel argument packs,
+// tuning constants and launcher prototypes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sa.h"
+
+namespace sa {
+
+// ---------------------------------------------------------------- tuning
+// Most rows (edges * qhead) in one work unit. A slot with more edges is split
+// into near-equal units so that one hot block does not serialise the grid.
+constexpr int kCapRows = 2048;
+// Smallest unit (in rows) that goes to the MFMA kernel. Smaller ones use the
+// wavefront-reduction kernel.
+constexpr int kMfmaMinRows = 32;
+// Head dims the MFMA kernel is built for; others always take the wave path.
+constexpr int kMfmaHeadDim = 128;
+constexpr int kMfmaMaxBlock = 128;
+
+// ---------------------------------------------------------------- errors
+// Device errors are ranked. The build keeps the smallest (rank, position)
+// key with one atomicMin, so the report does not depend on thread timing.
+enum ErrRank : uint64_t {
+  kRankCuContent = 1,   // cu[0] != 0 or decreasing
+  kRankCuTotal = 2,     // cu[batch] != tq
+  kRankSelected = 3,    // id outside [-1, msb), position = flat index
+  kRankPage = 4,        // page id >= num_pages, position = block-table index
+};
+__host__ __device__ inline unsigned long long err_key(uint64_t rank, uint64_t pos) {
+  return (rank << 56) | (pos & ((1ull << 56) - 1));
+}
+
+enum WhatCode : int32_t {
+  kWhatNone = 0,
+  kWhatCuTotal = 1,
+  kWhatPageId = 2,
+};
+
+// Device-resident header at the start of the index buffer (256 bytes).
+struct alignas(256) DevHeader {
+  unsigned long long err_key;   // ~0ull = no error
+  int32_t status;               // sa_status, filled by the last build kernel
+  int32_t what_code;            // WhatCode
+  int64_t err_expected;
+  int64_t err_got;
+  int64_t total_edges;
+  int32_t num_units_wave;
+  int32_t num_units_mfma;
+  int64_t num_slots;
+  uint32_t queue_mfma;          // dynamic unit queue of the MFMA kernel
+  uint32_t done_mfma;           // workgroups finished (last one resets the queue)
+  uint32_t queue_wave;
+  uint32_t done_wave;
+  int32_t geom[8];              // planned geometry fingerprint
+};
+static_assert(sizeof(DevHeader) == 256, "header is one 256-byte block");
+
+// Scratch region inside the index buffer (after the public arrays).
+struct ScratchLayout {
+  size_t cnt;        // int32 [hkv*nbs]   counts, then scatter cursors
+  size_t slot_uw;    // int32 [hkv*nbs]   wave-unit offset of compact slot (head-local)
+  size_t slot_um;    // int32 [hkv*nbs]   mfma-unit offset of compact slot (head-local)
+  size_t head_e;     // int32 [hkv]       E_h
+  size_t head_uw;    // int32 [hkv]
+  size_t head_um;    // int32 [hkv]
+  size_t keys;       // int32 [max_edges] scattered (q*topk + r), unordered per slot
+  size_t end;
+};
+
+// Plain pointers into one index buffer.
+struct IndexPtrs {
+  DevHeader* hdr;
+  int32_t* sel_slots;
+  int32_t* sel_offsets;
+  int32_t* num_sel;
+  int64_t* edge_head_base;
+  int32_t* edges;
+  int32_t* inv;
+  int4* units_wave;
+  int4* units_mfma;
+  int32_t* cnt;
+  int32_t* slot_uw;
+  int32_t* slot_um;
+  int32_t* head_e;
+  int32_t* head_uw;
+  int32_t* head_um;
+  int32_t* keys;
+};
+
+struct BuildArgs {
+  const int32_t* selected;
+  const int32_t* block_tables;
+  const int64_t* cu;
+  const int32_t* used;       // may be null
+  int64_t tq;
+  int64_t nbs;
+  int64_t num_pages;
+  int32_t hkv, topk, batch, max_pages, block_size, page_size, ppb, msb;
+  int32_t qhead, cap_edges, mfma_min_rows;
+};
+
+struct FwdArgs {
+  const float* q;
+  const float* k;
+  const float* v;
+  const int32_t* block_tables;
+  const int64_t* cu;
+  const int32_t* used;       // may be null
+  float* o;
+  float* m;
+  float* l;
+  int64_t nbs;
+  int64_t num_pages;
+  int32_t hq, hkv, qhead, head_dim, block_size, page_size, ppb, msb, max_pages, batch;
+  int32_t causal;
+  float scale_log2;          // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* o;
+  const float* m;
+  const float* l;
+  float* out;
+  float* lse;
+  int64_t tq;
+  int32_t hq, hkv, qhead, head_dim, topk;
+};
+
+IndexPtrs index_ptrs(const sa_index* idx);
+ScratchLayout scratch_layout(const sa_index* idx);
+
+// Whether the MFMA forward kernel is part of this build.
+bool mfma_enabled();
+
+// Launchers (enqueue only; return hipSuccess or the launch error).
+hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s);
+hipError_t launch_forward(const sa_index* idx, const FwdArgs& a, hipStream_t s);
+hipError_t launch_combine(const sa_index* idx, const CombineArgs& a, hipStream_t s);
+hipError_t launch_forward_wave(const sa_index* idx, const FwdArgs& a, hipStream_t s,
+                               unsigned grid);
+
+// ---------------------------------------------------------------- device helpers
+// Last b in [0, batch) with cu[b] <= q (types.rs CuSeqlensQ::batch_of).
+__device__ inline int32_t batch_of_dev(const int64_t* __restrict__ cu, int32_t batch, int64_t q) {
+  int32_t lo = 0, hi = batch + 1;      // first index with cu[i] > q lies in [lo, hi]
+  while (lo < hi) {
+    int32_t mid = (lo + hi) >> 1;
+    if (cu[mid] <= q) lo = mid + 1; else hi = mid;
+  }
+  int32_t b = lo - 1;
+  b = b < 0 ? 0 : b;
+  return b >= batch ? batch - 1 : b;
+}
+
+__device__ inline int64_t kv_len_dev(const int32_t* __restrict__ used, int32_t b, int32_t msb,
+                                     int32_t block_size) {
+  if (used == nullptr) return (int64_t)msb * block_size;
+  int32_t u = used[b];
+  return u > 0 ? (int64_t)u : 0;
+}
+
+}  // namespace sa

@@ -23,15 +23,17 @@ An empty ``T`` gives ``O = 0`` and ``lse = -inf``. Duplicate kept ids in one
 edges). With ``strict`` it raises ``ValueError``.
 
 Argument checks run in this order: head counts -> block/page sizes and
-head_dim -> the index build's checks -> ``q`` length -> K/V page stride ->
-the build's content checks (cu_seqlens, selected range, page ids).
+head_dim -> the index build's length checks -> ``q`` length -> K/V page
+stride -> the build's content checks (cu_seqlens content and total, selected
+range, page ids). Checks that read only lengths come before checks that read
+array contents.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .errors import SparseAttentionError
-from .index_ref import batch_of, resolve_kv_lens, validate_build_inputs
+from .index_ref import batch_of, resolve_kv_lens, validate_build_shapes, validate_cu_content
 
 
 def check_forward_args(hq, hkv, head_dim, block_size, page_size):
@@ -74,10 +76,11 @@ def attention_qo_ref(q, k_pages, v_pages, selected, block_tables, cu_seqlens_q,
     sel_np = np.asarray(selected)
     if topk is None:
         topk = sel_np.shape[-1] if sel_np.ndim == 3 else sel_np.size // max(tq * hkv, 1)
-    sel, tbl, cu = validate_build_inputs(selected, tq, hkv, topk, block_tables, batch,
+    sel, tbl, cu = validate_build_shapes(selected, tq, hkv, topk, block_tables, batch,
                                          max_pages, cu_seqlens_q, used_kv_lens,
                                          block_size, page_size)
     num_pages = check_tensor_lengths(q, k_pages, v_pages, hq, hkv, head_dim, page_size, tq)
+    validate_cu_content(cu, tq)
 
     ppb = block_size // page_size
     msb = max_pages // ppb

@@ -58,9 +58,9 @@ def resolve_kv_lens(used_kv_lens, batch, msb, block_size):
     return np.maximum(np.asarray(used_kv_lens, dtype=np.int64), 0)
 
 
-def validate_build_inputs(selected, tq, hkv, topk, block_tables, batch, max_pages,
+def validate_build_shapes(selected, tq, hkv, topk, block_tables, batch, max_pages,
                           cu_seqlens_q, used_kv_lens, block_size, page_size):
-    """Shape and content checks in the order stated in the module doc.
+    """Checks that need only lengths and scalars, in the module doc's order.
     Returns flat int64 copies of ``selected``, ``block_tables``, ``cu``."""
     cu = np.asarray(cu_seqlens_q, dtype=np.int64).ravel()
     if cu.shape[0] < 2:
@@ -80,10 +80,25 @@ def validate_build_inputs(selected, tq, hkv, topk, block_tables, batch, max_page
                                    np.asarray(used_kv_lens).ravel().shape[0])
     if tq == 0 or hkv == 0 or topk == 0:
         raise SparseAttentionError("EmptyInput")
+    return sel, tbl, cu
+
+
+def validate_cu_content(cu, tq):
+    """``cu[0] == 0``, non-decreasing (types.rs ``CuSeqlensQ::new``), and
+    ``cu[B] == tq``."""
     if cu[0] != 0 or np.any(cu[1:] < cu[:-1]):
         raise SparseAttentionError("CuSeqlensInvalid")
     if cu[-1] != tq:
         raise SparseAttentionError("ShapeMismatch", "cu_seqlens_q total", tq, int(cu[-1]))
+
+
+def validate_build_inputs(selected, tq, hkv, topk, block_tables, batch, max_pages,
+                          cu_seqlens_q, used_kv_lens, block_size, page_size):
+    """All of the builder's checks except the id and page-id checks."""
+    sel, tbl, cu = validate_build_shapes(selected, tq, hkv, topk, block_tables, batch,
+                                         max_pages, cu_seqlens_q, used_kv_lens, block_size,
+                                         page_size)
+    validate_cu_content(cu, tq)
     return sel, tbl, cu
 
 

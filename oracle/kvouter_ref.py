@@ -36,8 +36,11 @@ from .index_ref import batch_of
 
 def forward_partials_ref(q, k_pages, v_pages, index, block_tables, cu_seqlens_q,
                          used_kv_lens, hq, hkv, head_dim, block_size, page_size,
-                         softmax_scale, causal):
-    """Return ``(o [E*qhead, d], m [E*qhead], l [E*qhead])`` in float64."""
+                         softmax_scale, causal, only_edges=None):
+    """Return ``(o [E*qhead, d], m [E*qhead], l [E*qhead])`` in float64.
+
+    ``only_edges`` (a set of edge positions) restricts the work to those
+    edges; the other rows keep their initial ``(0, -inf, 0)``."""
     qhead = hq // hkv
     ppb = block_size // page_size
     msb = index["msb"]
@@ -59,6 +62,11 @@ def forward_partials_ref(q, k_pages, v_pages, index, block_tables, cu_seqlens_q,
     for h in range(hkv):
         head_base = int(index["edge_head_base"][h])
         for j in range(int(index["num_sel"][h])):
+            if only_edges is not None:
+                lo = head_base + int(index["sel_offsets"][h, j])
+                hi = head_base + int(index["sel_offsets"][h, j + 1])
+                if not any(lo <= e < hi for e in only_edges):
+                    continue
             raw = int(index["sel_slots"][h, j])
             b, blk = raw // msb, raw % msb
             lk = (msb * block_size if used_kv_lens is None
@@ -93,6 +101,8 @@ def forward_partials_ref(q, k_pages, v_pages, index, block_tables, cu_seqlens_q,
             e0 = head_base + int(index["sel_offsets"][h, j])
             e1 = head_base + int(index["sel_offsets"][h, j + 1])
             for e in range(e0, e1):
+                if only_edges is not None and e not in only_edges:
+                    continue
                 qi = int(edges[e, 0])
                 alive = np.ones(pos_arr.shape[0], dtype=bool)
                 if causal:

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* index: every array bit-exact against ``oracle.build_index_ref``;
+* partials: per-edge (o, m, l) against ``oracle.forward_partials_ref`` (fp64);
+* output: ``max|O_gpu - O_ref| <= 1e-4 * max|O_ref|`` against the query-outer
+  oracle (fp64); lse to 1e-4 absolute.
+
+Sizes: the tiny workload and random small geometries in full; the decode,
+ragged, prefill and skewed workloads at full size in the launch configuration
+the benchmark times, with the output compared on sampled queries (all queries
+for decode) and the index compared in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_paged_csr_amd as sa
+import oracle
+import workloads as W
+from _gpu import (assert_index_equal, check_units, dev_inputs, max_rel_err, oracle_index,
+                  run_attention, run_index)
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1e-4          # max|O_gpu - O_ref| / max|O_ref|
+TOL_LSE = 1e-4        # absolute, natural-log units
+TOL_M = 1e-5          # partial max, absolute (scores are O(1))
+TOL_OL = 1e-5         # partial o and l, relative to the largest magnitude
+
+
+def _qo(w, queries=None):
+    return oracle.attention_qo_ref(w.q, w.k_pages, w.v_pages, w.selected, w.block_tables,
+                                   w.cu_seqlens_q, w.used_kv_lens, w.hq, w.hkv, w.head_dim,
+                                   w.block_size, w.page_size, w.softmax_scale, w.causal,
+                                   queries=queries)
+
+
+def _print_case(case, **kw):
+    print(f"[gpu case] {case} {kw}", flush=True)
+
+
+def _check_output(w, out, lse, queries=None):
+    ref_o, ref_lse = _qo(w, queries)
+    got_o = out.cpu().numpy().astype(np.float64)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    if queries is not None:
+        got_o, got_lse = got_o[queries], got_lse[queries]
+    err, scale = max_rel_err(got_o, ref_o)
+    assert err <= TOL_O, f"O rel err {err:.3e} (max|O| {scale:.3e})"
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(got_lse))
+    if fin.any():
+        assert np.abs(got_lse[fin] - ref_lse[fin]).max() <= TOL_LSE
+    assert np.all(got_o[~fin] == 0.0)            # nothing alive: O = 0
+    return err
+
+
+# ------------------------------------------------------------------ small cases
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_small_end_to_end(seed):
+    w = W.make_random(500 + seed, batch=1 + seed % 3, qo_max=5, kv_max=40,
+                      hkv=1 + seed % 2, qhead=1 + seed % 4, head_dim=[8, 16, 32, 64][seed % 4],
+                      page_size=[1, 2, 4][seed % 3], pages_per_block=1 + seed % 3,
+                      topk=1 + seed % 5)
+    _print_case("random_small", seed=seed, tq=w.tq, d=w.head_dim)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges)
+    out, lse = run_attention(w, d)
+    _check_output(w, out, lse)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_partials_match_kvouter_ref(seed):
+    w = W.make_random(700 + seed, batch=2, qo_max=4, kv_max=48, hkv=2, qhead=1 + seed % 3,
+                      head_dim=32, page_size=2, pages_per_block=2 + seed % 2, topk=3)
+    _print_case("random_partials", seed=seed)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    assert_index_equal(idx, ref)
+    o, m, l = sa.sa_forward(idx, d["q"], d["k"], d["v"], d["bt"], d["cu"], d["used"], w.hq,
+                            w.hkv, w.head_dim, w.block_size, w.page_size, w.softmax_scale,
+                            w.causal)
+    ro, rm, rl = oracle.forward_partials_ref(w.q, w.k_pages, w.v_pages, ref, w.block_tables,
+                                             w.cu_seqlens_q, w.used_kv_lens, w.hq, w.hkv,
+                                             w.head_dim, w.block_size, w.page_size,
+                                             w.softmax_scale, w.causal)
+    rows = rm.shape[0]
+    gm = m[:rows].cpu().numpy().astype(np.float64)
+    gl = l[:rows].cpu().numpy().astype(np.float64)
+    go = o[:rows].cpu().numpy().astype(np.float64)
+    fin = np.isfinite(rm)
+    assert np.array_equal(fin, np.isfinite(gm))
+    if fin.any():
+        assert np.abs(gm[fin] - rm[fin]).max() <= TOL_M
+        assert max_rel_err(gl, rl)[0] <= TOL_OL
+        assert max_rel_err(go, ro)[0] <= TOL_OL
+    assert np.all(gl[~fin] == 0) and np.all(go[~fin] == 0)
+
+
+def test_tiny_workload():
+    w = W.make_config("tiny")
+    _print_case("tiny")
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges)
+    out, lse = run_attention(w, d)
+    _check_output(w, out, lse)
+
+
+@pytest.mark.parametrize("name", ["pages_small_fixture_index.json", "pages_gqa_fixture_index.json",
+                                  "handmade_index.json"])
+def test_golden_index_on_gpu(golden_dir, name):
+    import json
+    import os
+    with open(os.path.join(golden_dir, name)) as f:
+        g = json.load(f)
+    inp = g["inputs"]
+    tbl = np.asarray(inp["block_tables"], dtype=np.int32)
+    tq, hkv, topk = inp["tq"], inp["hkv"], inp["topk"]
+    idx = sa.sa_index_plan(tq, hkv, topk, tbl.shape[0], tbl.shape[1], inp["block_size"],
+                           inp["page_size"], hkv, 4, inp["num_pages"])
+    idx.allocate("cuda")
+    t = lambda a, dt: torch.tensor(a, dtype=dt, device="cuda")
+    used = None if inp.get("used_kv_lens") is None else t(inp["used_kv_lens"], torch.int32)
+    sa.sa_build_index(t(inp["selected"], torch.int32), t(tbl, torch.int32),
+                      t(inp["cu_seqlens_q"], torch.int64), used, idx)
+    info = sa.sa_index_status(idx)
+    arrs = sa.index_arrays(idx, info)
+    for key in ("sel_slots", "sel_offsets", "num_sel", "edges", "edge_head_base", "inv"):
+        np.testing.assert_array_equal(arrs[key].cpu().numpy(), np.asarray(g["expected"][key]),
+                                      err_msg=key)
+
+
+def test_determinism_bitwise():
+    w = W.make_random(901, batch=3, qo_max=6, kv_max=64, hkv=2, qhead=4, head_dim=64, topk=4)
+    d = dev_inputs(w)
+    o1, l1 = run_attention(w, d)
+    o2, l2 = run_attention(w, d)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ device errors
+
+def _device_error(w, d, **over):
+    dd = dict(d)
+    dd.update(over)
+    idx = run_index(w, dd)
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_index_status(idx)
+    return ei.value
+
+
+def _oracle_error(w, **over):
+    import dataclasses
+    w2 = dataclasses.replace(w, **over)
+    with pytest.raises(oracle.SparseAttentionError) as ei:
+        oracle_index(w2)
+    return ei.value
+
+
+def test_device_error_selected_out_of_range():
+    w = W.make_random(31, batch=2, hkv=2, topk=3)
+    msb = w.max_pages // (w.block_size // w.page_size)
+    sel = w.selected.copy()
+    sel.reshape(-1)[7] = msb + 5
+    sel.reshape(-1)[4] = -3
+    d = dev_inputs(w)
+    got = _device_error(w, d, sel=torch.from_numpy(sel).cuda())
+    ref = _oracle_error(w, selected=sel)
+    assert got.kind == ref.kind == "SelectedOutOfRange"
+    assert (got.got, got.expected) == (ref.got, ref.expected) == (-3, msb)
+
+
+def test_device_error_cu_seqlens():
+    w = W.make_random(32, batch=3, hkv=1, topk=2)
+    d = dev_inputs(w)
+    cu = w.cu_seqlens_q.copy()
+    cu[1], cu[2] = cu[2] + 1, cu[1]               # decreasing pair
+    got = _device_error(w, d, cu=torch.from_numpy(cu).cuda())
+    assert got.kind == "CuSeqlensInvalid"
+    cu = w.cu_seqlens_q.copy()
+    cu[-1] = cu[-1] - 1 if cu[-1] > cu[-2] else cu[-1] + 1
+    got = _device_error(w, d, cu=torch.from_numpy(cu).cuda())
+    assert (got.kind, got.what, got.expected, got.got) == ("ShapeMismatch", "cu_seqlens_q total",
+                                                           w.tq, int(cu[-1]))
+
+
+def test_device_error_page_id(golden_dir):
+    import json
+    import os
+    with open(os.path.join(golden_dir, "handmade_index.json")) as f:
+        g = json.load(f)
+    inp, case = g["inputs"], g["page_error_case"]
+    tbl = np.asarray(inp["block_tables"], dtype=np.int32)
+    idx = sa.sa_index_plan(inp["tq"], inp["hkv"], inp["topk"], tbl.shape[0], tbl.shape[1],
+                           inp["block_size"], inp["page_size"], inp["hkv"], 4, case["num_pages"])
+    idx.allocate("cuda")
+    t = lambda a, dt: torch.tensor(a, dtype=dt, device="cuda")
+    sa.sa_build_index(t(inp["selected"], torch.int32), t(tbl, torch.int32),
+                      t(inp["cu_seqlens_q"], torch.int64), t(inp["used_kv_lens"], torch.int32), idx)
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_index_status(idx)
+    e = ei.value
+    assert (e.kind, e.what, e.expected, e.got) == (case["kind"], case["what"], case["expected"],
+                                                   case["got"])
+
+
+def test_forward_skips_on_device_error():
+    w = W.make_random(33, batch=2, hkv=1, topk=2)
+    d = dev_inputs(w)
+    sel = w.selected.copy()
+    sel.reshape(-1)[0] = 10 ** 6
+    d["sel"] = torch.from_numpy(sel).cuda()
+    out = torch.full((w.tq, w.hq, w.head_dim), 7.0, device="cuda")
+    o, lse, idx = sa.sa_attention(d["q"], d["k"], d["v"], d["sel"], d["bt"], d["cu"], d["used"],
+                                  w.block_size, w.softmax_scale, w.causal, out=out,
+                                  return_index=True)
+    with pytest.raises(sa.SaError):
+        sa.sa_index_status(idx)
+    assert torch.all(out == 7.0)                  # nothing written
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sample_queries(w, n, seed=0):
+    rng = np.random.default_rng(seed)
+    cu = w.cu_seqlens_q
+    picks = set()
+    for b in range(w.batch):
+        if cu[b + 1] > cu[b]:
+            picks.update({int(cu[b]), int(cu[b + 1] - 1)})
+    picks.update(rng.choice(w.tq, size=min(n, w.tq), replace=False).tolist())
+    return np.asarray(sorted(picks))
+
+
+@pytest.mark.parametrize("name,n_sample", [("decode", None), ("ragged", 48),
+                                           ("prefill", 24), ("skewed", 16)])
+def test_full_size_workload(name, n_sample):
+    _print_case("full_size", name=name)
+    w = W.make_config(name)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges)
+    out, lse = run_attention(w, d)
+    torch.cuda.synchronize()
+    queries = None if n_sample is None else _sample_queries(w, n_sample)
+    err = _check_output(w, out, lse, queries)
+    print(f"[gpu case] {name}: O rel err {err:.3e}", flush=True)
