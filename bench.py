@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-outer block-sparse paged attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: index build (histogram,
+scan, scatter, rank, work units) -> KV-outer forward -> LSE combine. Inputs
+are resident in HBM before the timed region. Steps rotate over ``--rotate``
+independent selections and page tables that share one K/V cache. A step
+therefore does not find its blocks in the 256 MB Infinity Cache from the
+step before.
+
+Prints ONE JSON line. ``value`` is kept edges per second of whole steps.
+``roofline`` is for the forward kernel, the dominant one. Its average
+duration is measured with HIP events recorded on the stream the kernel is
+launched on, inside the timed region, and its algorithmic bytes are counted
+from the built index. ``cpu_baseline`` is the CPU oracle timed on this host.
+
+    python bench.py [--steps K] [--warmup W] [--config decode|tiny|prefill|ragged|skewed]
+    python bench.py --copy-calibration   # plain copy kernel of known size, for PMC scaling
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selected-block attention edges/s + effective TFLOP/s and HBM GB/s % of peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
+DEFAULT_CONFIG = "decode"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default=DEFAULT_CONFIG,
+                   choices=["tiny", "decode", "prefill", "ragged", "skewed"])
+    p.add_argument("--rotate", type=int, default=4, help="independent input batches cycled")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle leg")
+    p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step replayed from a captured HIP graph")
+    return p.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of a known size (1 GiB read + 1 GiB written),
+    for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 28                                   # 2^28 floats = 1 GiB
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}), flush=True)
+
+
+def variants(name, rotate):
+    """The base workload with K/V, plus rotate-1 more selections/page tables."""
+    import workloads as W
+    base = W.make_config(name)
+    out = [base]
+    for r in range(1, rotate):
+        v = W.make_config(name, seed=W.CONFIG_SEEDS[name] + 1000 * r, with_kv=False)
+        assert v.num_pages == base.num_pages
+        out.append(v)
+    return base, out
+
+
+def algorithmic_work(w, arrs, info):
+    """Bytes and flops the method must move/do for this batch, from the index.
+
+    forward: K and V rows of every selected block once (valid positions with a
+    page), Q once, partials (o, m, l) written.  combine: partials read once,
+    inv read, O (and lse) written.  Flops: 4*d per (row, valid key)."""
+    ppb = w.block_size // w.page_size
+    msb = w.max_pages // ppb
+    d = w.head_dim
+    qhead = w.hq // w.hkv
+    num_sel = arrs["num_sel"]
+    offs = arrs["sel_offsets"]
+    slots = arrs["sel_slots"]
+    lk = (np.full(w.batch, msb * w.block_size, dtype=np.int64) if w.used_kv_lens is None
+          else np.maximum(w.used_kv_lens.astype(np.int64), 0))
+    kv_bytes = 0
+    flops = 0
+    for h in range(w.hkv):
+        n = int(num_sel[h])
+        raw = slots[h, :n].astype(np.int64)
+        b, blk = raw // msb, raw % msb
+        start = blk * w.block_size
+        end = np.minimum(start + w.block_size, lk[b])
+        # valid positions: inside [start, end) and on a page >= 0
+        valid = np.zeros(n, dtype=np.int64)
+        for pl in range(ppb):
+            p0 = start + pl * w.page_size
+            p1 = np.minimum(p0 + w.page_size, end)
+            page = w.block_tables[b, blk * ppb + pl]
+            valid += np.where((p1 > p0) & (page >= 0), p1 - p0, 0)
+        edges_per_slot = np.diff(offs[h, :n + 1]).astype(np.int64)
+        kv_bytes += int(2 * valid.sum() * d * 4)
+        flops += int((edges_per_slot * valid).sum() * qhead * 4 * d)
+    E = info["total_edges"]
+    rows = E * qhead
+    q_bytes = w.tq * w.hq * d * 4
+    part_bytes = rows * (d + 2) * 4
+    meta_fwd = info["num_units_wave"] * 16 + info["num_units_mfma"] * 16 + E * 8
+    fwd_bytes = kv_bytes + q_bytes + part_bytes + meta_fwd
+    comb_bytes = part_bytes + w.tq * w.hkv * w.topk * 4 + w.tq * w.hq * (d + 1) * 4
+    return {"kv_bytes": kv_bytes, "fwd_bytes": fwd_bytes, "comb_bytes": comb_bytes,
+            "total_bytes": fwd_bytes + comb_bytes, "flops": flops, "edges": E, "rows": rows}
+
+
+def cpu_baseline(w, target_s):
+    """The oracle (index build + query-outer attention) on the host, one
+    thread, over whole queries of this workload until ~target_s seconds."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(oracle, w, target_s)
+
+
+def _cpu_baseline(oracle, w, target_s):
+    t0 = time.perf_counter()
+    idx = oracle.build_index_ref(w.selected, w.tq, w.hkv, w.topk, w.block_tables, w.batch,
+                                 w.max_pages, w.cu_seqlens_q, w.used_kv_lens, w.block_size,
+                                 w.page_size, w.num_pages)
+    t_index = time.perf_counter() - t0
+    inv = idx["inv"]
+    done_q, edges_done, t_attn = 0, 0, 0.0
+    order = np.random.default_rng(0).permutation(w.tq)
+    min_s = min(2.0, target_s)
+    # whole passes over the batch while they are short, else a prefix of one pass
+    while (done_q < w.tq and t_attn < target_s) or (done_q % w.tq == 0 and t_attn < min_s):
+        at = done_q % w.tq
+        chunk = order[at:at + max(1, min(64, w.tq - at))]
+        t0 = time.perf_counter()
+        oracle.attention_qo_ref(w.q, w.k_pages, w.v_pages, w.selected, w.block_tables,
+                                w.cu_seqlens_q, w.used_kv_lens, w.hq, w.hkv, w.head_dim,
+                                w.block_size, w.page_size, w.softmax_scale, w.causal,
+                                queries=chunk)
+        t_attn += time.perf_counter() - t0
+        done_q += len(chunk)
+        edges_done += int((inv[:, chunk, :] >= 0).sum())
+    frac = done_q / w.tq
+    secs = t_attn + t_index * frac            # index build charged pro rata
+    return {"value": edges_done / secs, "unit": "edges/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_q} query rows ({frac:.2f} passes over the {w.tq} queries of "
+                      f"the {w.name} batch, {edges_done} edges); index build over the whole "
+                      f"batch charged pro rata; float64 NumPy, 1 thread",
+            "seconds": round(secs, 3)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the design for sharding is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    import block_sparse_paged_csr_amd as sa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base, vs = variants(args.config, max(1, args.rotate))
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+    k = t(base.k_pages, torch.float32)
+    v = t(base.v_pages, torch.float32)
+    sets = []
+    for w in vs:
+        idx = sa.sa_index_plan(w.tq, w.hkv, w.topk, w.batch, w.max_pages, w.block_size,
+                               w.page_size, w.hq, w.head_dim, base.num_pages).allocate(dev)
+        rows = idx.c.max_edges * (w.hq // w.hkv)
+        sets.append({
+            "w": w, "idx": idx,
+            "q": t(w.q, torch.float32), "sel": t(w.selected, torch.int32),
+            "bt": t(w.block_tables, torch.int32), "cu": t(w.cu_seqlens_q, torch.int64),
+            "used": None if w.used_kv_lens is None else t(w.used_kv_lens, torch.int32),
+            "o": torch.empty((rows, w.head_dim), dtype=torch.float32, device=dev),
+            "m": torch.empty(rows, dtype=torch.float32, device=dev),
+            "l": torch.empty(rows, dtype=torch.float32, device=dev),
+            "out": torch.empty((w.tq, w.hq, w.head_dim), dtype=torch.float32, device=dev),
+            "lse": torch.empty((w.tq, w.hq), dtype=torch.float32, device=dev),
+        })
+
+    def step(s, ev=None):
+        w = s["w"]
+        if ev is not None:
+            ev[0].record()
+        sa.sa_build_index(s["sel"], s["bt"], s["cu"], s["used"], s["idx"])
+        if ev is not None:
+            ev[1].record()
+        sa.sa_forward(s["idx"], s["q"], k, v, s["bt"], s["cu"], s["used"], w.hq, w.hkv,
+                      w.head_dim, w.block_size, w.page_size, w.softmax_scale, w.causal,
+                      s["o"], s["m"], s["l"])
+        if ev is not None:
+            ev[2].record()
+        sa.sa_combine(s["idx"], s["o"], s["m"], s["l"], w.hq, w.head_dim, s["out"], s["lse"])
+        if ev is not None:
+            ev[3].record()
+
+    # algorithmic work of each batch, counted from the built index
+    work = []
+    for s in sets:
+        step(s)
+        info = sa.sa_index_status(s["idx"])
+        arrs = {kk: vv.cpu().numpy() for kk, vv in sa.index_arrays(s["idx"], info).items()}
+        work.append(algorithmic_work(s["w"], arrs, info))
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in sets:                                  # device-side status of the last builds
+        sa.sa_index_status(s["idx"])
+
+    build_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    per = [work[i % len(sets)] for i in range(args.steps)]
+    edges = sum(p["edges"] for p in per)
+    fwd_bytes = np.mean([p["fwd_bytes"] for p in per])
+    fwd_avg_s = float(np.mean(fwd_ms)) / 1e3
+    step_s = wall / args.steps
+    total_bytes = np.mean([p["total_bytes"] for p in per])
+    flops = np.mean([p["flops"] for p in per])
+    fc_s = (float(np.mean(fwd_ms)) + float(np.mean(comb_ms))) / 1e3
+    achieved = fwd_bytes / fwd_avg_s / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": edges / wall,
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {**base.describe(), "edges_per_batch": int(np.mean([p["edges"] for p in per])),
+                   "rotated_batches": len(sets), "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k_fwd_wave", "alg_bytes_per_launch": int(fwd_bytes),
+                     "avg_launch_us": fwd_avg_s * 1e6},
+        "forward_plus_combine": {
+            "us": fc_s * 1e6,
+            "edges_per_s": edges / args.steps / fc_s,
+            "tflops": flops / fc_s / 1e12,
+            "hbm_gbps": total_bytes / fc_s / 1e9,
+            "hbm_frac": total_bytes / fc_s / 1e9 / HBM_PEAK_GBPS,
+            "mfma_frac_fp32": flops / fc_s / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        },
+        "index_build_us": float(np.mean(build_ms)) * 1e3,
+        "combine_us": float(np.mean(comb_ms)) * 1e3,
+    }
+    if args.graph:
+        result["graph_step_us"] = graph_step_us(sets, step, args.steps)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def graph_step_us(sets, step, steps):
+    """The same steps replayed from captured HIP graphs (one per batch)."""
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in sets:
+            step(s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for s in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(s)
+        graphs.append(g)
+    for i in range(len(graphs) * 2):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e6
+
+
+if __name__ == "__main__":
+    main()

@@ -352,10 +352,10 @@ def index_arrays(index: Index, info: dict | None = None) -> dict:
         "edge_head_base": view(c.off_edge_head_base, hkv + 1, torch.int64, (hkv + 1,)),
         "edges": view(c.off_edges, 2 * E, torch.int32, (E, 2)),
         "inv": view(c.off_inv, hkv * tq * topk, torch.int32, (hkv, tq, topk)),
-        "units_wave": view(c.off_units_wave, 4 * info["num_units_wave"], torch.int32,
-                           (info["num_units_wave"], 4)),
-        "units_mfma": view(c.off_units_mfma, 4 * info["num_units_mfma"], torch.int32,
-                           (info["num_units_mfma"], 4)),
+        "units_wave": view(c.off_units_wave, 8 * info["num_units_wave"], torch.int32,
+                           (info["num_units_wave"], 8)),
+        "units_mfma": view(c.off_units_mfma, 8 * info["num_units_mfma"], torch.int32,
+                           (info["num_units_mfma"], 8)),
     }
     return out
 

@@ -109,6 +109,7 @@ ScratchLayout scratch_layout(const sa_index* idx) {
   L.head_uw = o; o = align256(o + 4 * (size_t)idx->hkv);
   L.head_um = o; o = align256(o + 4 * (size_t)idx->hkv);
   L.keys = o;    o = align256(o + 4 * (size_t)idx->max_edges);
+  L.qinfo = o;   o = align256(o + 8 * (size_t)idx->tq);
   L.end = o;
   return L;
 }
@@ -124,8 +125,8 @@ IndexPtrs index_ptrs(const sa_index* idx) {
   P.edge_head_base = reinterpret_cast<int64_t*>(b + idx->off_edge_head_base);
   P.edges = reinterpret_cast<int32_t*>(b + idx->off_edges);
   P.inv = reinterpret_cast<int32_t*>(b + idx->off_inv);
-  P.units_wave = reinterpret_cast<int4*>(b + idx->off_units_wave);
-  P.units_mfma = reinterpret_cast<int4*>(b + idx->off_units_mfma);
+  P.units_wave = reinterpret_cast<Unit*>(b + idx->off_units_wave);
+  P.units_mfma = reinterpret_cast<Unit*>(b + idx->off_units_mfma);
   P.cnt = reinterpret_cast<int32_t*>(b + L.cnt);
   P.slot_uw = reinterpret_cast<int32_t*>(b + L.slot_uw);
   P.slot_um = reinterpret_cast<int32_t*>(b + L.slot_um);
@@ -133,6 +134,7 @@ IndexPtrs index_ptrs(const sa_index* idx) {
   P.head_uw = reinterpret_cast<int32_t*>(b + L.head_uw);
   P.head_um = reinterpret_cast<int32_t*>(b + L.head_um);
   P.keys = reinterpret_cast<int32_t*>(b + L.keys);
+  P.qinfo = reinterpret_cast<int2*>(b + L.qinfo);
   return P;
 }
 
@@ -176,10 +178,17 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch, in
   if (head_dim % 4 != 0 || head_dim > 256)
     return fail(SA_ERR_UNSUPPORTED, "head_dim must be a multiple of 4, at most 256", 256, head_dim);
   const int32_t qhead = hq / hkv;
+  if ((int64_t)qhead * head_dim > 4096)
+    return fail(SA_ERR_UNSUPPORTED, "(hq/hkv)*head_dim must be at most 4096", 4096,
+                (int64_t)qhead * head_dim);
   const int64_t max_edges = tq * (int64_t)hkv * topk;
   if (max_edges * (int64_t)qhead >= INT32_MAX || tq * (int64_t)topk >= INT32_MAX)
     return fail(SA_ERR_UNSUPPORTED, "tq*hkv*topk*qhead must stay below 2^31", INT32_MAX,
                 max_edges * qhead);
+  const int64_t kv_cap = (int64_t)(max_pages / (block_size / page_size)) * block_size;
+  if (block_size >= (1 << 20) || kv_cap >= INT32_MAX)
+    return fail(SA_ERR_UNSUPPORTED, "block_size < 2^20 and msb*block_size < 2^31",
+                1 << 20, block_size);
   std::memset(idx, 0, sizeof(*idx));
   idx->tq = tq;
   idx->hkv = hkv;
@@ -209,8 +218,8 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch, in
   idx->off_edge_head_base = o;  o = align256(o + 8 * (size_t)(hkv + 1));
   idx->off_edges = o;           o = align256(o + 8 * (size_t)max_edges);
   idx->off_inv = o;             o = align256(o + 4 * (size_t)max_edges);
-  idx->off_units_wave = o;      o = align256(o + 16 * (size_t)idx->max_units);
-  idx->off_units_mfma = o;      o = align256(o + 16 * (size_t)idx->max_units);
+  idx->off_units_wave = o;      o = align256(o + sizeof(sa::Unit) * (size_t)idx->max_units);
+  idx->off_units_mfma = o;      o = align256(o + sizeof(sa::Unit) * (size_t)idx->max_units);
   idx->off_scratch = o;
   idx->index_bytes = sa::scratch_layout(idx).end;
   idx->buffer = nullptr;
@@ -312,6 +321,7 @@ sa_status sa_forward(const sa_index* idx, const float* q, int64_t q_len, const f
   a.batch = idx->batch;
   a.causal = causal != 0;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.ps_magic = sa::make_div_magic((uint32_t)page_size);
   hipError_t e = sa::launch_forward(idx, a, stream);
   if (e != hipSuccess) return runtime_error(e, "forward launch");
   return ok();

@@ -9,8 +9,10 @@ namespace sa {
 bool mfma_enabled() { return false; }
 
 hipError_t launch_forward(const sa_index* idx, const FwdArgs& a, hipStream_t s) {
-  // Enough workgroups to fill 256 CUs a few times over; each loops over units.
-  const unsigned grid = 1024;
+  // One workgroup per unit up to a cap; past the cap workgroups loop. Units
+  // beyond the device-side count exit at once.
+  const int64_t cap = 16384;
+  const unsigned grid = (unsigned)(idx->max_units < cap ? idx->max_units : cap);
   return launch_forward_wave(idx, a, s, grid);
 }
 

@@ -8,20 +8,26 @@
 //   t < min((blk+1)*bs, lk_b), causally alive positions only; m = max s;
 //   l = sum exp(s - m); o = sum exp(s - m) v_t; nothing alive -> (0, -inf, 0).
 //
+// Latency: a unit costs two dependent memory round trips. (1) The edges'
+// query ids and the chunk's block-table entries go to LDS. (2) The K, V and
+// q loads are issued together. Several workgroups per CU overlap their
+// round trips.
+//
 // Data movement, per key chunk of KC keys:
 //  * K and V rows are gathered through the block table with 128-bit loads.
-//    Thread t owns float4 column c4 = t % D4P of keys i*KS + t/D4P (KS =
-//    256/D4P key slots), so every load instruction reads whole rows.
-//  * Scores: each thread forms NI*4 partial dot products (NI keys x 4 rows)
-//    over its column, then a transpose-reduce across the D4P lanes of its
-//    key slot leaves each lane with finished scores, written to LDS.
+//  * Scores: TPK = D4P/NI threads share a key; thread (k, qq) holds the K
+//    float4 columns qq + TPK*j (j < NI), so one load instruction reads
+//    TPK*16 contiguous bytes per key. It forms 4 partial dots against q rows
+//    read from LDS (broadcast), and a TPK-lane butterfly finishes them.
+//  * V uses the PV layout: thread t owns float4 column c4 = t % D4P of keys
+//    i*KS + t/D4P (KS = 256/D4P key slots).
 //  * Softmax: wave w owns row w of the current 4-row group; it applies the
 //    validity and causal masks, keeps the running (m, l) in base 2 (the
 //    scale carries log2 e), writes p = exp2(s - m) back and the rescale
 //    factor of the running output.
 //  * PV: each thread accumulates p * v over its keys for 4 rows, a lane
 //    butterfly and an LDS sum across waves finish the reduction, and the
-//    running output rows (up to 32 per pass) live in LDS.
+//    running output rows (up to 16 per pass) live in LDS.
 #include "sa_internal.h"
 
 namespace sa {
@@ -29,7 +35,7 @@ namespace sa {
 namespace {
 
 constexpr int kRowsPerGroup = 4;     // one row per wave
-constexpr int kRowsPerPass = 32;     // running output rows kept in LDS
+constexpr int kRowsPerPass = 16;     // running output rows kept in LDS
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ inline float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -38,6 +44,9 @@ __device__ inline float dot4(float4 a, float4 b) {
 }
 __device__ inline float4 fma4(float s, float4 v, float4 a) {
   return make_float4(fmaf(s, v.x, a.x), fmaf(s, v.y, a.y), fmaf(s, v.z, a.z), fmaf(s, v.w, a.w));
+}
+__device__ inline float4 add4f(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 __device__ inline float4 shfl_xor4(float4 v, int m) {
   return make_float4(__shfl_xor(v.x, m, 64), __shfl_xor(v.y, m, 64), __shfl_xor(v.z, m, 64),
@@ -59,140 +68,141 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 template <int D4P>
 struct WaveCfg {
   static constexpr int NI = D4P < 8 ? D4P : 8;      // float4 of K (and of V) per thread per chunk
-  static constexpr int KS = 256 / D4P;              // key slots per chunk step
-  static constexpr int KC = NI * KS;                // keys per chunk (<= 256)
-  static constexpr int NV = NI * kRowsPerGroup;     // partial dots per thread
-  static constexpr int S = ilog2(D4P);              // butterfly stages inside a key slot
+  static constexpr int TPK = D4P / NI;              // threads per key in the score pass
+  static constexpr int KC = 256 / TPK;              // keys per chunk (<= 256)
+  static constexpr int KS = 256 / D4P;              // key slots of the PV pass
+  static constexpr int MAXPG = KC + 1;              // pages one chunk can touch
 };
 
 template <int D4P>
 __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
   using C = WaveCfg<D4P>;
-  constexpr int NI = C::NI, KS = C::KS, KC = C::KC, NV = C::NV, S = C::S;
+  constexpr int NI = C::NI, TPK = C::TPK, KC = C::KC, KS = C::KS;
 
   __shared__ float s_sc[kRowsPerGroup][KC];              // scores, then probabilities
   __shared__ int s_kvalid[KC];
   __shared__ float4 s_red[4][kRowsPerGroup][D4P];
   __shared__ float4 s_o[kRowsPerPass][D4P];
+  __shared__ float4 s_q[kRowsPerPass][D4P];
   __shared__ float s_m[kRowsPerPass], s_l[kRowsPerPass], s_alpha[kRowsPerGroup];
+  __shared__ int64_t s_qoff[kRowsPerPass];
+  __shared__ int32_t s_lim[kRowsPerPass];
+  __shared__ int64_t s_pg[C::MAXPG];
 
   const DevHeader* hdr = P.hdr;
   if (hdr->status != SA_OK) return;
   const int32_t num_units = hdr->num_units_wave;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int c4 = tid % D4P;          // float4 column
-  const int ks = tid / D4P;          // key slot
+  // score pass: key kq = tid / TPK, float4 columns qq + TPK*j
+  const int kq = tid / TPK, qq = tid % TPK;
+  // PV pass: float4 column c4 of keys i*KS + ks
+  const int c4 = tid % D4P, ks = tid / D4P;
   const int D = A.head_dim, D4 = D >> 2;
   const bool col_ok = c4 < D4;
   const int32_t qhead = A.qhead;
+  const int64_t page_stride = (int64_t)A.hkv * A.page_size * D;
 
   for (int32_t u = blockIdx.x; u < num_units; u += gridDim.x) {
-    const int4 unit = P.units_wave[u];
-    const int32_t h = unit.x, j = unit.y, e0 = unit.z, e1 = unit.w;
-    const int32_t raw = P.sel_slots[(int64_t)h * A.nbs + j];
-    const int32_t b = raw / A.msb, blk = raw % A.msb;
-    const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
-    const int64_t block_start = (int64_t)blk * A.block_size;
+    const Unit unit = P.units_wave[u];
+    const int32_t h = unit.h, e0 = unit.e0, e1 = unit.e1;
+    const int64_t lk = unit.lk;
+    const int64_t block_start = (int64_t)unit.blk * A.block_size;
     int64_t block_end = block_start + A.block_size;
     block_end = block_end < lk ? block_end : lk;
     const int32_t rows = (e1 - e0) * qhead;
     const int64_t row0 = (int64_t)e0 * qhead;                 // first partial row
-    const int64_t q_start = A.cu[b];
-    const int64_t qo_len = A.cu[b + 1] - q_start;
     const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
-    const int64_t bt_row = (int64_t)b * A.max_pages + (int64_t)blk * A.ppb;
+    const int64_t bt_row = (int64_t)unit.b * A.max_pages + (int64_t)unit.blk * A.ppb;
+    const int64_t head_off = (int64_t)h * A.page_size * D;
 
     for (int32_t pass0 = 0; pass0 < rows; pass0 += kRowsPerPass) {
       const int32_t prow = rows - pass0 < kRowsPerPass ? rows - pass0 : kRowsPerPass;
       __syncthreads();                                        // previous pass fully stored
-      for (int x = tid; x < kRowsPerPass * D4P; x += 256)
-        s_o[x / D4P][x % D4P] = make_float4(0.f, 0.f, 0.f, 0.f);
+      // ---- round trip 1: query ids of the pass's rows
       if (tid < kRowsPerPass) {
         s_m[tid] = -INFINITY;
         s_l[tid] = 0.f;
+        if (tid < prow) {
+          const int32_t ur = pass0 + tid;
+          const int32_t qi = P.edges[2 * (int64_t)(e0 + ur / qhead)];
+          s_qoff[tid] = ((int64_t)qi * A.hq + (int64_t)h * qhead + ur % qhead) * D;
+          s_lim[tid] = A.causal ? qi + unit.delta : INT32_MAX;
+        }
       }
+      for (int x = tid; x < kRowsPerPass * D4P; x += 256)
+        s_o[x / D4P][x % D4P] = make_float4(0.f, 0.f, 0.f, 0.f);
 
       for (int32_t cp = 0; cp < nkeys; cp += KC) {
-        // ---- gather the chunk's K and V rows (zero for invalid keys)
+        const int32_t pg0 = (int32_t)div_magic((uint32_t)cp, A.ps_magic);
+        const int32_t last = (cp + KC < nkeys ? cp + KC : nkeys) - 1;
+        const int32_t npg = (int32_t)div_magic((uint32_t)last, A.ps_magic) - pg0 + 1;
+        if (cp > 0) __syncthreads();                           // s_pg of the last chunk read
+        for (int x = tid; x < npg; x += 256) {
+          const int32_t page = A.block_tables[bt_row + pg0 + x];
+          s_pg[x] = (page >= 0 && page < A.num_pages) ? (int64_t)page * page_stride + head_off : -1;
+        }
+        __syncthreads();
+        // ---- round trip 2: K, V (this chunk) and, on the first chunk, q
         float4 kr[NI], vr[NI];
+        {
+          const int32_t tb = cp + kq;
+          const int32_t pgl = (int32_t)div_magic((uint32_t)tb, A.ps_magic);
+          const int64_t base = tb < nkeys ? s_pg[pgl - pg0] : -1;
+          const bool valid = base >= 0;
+          if (qq == 0) s_kvalid[kq] = valid;
+          const float* kp = A.k + base + (int64_t)(tb - pgl * A.page_size) * D;
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const int c = qq + TPK * j;
+            kr[j] = (valid && c < D4) ? ld4(kp + c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          const int32_t kk = i * KS + ks;
-          const int32_t tb = cp + kk;                         // block-local position
-          bool valid = tb < nkeys;
-          int64_t off = 0;
-          if (valid) {
-            const int32_t page = A.block_tables[bt_row + tb / A.page_size];
-            valid = page >= 0 && page < A.num_pages;
-            off = (((int64_t)page * A.hkv + h) * A.page_size + tb % A.page_size) * D + c4 * 4;
+          const int32_t tb = cp + i * KS + ks;
+          const int32_t pgl = (int32_t)div_magic((uint32_t)tb, A.ps_magic);
+          const int64_t base = tb < nkeys ? s_pg[pgl - pg0] : -1;
+          const int64_t off = base + (int64_t)(tb - pgl * A.page_size) * D + c4 * 4;
+          vr[i] = (base >= 0 && col_ok) ? ld4(A.v + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (cp == 0) {
+          for (int x = tid; x < prow * D4P; x += 256) {
+            const int r = x / D4P, c = x % D4P;
+            s_q[r][c] = c < D4 ? ld4(A.q + s_qoff[r] + c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
           }
-          if (c4 == 0) s_kvalid[kk] = valid;
-          kr[i] = (valid && col_ok) ? ld4(A.k + off) : make_float4(0.f, 0.f, 0.f, 0.f);
-          vr[i] = (valid && col_ok) ? ld4(A.v + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+          __syncthreads();
         }
 
         for (int32_t g0 = 0; g0 < prow; g0 += kRowsPerGroup) {
-          // ---- q of the group's 4 rows, this thread's column
-          float4 qr[kRowsPerGroup];
+          // ---- scores of key kq for the group's 4 rows, reduced over TPK lanes
+          float sc[kRowsPerGroup];
 #pragma unroll
           for (int r = 0; r < kRowsPerGroup; ++r) {
-            const int32_t ur = pass0 + g0 + r;
-            qr[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (ur < rows && col_ok) {
-              const int32_t e = e0 + ur / qhead, qh = ur % qhead;
-              const int64_t qi = P.edges[2 * (int64_t)e];
-              qr[r] = ld4(A.q + ((qi * A.hq + (int64_t)h * qhead + qh) * D) + c4 * 4);
+            float acc = 0.f;
+            if (g0 + r < prow) {
+#pragma unroll
+              for (int j = 0; j < NI; ++j) acc += dot4(s_q[g0 + r][qq + TPK * j], kr[j]);
             }
+            sc[r] = acc;
+            // one q row live at a time: keeps the K and V registers resident
+            __builtin_amdgcn_sched_barrier(0);
           }
-          float vals[NV];
 #pragma unroll
-          for (int i = 0; i < NI; ++i)
+          for (int m = 1; m < TPK; m <<= 1)
 #pragma unroll
-            for (int r = 0; r < kRowsPerGroup; ++r) vals[i * kRowsPerGroup + r] = dot4(qr[r], kr[i]);
-          // ---- transpose-reduce across the D4P lanes of the key slot
-          int base = 0;
+            for (int r = 0; r < kRowsPerGroup; ++r) sc[r] += __shfl_xor(sc[r], m, 64);
+          if (g0 > 0) __syncthreads();                        // s_sc / s_red free again
+          if (qq == 0) {
 #pragma unroll
-          for (int st = 0; st < S; ++st) {
-            const int n = (NV >> st) > 1 ? (NV >> st) : 1;
-            const bool hi = (lane >> st) & 1;
-            if (n > 1) {
-              const int half = n >> 1;
-#pragma unroll
-              for (int x = 0; x < half; ++x) {
-                const float send = hi ? vals[x] : vals[x + half];
-                const float keep = hi ? vals[x + half] : vals[x];
-                vals[x] = keep + __shfl_xor(send, 1 << st, 64);
-              }
-              base += hi ? half : 0;
-            } else {
-              vals[0] += __shfl_xor(vals[0], 1 << st, 64);
-            }
-          }
-          constexpr int NF = (NV >> S) > 1 ? (NV >> S) : 1;
-          __syncthreads();                                    // s_sc / s_red free again
-          // With D4P > NV the last stages are plain butterflies and lane pairs
-          // hold the same sums; only the lower lane of each pair writes.
-          const bool writer = (S <= ilog2(NV)) || ((lane >> ilog2(NV)) & ((D4P >> ilog2(NV)) - 1)) == 0;
-          if (writer) {
-#pragma unroll
-            for (int x = 0; x < NF; ++x) {
-              const int idx = base + x;
-              s_sc[idx % kRowsPerGroup][(idx / kRowsPerGroup) * KS + ks] = vals[x];
-            }
+            for (int r = 0; r < kRowsPerGroup; ++r) s_sc[r][kq] = sc[r];
           }
           __syncthreads();
           // ---- softmax update: wave wid owns row g0 + wid
           {
             const int32_t lr = g0 + wid;                      // row within the pass
-            const int32_t ur = pass0 + lr;
-            if (ur < rows) {
-              int64_t limit = INT64_MAX;
-              if (A.causal) {
-                const int32_t e = e0 + ur / qhead;
-                const int64_t q_local = (int64_t)P.edges[2 * (int64_t)e] - q_start;
-                limit = lk >= qo_len ? lk - qo_len + q_local : q_local;
-              }
+            if (lr < prow) {
+              const int64_t limit = s_lim[lr];
               float mc = -INFINITY;
               for (int kk = lane; kk < KC; kk += 64) {
                 const int64_t t = block_start + cp + kk;
@@ -218,10 +228,8 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
                 s_l[lr] = s_l[lr] * alpha + lc;
                 s_alpha[wid] = alpha;
               }
-            } else if (lane == 0) {
-              s_alpha[wid] = 0.f;
-            }
-            if (ur >= rows) {
+            } else {
+              if (lane == 0) s_alpha[wid] = 0.f;
               for (int kk = lane; kk < KC; kk += 64) s_sc[wid][kk] = 0.f;
             }
           }
@@ -239,10 +247,7 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
 #pragma unroll
           for (int m = D4P; m < 64; m <<= 1)
 #pragma unroll
-            for (int r = 0; r < kRowsPerGroup; ++r) {
-              const float4 o = shfl_xor4(acc[r], m);
-              acc[r] = make_float4(acc[r].x + o.x, acc[r].y + o.y, acc[r].z + o.z, acc[r].w + o.w);
-            }
+            for (int r = 0; r < kRowsPerGroup; ++r) acc[r] = add4f(acc[r], shfl_xor4(acc[r], m));
           if (lane < D4P) {
 #pragma unroll
             for (int r = 0; r < kRowsPerGroup; ++r) s_red[wid][r][lane] = acc[r];
@@ -254,10 +259,7 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
             if (lr < prow) {
               float4 sum = s_red[0][r][c];
 #pragma unroll
-              for (int w = 1; w < 4; ++w) {
-                const float4 o = s_red[w][r][c];
-                sum = make_float4(sum.x + o.x, sum.y + o.y, sum.z + o.z, sum.w + o.w);
-              }
+              for (int w = 1; w < 4; ++w) sum = add4f(sum, s_red[w][r][c]);
               const float a = s_alpha[r];
               const float4 prev = s_o[lr][c];
               s_o[lr][c] = make_float4(fmaf(prev.x, a, sum.x), fmaf(prev.y, a, sum.y),

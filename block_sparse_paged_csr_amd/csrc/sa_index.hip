@@ -1,12 +1,14 @@
 // Index build on the GPU: the KV-outer CSR index of types.rs (alice-llm
 // 2.0.0, KvOuterIndex field docs) plus the work units that the forward walks.
 //
-//   k_index_init     zero the per-slot counters, reset the header, check cu_seqlens
+//   k_index_init     zero the per-slot counters, reset the header, check
+//                    cu_seqlens, and resolve (sequence, kv length) per query
 //   k_index_hist     one thread per (q, h, r): drop padding / past-lk ranks,
-//                    flag ids outside [-1, msb), count edges per (h, raw slot)
+//                    flag ids outside [-1, msb), check the block's touched
+//                    page ids, count edges per (h, raw slot)
 //   k_index_scan     one workgroup per head: exclusive scans of the counts,
 //                    compaction of nonempty slots, plateaued offsets, unit
-//                    counts per slot, page-id check of touched pages
+//                    counts per slot
 //   k_index_scatter  one thread per kept (q, h, r): atomic cursor per slot,
 //                    key q*topk + r into the slot's segment (unordered)
 //   k_index_rank     per compact slot: rank of each key inside the segment
@@ -57,9 +59,12 @@ __device__ inline void unit_split(int c, int cap, int thr_e, int* n_wave, int* n
 
 __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
   const int64_t n = (int64_t)A.hkv * A.nbs;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * 256)
-    P.cnt[i] = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) P.cnt[i] = 0;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < A.tq; q += stride) {
+    const int32_t b = batch_of_dev(A.cu, A.batch, q);
+    P.qinfo[q] = make_int2(b, (int32_t)kv_len_dev(A.used, b, A.msb, A.block_size));
+  }
   if (blockIdx.x != 0) return;
   if (threadIdx.x == 0) {
     DevHeader* h = P.hdr;
@@ -105,15 +110,30 @@ __global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
   const int32_t h = (int32_t)(qh % A.hkv);
   const int64_t q = qh / A.hkv;
   const int32_t v = A.selected[idx];
+  const int2 qi = P.qinfo[q];
   P.inv[((int64_t)h * A.tq + q) * A.topk + r] = -1;
   if (v == -1) return;
   if (v < -1 || v >= A.msb) {
     atomicMin(&P.hdr->err_key, err_key(kRankSelected, (uint64_t)idx));
     return;
   }
-  const int32_t b = batch_of_dev(A.cu, A.batch, q);
-  const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
-  if ((int64_t)v * A.block_size >= lk) return;
+  const int32_t b = qi.x;
+  const int64_t lk = qi.y;
+  const int64_t block_start = (int64_t)v * A.block_size;
+  if (block_start >= lk) return;
+  if (A.num_pages >= 0) {
+    // Pages that the kept block's valid range touches must exist (the
+    // forward's "block_tables page id" check, moved into the build).
+    const int64_t block_end = block_start + A.block_size < lk ? block_start + A.block_size : lk;
+    const int64_t col0 = (int64_t)b * A.max_pages + (int64_t)v * A.ppb;
+    int64_t bad = INT64_MAX;
+    for (int32_t pl = 0; pl < A.ppb; ++pl) {
+      const bool touched = block_start + (int64_t)pl * A.page_size < block_end;
+      const int32_t page = touched ? A.block_tables[col0 + pl] : -1;
+      if (page >= A.num_pages && col0 + pl < bad) bad = col0 + pl;
+    }
+    if (bad != INT64_MAX) atomicMin(&P.hdr->err_key, err_key(kRankPage, (uint64_t)bad));
+  }
   atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
 }
 
@@ -135,6 +155,9 @@ __global__ __launch_bounds__(kScanThreads) void k_index_scan(IndexPtrs P, BuildA
     for (int k = 0; k < kScanItems; ++k) {
       const int64_t raw = base + (int64_t)tid * kScanItems + k;
       c[k] = raw < nbs ? cnt[raw] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
       unit_split(c[k], cap, thr_e, &nw[k], &nm[k]);
       mine = add4(mine, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
     }
@@ -160,20 +183,6 @@ __global__ __launch_bounds__(kScanThreads) void k_index_scan(IndexPtrs P, BuildA
         P.slot_uw[(int64_t)h * nbs + j] = run.z;
         P.slot_um[(int64_t)h * nbs + j] = run.w;
         cnt[raw] = run.x;                               // scatter cursor
-        if (A.num_pages >= 0) {
-          // Pages that the kept block's valid range touches (the forward's
-          // "block_tables page id" check, moved into the build).
-          const int32_t b = (int32_t)(raw / A.msb), blk = (int32_t)(raw % A.msb);
-          const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
-          int64_t block_end = (int64_t)(blk + 1) * A.block_size;
-          block_end = block_end < lk ? block_end : lk;
-          for (int32_t pl = 0; pl < A.ppb; ++pl) {
-            if ((int64_t)blk * A.block_size + (int64_t)pl * A.page_size >= block_end) break;
-            const int64_t col = (int64_t)b * A.max_pages + (int64_t)blk * A.ppb + pl;
-            if (A.block_tables[col] >= A.num_pages)
-              atomicMin(&P.hdr->err_key, err_key(kRankPage, (uint64_t)col));
-          }
-        }
       }
       run = add4(run, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
     }
@@ -203,17 +212,17 @@ __global__ __launch_bounds__(256) void k_index_scatter(IndexPtrs P, BuildArgs A)
   const int64_t total = A.tq * A.hkv * A.topk;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int32_t v = A.selected[idx];
-  if (v < 0 || v >= A.msb) return;
   const int32_t r = (int32_t)(idx % A.topk);
   const int64_t qh = idx / A.topk;
   const int32_t h = (int32_t)(qh % A.hkv);
   const int64_t q = qh / A.hkv;
-  const int32_t b = batch_of_dev(A.cu, A.batch, q);
-  const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
-  if ((int64_t)v * A.block_size >= lk) return;
-  const int32_t pos = atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
-  P.keys[head_edge_base(P, h) + pos] = (int32_t)(q * A.topk + r);
+  const int32_t v = A.selected[idx];
+  const int2 qi = P.qinfo[q];
+  const int64_t hb = head_edge_base(P, h);
+  if (v < 0 || v >= A.msb) return;
+  if ((int64_t)v * A.block_size >= qi.y) return;
+  const int32_t pos = atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)qi.x * A.msb + v], 1);
+  P.keys[hb + pos] = (int32_t)(q * A.topk + r);
 }
 
 __device__ void finalize_header(const IndexPtrs& P, const BuildArgs& A) {
@@ -262,10 +271,14 @@ __device__ inline void write_edge(const IndexPtrs& P, const BuildArgs& A, int32_
                                   int64_t head_base, int32_t off0, int32_t key, int32_t rank) {
   const int32_t q = key / A.topk, r = key % A.topk;
   const int64_t e = head_base + off0 + rank;
-  P.edges[2 * e] = q;
-  P.edges[2 * e + 1] = r;
+  *reinterpret_cast<int2*>(P.edges + 2 * e) = make_int2(q, r);
   P.inv[((int64_t)h * A.tq + q) * A.topk + r] = off0 + rank;
 }
+
+struct SlotInfo {
+  int32_t n, h, j, off0, uw, um, b, blk, lk, delta;
+  int64_t base;
+};
 
 // Each workgroup owns 4 consecutive compact-slot ids g = 4*blockIdx + wave
 // over all heads (h = g / nbs, j = g % nbs). Slots with <= 64 keys are ranked
@@ -274,43 +287,62 @@ __device__ inline void write_edge(const IndexPtrs& P, const BuildArgs& A, int32_
 __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
   if (blockIdx.x == 0 && threadIdx.x == 0) finalize_header(P, A);
   if (A.nbs == 0) return;                          // no slots at all (msb == 0)
-  __shared__ int32_t s_n[4], s_h[4], s_j[4], s_off[4];
-  __shared__ int64_t s_base[4];
+  __shared__ SlotInfo s_slot[4];
   __shared__ __align__(16) int32_t s_keys[kRankChunk];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t g = (int64_t)blockIdx.x * 4 + w;
   if (lane == 0) {
+    SlotInfo si{};
     const int32_t h = (int32_t)(g / A.nbs);
     const int64_t j = g % A.nbs;
-    int32_t n = 0, off0 = 0;
-    int64_t hb = 0;
-    if (h < A.hkv && j < P.num_sel[h]) {
-      off0 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j];
-      n = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j + 1] - off0;
-      hb = head_edge_base(P, h);
+    if (h < A.hkv) {
+      // all loads independent of each other
+      const int32_t nsel = P.num_sel[h];
+      const int32_t o0 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j];
+      const int32_t o1 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j + 1];
+      const int32_t raw = P.sel_slots[(int64_t)h * A.nbs + j];
+      int32_t uw = P.slot_uw[(int64_t)h * A.nbs + j], um = P.slot_um[(int64_t)h * A.nbs + j];
+      int64_t hb = 0;
+      for (int32_t i = 0; i < h; ++i) {
+        hb += P.head_e[i];
+        uw += P.head_uw[i];
+        um += P.head_um[i];
+      }
+      if (j < nsel) {
+        si.n = o1 - o0;
+        si.off0 = o0;
+        si.base = hb;
+        si.uw = uw;
+        si.um = um;
+        si.b = raw / A.msb;
+        si.blk = raw % A.msb;
+        const int64_t q0 = A.cu[si.b], qo_len = A.cu[si.b + 1] - q0;
+        const int64_t lk = kv_len_dev(A.used, si.b, A.msb, A.block_size);
+        si.lk = (int32_t)lk;
+        si.delta = (int32_t)((lk >= qo_len ? lk - qo_len : 0) - q0);
+      }
     }
-    s_n[w] = n;
-    s_h[w] = h;
-    s_j[w] = (int32_t)j;
-    s_off[w] = off0;
-    s_base[w] = hb;
+    si.h = h;
+    si.j = (int32_t)j;
+    s_slot[w] = si;
   }
   __syncthreads();
-  const bool block_mode = s_n[0] > 64 || s_n[1] > 64 || s_n[2] > 64 || s_n[3] > 64;
+  const bool block_mode =
+      s_slot[0].n > 64 || s_slot[1].n > 64 || s_slot[2].n > 64 || s_slot[3].n > 64;
   if (!block_mode) {
-    const int32_t n = s_n[w];
+    const int32_t n = s_slot[w].n;
     if (n > 0) {
-      const int32_t* seg = P.keys + s_base[w] + s_off[w];
+      const int32_t* seg = P.keys + s_slot[w].base + s_slot[w].off0;
       const int32_t key = lane < n ? seg[lane] : INT32_MAX;
       int32_t rank = 0;
       for (int32_t x = 0; x < n; ++x) rank += __shfl(key, x, 64) < key;
-      if (lane < n) write_edge(P, A, s_h[w], s_base[w], s_off[w], key, rank);
+      if (lane < n) write_edge(P, A, s_slot[w].h, s_slot[w].base, s_slot[w].off0, key, rank);
     }
   } else {
     for (int s = 0; s < 4; ++s) {
-      const int32_t n = s_n[s];
+      const int32_t n = s_slot[s].n;
       if (n == 0) continue;
-      const int32_t* seg = P.keys + s_base[s] + s_off[s];
+      const int32_t* seg = P.keys + s_slot[s].base + s_slot[s].off0;
       for (int32_t pass = 0; pass < n; pass += 256 * kRankKeys) {
         int32_t mine[kRankKeys], rank[kRankKeys];
 #pragma unroll
@@ -335,42 +367,36 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
 #pragma unroll
         for (int k = 0; k < kRankKeys; ++k) {
           const int32_t i = pass + tid + 256 * k;
-          if (i < n) write_edge(P, A, s_h[s], s_base[s], s_off[s], mine[k], rank[k]);
+          if (i < n)
+            write_edge(P, A, s_slot[s].h, s_slot[s].base, s_slot[s].off0, mine[k], rank[k]);
         }
       }
     }
   }
   // Work units of this wave's slot, in CSR order within each kind.
-  const int32_t n = s_n[w];
-  if (n == 0) return;
-  const int32_t h = s_h[w], j = s_j[w];
+  const SlotInfo si = s_slot[w];
+  if (si.n == 0) return;
   const int32_t cap = A.cap_edges;
   const int32_t thr_e = (int32_t)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
-  const int32_t k_units = (n + cap - 1) / cap;
-  int32_t uw = P.slot_uw[(int64_t)h * A.nbs + j], um = P.slot_um[(int64_t)h * A.nbs + j];
-  for (int32_t i = 0; i < h; ++i) {
-    uw += P.head_uw[i];
-    um += P.head_um[i];
-  }
-  const int64_t e_base = s_base[w] + s_off[w];
+  const int32_t k_units = (si.n + cap - 1) / cap;
+  int32_t uw = si.uw, um = si.um;
+  const int64_t e_base = si.base + si.off0;
   for (int32_t i0 = 0; i0 < k_units; i0 += 64) {
     const int32_t i = i0 + lane;
     const bool active = i < k_units;
     int32_t s0 = 0, s1 = 0;
     if (active) {
-      s0 = (int32_t)(((int64_t)i * n) / k_units);
-      s1 = (int32_t)(((int64_t)(i + 1) * n) / k_units);
+      s0 = (int32_t)(((int64_t)i * si.n) / k_units);
+      s1 = (int32_t)(((int64_t)(i + 1) * si.n) / k_units);
     }
     const bool is_m = active && (s1 - s0) >= thr_e;
     const bool is_w = active && !is_m;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const uint64_t bm = __ballot(is_m), bw = __ballot(is_w);
-    if (is_m)
-      P.units_mfma[um + __popcll(bm & below)] =
-          make_int4(h, j, (int32_t)(e_base + s0), (int32_t)(e_base + s1));
-    if (is_w)
-      P.units_wave[uw + __popcll(bw & below)] =
-          make_int4(h, j, (int32_t)(e_base + s0), (int32_t)(e_base + s1));
+    const Unit u{si.h, si.j, (int32_t)(e_base + s0), (int32_t)(e_base + s1),
+                 si.b, si.blk, si.lk, si.delta};
+    if (is_m) P.units_mfma[um + __popcll(bm & below)] = u;
+    if (is_w) P.units_wave[uw + __popcll(bw & below)] = u;
     um += __popcll(bm);
     uw += __popcll(bw);
   }
@@ -386,7 +412,7 @@ inline unsigned grid_for(int64_t n, int per) {
 hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) {
   const IndexPtrs P = index_ptrs(idx);
   const int64_t slots = (int64_t)a.hkv * a.nbs;
-  int64_t init_grid = (slots + 255) / 256;
+  int64_t init_grid = ((slots > a.tq ? slots : a.tq) + 255) / 256;
   if (init_grid > 2048) init_grid = 2048;
   if (init_grid < 1) init_grid = 1;
   hipLaunchKernelGGL(k_index_init, dim3((unsigned)init_grid), dim3(256), 0, s, P, a);

@@ -40,6 +40,16 @@ enum WhatCode : int32_t {
   kWhatPageId = 2,
 };
 
+// One work unit: a sub-range [e0, e1) of compact slot j of head h (the
+// WorkSplit fields of forward.rs), plus what the forward needs without
+// further lookups: the slot's sequence b and block blk, the resolved KV length
+// lk_b, and delta such that the causal limit of query q is q + delta.
+struct alignas(16) Unit {
+  int32_t h, j, e0, e1;
+  int32_t b, blk, lk, delta;
+};
+static_assert(sizeof(Unit) == 32, "unit record is 32 bytes");
+
 // Device-resident header at the start of the index buffer (256 bytes).
 struct alignas(256) DevHeader {
   unsigned long long err_key;   // ~0ull = no error
@@ -68,6 +78,7 @@ struct ScratchLayout {
   size_t head_uw;    // int32 [hkv]
   size_t head_um;    // int32 [hkv]
   size_t keys;       // int32 [max_edges] scattered (q*topk + r), unordered per slot
+  size_t qinfo;      // int2  [tq]        (sequence b, resolved kv length lk_b) per query
   size_t end;
 };
 
@@ -80,8 +91,8 @@ struct IndexPtrs {
   int64_t* edge_head_base;
   int32_t* edges;
   int32_t* inv;
-  int4* units_wave;
-  int4* units_mfma;
+  Unit* units_wave;
+  Unit* units_mfma;
   int32_t* cnt;
   int32_t* slot_uw;
   int32_t* slot_um;
@@ -89,6 +100,7 @@ struct IndexPtrs {
   int32_t* head_uw;
   int32_t* head_um;
   int32_t* keys;
+  int2* qinfo;
 };
 
 struct BuildArgs {
@@ -118,6 +130,8 @@ struct FwdArgs {
   int32_t hq, hkv, qhead, head_dim, block_size, page_size, ppb, msb, max_pages, batch;
   int32_t causal;
   float scale_log2;          // softmax_scale * log2(e)
+  uint64_t ps_magic;         // ceil(2^40 / page_size): n / page_size == (n * ps_magic) >> 40
+                             // for n * page_size < 2^40
 };
 
 struct CombineArgs {
@@ -142,6 +156,14 @@ hipError_t launch_forward(const sa_index* idx, const FwdArgs& a, hipStream_t s);
 hipError_t launch_combine(const sa_index* idx, const CombineArgs& a, hipStream_t s);
 hipError_t launch_forward_wave(const sa_index* idx, const FwdArgs& a, hipStream_t s,
                                unsigned grid);
+hipError_t launch_forward_mfma(const sa_index* idx, const FwdArgs& a, hipStream_t s,
+                               unsigned grid);
+
+// Exact n / d for n * d < 2^40 with magic = ceil(2^40 / d).
+__host__ __device__ inline uint32_t div_magic(uint32_t n, uint64_t magic) {
+  return (uint32_t)(((uint64_t)n * magic) >> 40);
+}
+inline uint64_t make_div_magic(uint32_t d) { return ((1ull << 40) + d - 1) / d; }
 
 // ---------------------------------------------------------------- device helpers
 // Last b in [0, batch) with cu[b] <= q (types.rs CuSeqlensQ::batch_of).

@@ -71,7 +71,10 @@ typedef struct sa_error_detail {
  *   edge_head_base int64 [hkv+1]       exclusive prefix of E_h over heads
  *   edges          int32 [E, 2]        (query, rank) in CSR order across heads
  *   inv            int32 [hkv, tq, topk]  head-local edge position, or -1
- *   units          int32 [U, 4]        work units (head, compact slot, e0, e1)
+ *   units          int32 [U, 8]        work units: head, compact slot, e0, e1 (the
+ *                                      WorkSplit fields of forward.rs), then the
+ *                                      slot's batch b and block blk, lk_b, and d with
+ *                                      causal limit(q) = q + d
  *
  * E (kept edges) is known only on the device. Buffers are sized for the
  * worst case max_edges = tq*hkv*topk. The offsets below are byte offsets
@@ -112,7 +115,9 @@ typedef struct sa_index_info {
  * Checks, in order: batch >= 1 (else CU_SEQLENS); block/page (BLOCK_PAGE);
  * tq, hkv, topk > 0 (EMPTY); hq > 0 and hq % hkv == 0 (HEAD_COUNT);
  * head_dim > 0 (BLOCK_PAGE); max_pages >= 0 (SHAPE "block_tables");
- * head_dim % 4 == 0 and <= 256, tq*hkv*topk*(hq/hkv) < 2^31 (UNSUPPORTED). */
+ * head_dim % 4 == 0 and <= 256, (hq/hkv)*head_dim <= 4096,
+ * tq*hkv*topk*(hq/hkv) < 2^31, block_size < 2^20 and msb*block_size < 2^31
+ * (UNSUPPORTED). */
 sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch,
                         int32_t max_pages, int32_t block_size, int32_t page_size,
                         int32_t hq, int32_t head_dim, int64_t num_pages,

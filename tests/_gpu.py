@@ -50,17 +50,23 @@ def assert_index_equal(idx, ref):
     return info, arrs
 
 
-def check_units(arrs, info, ref, cap_edges):
-    """Units tile [0, E) exactly, each inside one slot, in CSR order per kind."""
+def check_units(arrs, info, ref, cap_edges, w=None):
+    """Units tile [0, E) exactly, each inside one slot, in CSR order per kind;
+    each record's (b, blk, lk, delta) matches its slot."""
     E = info["total_edges"]
     units = np.concatenate([arrs["units_wave"].cpu().numpy(), arrs["units_mfma"].cpu().numpy()])
     cover = np.zeros(E, dtype=np.int64)
-    for h, j, e0, e1 in units:
+    for h, j, e0, e1, b, blk, lk, delta in units:
         assert 0 <= e0 < e1 <= E and e1 - e0 <= cap_edges
         base = ref["edge_head_base"][h]
         lo = base + ref["sel_offsets"][h, j]
         hi = base + ref["sel_offsets"][h, j + 1]
         assert lo <= e0 and e1 <= hi
+        assert ref["sel_slots"][h, j] == b * ref["msb"] + blk
+        assert lk == ref["lk"][b]
+        if w is not None:
+            q0, qo_len = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1] - w.cu_seqlens_q[b])
+            assert delta == (lk - qo_len if lk >= qo_len else 0) - q0
         cover[e0:e1] += 1
     assert np.all(cover == 1)
     for key in ("units_wave", "units_mfma"):

@@ -68,7 +68,7 @@ def test_random_small_end_to_end(seed):
     idx = run_index(w, d)
     ref = oracle_index(w)
     info, arrs = assert_index_equal(idx, ref)
-    check_units(arrs, info, ref, idx.c.cap_edges)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
     out, lse = run_attention(w, d)
     _check_output(w, out, lse)
 
@@ -109,7 +109,7 @@ def test_tiny_workload():
     idx = run_index(w, d)
     ref = oracle_index(w)
     info, arrs = assert_index_equal(idx, ref)
-    check_units(arrs, info, ref, idx.c.cap_edges)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
     out, lse = run_attention(w, d)
     _check_output(w, out, lse)
 
@@ -249,7 +249,7 @@ def test_full_size_workload(name, n_sample):
     idx = run_index(w, d)
     ref = oracle_index(w)
     info, arrs = assert_index_equal(idx, ref)
-    check_units(arrs, info, ref, idx.c.cap_edges)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
     out, lse = run_attention(w, d)
     torch.cuda.synchronize()
     queries = None if n_sample is None else _sample_queries(w, n_sample)
