@@ -68,15 +68,22 @@ def copy_calibration():
 
 
 def variants(name, rotate):
-    """The base workload with K/V, plus rotate-1 more selections/page tables."""
+    """The base workload with K/V, plus rotate-1 more selections/page tables
+    drawn with other seeds. They share one K/V cache, padded with seeded
+    N(0,1) pages when a variant addresses more pages than the base."""
     import workloads as W
     base = W.make_config(name)
     out = [base]
     for r in range(1, rotate):
-        v = W.make_config(name, seed=W.CONFIG_SEEDS[name] + 1000 * r, with_kv=False)
-        assert v.num_pages == base.num_pages
-        out.append(v)
-    return base, out
+        out.append(W.make_config(name, seed=W.CONFIG_SEEDS[name] + 1000 * r, with_kv=False))
+    pages = max(v.num_pages for v in out)
+    k, v = base.k_pages, base.v_pages
+    if pages > base.num_pages:
+        rng = np.random.Generator(np.random.PCG64(W.CONFIG_SEEDS[name] + 99))
+        extra = (pages - base.num_pages,) + k.shape[1:]
+        k = np.concatenate([k, rng.standard_normal(extra, dtype=np.float32)])
+        v = np.concatenate([v, rng.standard_normal(extra, dtype=np.float32)])
+    return base, out, k, v
 
 
 def algorithmic_work(w, arrs, info):
@@ -179,14 +186,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    base, vs = variants(args.config, max(1, args.rotate))
+    base, vs, k_all, v_all = variants(args.config, max(1, args.rotate))
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
-    k = t(base.k_pages, torch.float32)
-    v = t(base.v_pages, torch.float32)
+    k = t(k_all, torch.float32)
+    v = t(v_all, torch.float32)
+    num_pages = int(k_all.shape[0])
+    del k_all, v_all
     sets = []
     for w in vs:
         idx = sa.sa_index_plan(w.tq, w.hkv, w.topk, w.batch, w.max_pages, w.block_size,
-                               w.page_size, w.hq, w.head_dim, base.num_pages).allocate(dev)
+                               w.page_size, w.hq, w.head_dim, num_pages).allocate(dev)
         rows = idx.c.max_edges * (w.hq // w.hkv)
         sets.append({
             "w": w, "idx": idx,

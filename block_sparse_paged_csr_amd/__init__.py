@@ -49,7 +49,7 @@ class SaIndex(Structure):
         ("block_size", c_int32), ("page_size", c_int32), ("hq", c_int32), ("head_dim", c_int32),
         ("num_pages", c_int64), ("pages_per_block", c_int32), ("msb", c_int32),
         ("nbs", c_int64), ("max_edges", c_int64), ("max_units", c_int64),
-        ("cap_edges", c_int32), ("mfma_min_rows", c_int32),
+        ("cap_edges", c_int32), ("wave_cap_edges", c_int32), ("mfma_min_rows", c_int32),
         ("off_header", c_size_t), ("off_sel_slots", c_size_t), ("off_sel_offsets", c_size_t),
         ("off_num_sel", c_size_t), ("off_edge_head_base", c_size_t), ("off_edges", c_size_t),
         ("off_inv", c_size_t), ("off_units_wave", c_size_t), ("off_units_mfma", c_size_t),

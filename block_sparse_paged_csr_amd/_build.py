@@ -14,7 +14,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libsa.so")
 SOURCES = ["sa_api.hip", "sa_index.hip", "sa_forward.hip", "sa_forward_wave.hip",
-           "sa_forward_mfma.hip", "sa_combine.hip"]
+           "sa_forward_small.hip", "sa_forward_mfma.hip", "sa_combine.hip"]
 
 # Packed fp32 VALU forms are kept out of the generated code; the compiler
 # only warns on the host pass that it does not know the feature.

@@ -90,6 +90,7 @@ sa::BuildArgs build_args(const sa_index* idx, const int32_t* selected, const int
   a.msb = idx->msb;
   a.qhead = idx->hq / idx->hkv;
   a.cap_edges = idx->cap_edges;
+  a.wave_cap_edges = idx->wave_cap_edges;
   a.mfma_min_rows = idx->mfma_min_rows;
   return a;
 }
@@ -208,8 +209,12 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch, in
   const bool mfma_ok = head_dim == sa::kMfmaHeadDim && block_size <= sa::kMfmaMaxBlock &&
                        sa::mfma_enabled();
   idx->mfma_min_rows = mfma_ok ? sa::kMfmaMinRows : INT32_MAX;
+  idx->wave_cap_edges = sa::small_kernel_fits(head_dim, block_size, page_size, qhead)
+                            ? (sa::small_kernel_rows() / qhead > 0 ? sa::small_kernel_rows() / qhead : 1)
+                            : idx->cap_edges;
   const int64_t slots = (int64_t)hkv * idx->nbs;
-  idx->max_units = (slots < max_edges ? slots : max_edges) + max_edges / idx->cap_edges + 1;
+  const int32_t min_cap = idx->wave_cap_edges < idx->cap_edges ? idx->wave_cap_edges : idx->cap_edges;
+  idx->max_units = (slots < max_edges ? slots : max_edges) + max_edges / min_cap + 1;
   size_t o = 0;
   idx->off_header = o;          o = align256(o + sizeof(sa::DevHeader));
   idx->off_sel_slots = o;       o = align256(o + 4 * (size_t)slots);

@@ -1,19 +1,36 @@
 // Forward dispatch: the wavefront-reduction kernel takes the units tagged
-// "wave" by the build; the MFMA kernel (when built) takes the others. Both
-// are persistent grids whose unit counts are read on the device, so nothing
-// here waits for the build.
+// "wave" by the build, the MFMA kernel the units tagged "mfma". Both read
+// their unit counts on the device, so nothing here waits for the build.
 #include "sa_internal.h"
 
 namespace sa {
 
-bool mfma_enabled() { return false; }
+unsigned cu_count() {
+  static thread_local int dev_cached = -1;
+  static thread_local unsigned cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != dev_cached) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus = (unsigned)n;
+    dev_cached = dev;
+  }
+  return cus;
+}
 
 hipError_t launch_forward(const sa_index* idx, const FwdArgs& a, hipStream_t s) {
-  // One workgroup per unit up to a cap; past the cap workgroups loop. Units
-  // beyond the device-side count exit at once.
-  const int64_t cap = 16384;
-  const unsigned grid = (unsigned)(idx->max_units < cap ? idx->max_units : cap);
-  return launch_forward_wave(idx, a, s, grid);
+  // Wave path: a persistent grid, never larger than the unit bound.
+  const int64_t cap = 1 << 20;
+  const unsigned max_grid = (unsigned)(idx->max_units < cap ? idx->max_units : cap);
+  hipError_t e = small_kernel_fits(a.head_dim, a.block_size, a.page_size, a.qhead)
+                     ? launch_forward_small(idx, a, s, max_grid)
+                     : launch_forward_wave(idx, a, s, max_grid);
+  if (e != hipSuccess) return e;
+  // MFMA path: one persistent workgroup per CU pulling units from a queue.
+  if (idx->mfma_min_rows != INT32_MAX) e = launch_forward_mfma(idx, a, s, cu_count());
+  return e;
 }
 
 }  // namespace sa

@@ -8,10 +8,10 @@
 //   t < min((blk+1)*bs, lk_b), causally alive positions only; m = max s;
 //   l = sum exp(s - m); o = sum exp(s - m) v_t; nothing alive -> (0, -inf, 0).
 //
-// Latency: a unit costs two dependent memory round trips. (1) The edges'
-// query ids and the chunk's block-table entries go to LDS. (2) The K, V and
-// q loads are issued together. Several workgroups per CU overlap their
-// round trips.
+// Latency: the grid is persistent (a few workgroups per CU, units assigned
+// round-robin). While a unit computes, the workgroup already holds the next
+// unit's record and loads its query ids and first-chunk page ids, so the
+// next unit starts with its K, V and q loads: one dependent round trip.
 //
 // Data movement, per key chunk of KC keys:
 //  * K and V rows are gathered through the block table with 128-bit loads.
@@ -74,6 +74,14 @@ struct WaveCfg {
   static constexpr int MAXPG = KC + 1;              // pages one chunk can touch
 };
 
+// What a unit's first chunk needs before its K/V loads can be issued: the
+// query ids of its first rows and the page ids of its first chunk.
+struct Stage {
+  int32_t qi;       // thread t < kRowsPerPass: query id of row t (or -1)
+  int32_t page;     // thread t < npg: block-table entry of the chunk's page t
+  bool ok;          // the page list fitted in one entry per thread
+};
+
 template <int D4P>
 __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
   using C = WaveCfg<D4P>;
@@ -103,32 +111,79 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
   const int32_t qhead = A.qhead;
   const int64_t page_stride = (int64_t)A.hkv * A.page_size * D;
 
-  for (int32_t u = blockIdx.x; u < num_units; u += gridDim.x) {
-    const Unit unit = P.units_wave[u];
-    const int32_t h = unit.h, e0 = unit.e0, e1 = unit.e1;
-    const int64_t lk = unit.lk;
-    const int64_t block_start = (int64_t)unit.blk * A.block_size;
+  // Loads of a unit's first rows and first-chunk pages (into registers).
+  auto stage_load = [&](const Unit& U) {
+    Stage st{-1, -1, true};
+    const int32_t rows = (U.e1 - U.e0) * qhead;
+    if (tid < kRowsPerPass && tid < rows) st.qi = P.edges[2 * (int64_t)(U.e0 + tid / qhead)];
+    const int64_t bstart = (int64_t)U.blk * A.block_size;
+    int64_t bend = bstart + A.block_size;
+    bend = bend < U.lk ? bend : U.lk;
+    const int32_t nk = bend > bstart ? (int32_t)(bend - bstart) : 0;
+    if (nk > 0) {
+      const int32_t last = (KC < nk ? KC : nk) - 1;
+      const int32_t npg = (int32_t)div_magic((uint32_t)last, A.ps_magic) + 1;
+      st.ok = npg <= 256;
+      if (tid < npg) st.page = A.block_tables[(int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb + tid];
+    }
+    return st;
+  };
+  // Staged values into LDS for the unit about to run.
+  auto stage_store = [&](const Unit& U, const Stage& st) {
+    const int32_t rows = (U.e1 - U.e0) * qhead;
+    if (tid < kRowsPerPass && tid < rows) {
+      s_qoff[tid] = ((int64_t)st.qi * A.hq + (int64_t)U.h * qhead + tid % qhead) * D;
+      s_lim[tid] = A.causal ? st.qi + U.delta : INT32_MAX;
+    }
+    const int64_t head_off = (int64_t)U.h * A.page_size * D;
+    if (tid < C::MAXPG)
+      s_pg[tid] = (st.page >= 0 && st.page < A.num_pages)
+                      ? (int64_t)st.page * page_stride + head_off : -1;
+  };
+
+  int32_t u = blockIdx.x;
+  Unit cur{};
+  bool staged = false;                     // s_qoff / s_lim / s_pg hold cur's first chunk
+  if (u < num_units) {
+    cur = P.units_wave[u];
+    const Stage st = stage_load(cur);
+    stage_store(cur, st);
+    staged = st.ok;
+  }
+
+  while (u < num_units) {
+    const int32_t un = u + gridDim.x;
+    Unit nxt{};
+    if (un < num_units) nxt = P.units_wave[un];          // in flight with cur's loads
+    Stage pre{-1, -1, false};
+    bool have_pre = false;
+
+    const int32_t h = cur.h, e0 = cur.e0, e1 = cur.e1;
+    const int64_t lk = cur.lk;
+    const int64_t block_start = (int64_t)cur.blk * A.block_size;
     int64_t block_end = block_start + A.block_size;
     block_end = block_end < lk ? block_end : lk;
     const int32_t rows = (e1 - e0) * qhead;
     const int64_t row0 = (int64_t)e0 * qhead;                 // first partial row
     const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
-    const int64_t bt_row = (int64_t)unit.b * A.max_pages + (int64_t)unit.blk * A.ppb;
+    const int64_t bt_row = (int64_t)cur.b * A.max_pages + (int64_t)cur.blk * A.ppb;
     const int64_t head_off = (int64_t)h * A.page_size * D;
 
     for (int32_t pass0 = 0; pass0 < rows; pass0 += kRowsPerPass) {
       const int32_t prow = rows - pass0 < kRowsPerPass ? rows - pass0 : kRowsPerPass;
-      __syncthreads();                                        // previous pass fully stored
-      // ---- round trip 1: query ids of the pass's rows
-      if (tid < kRowsPerPass) {
-        s_m[tid] = -INFINITY;
-        s_l[tid] = 0.f;
+      if (!staged) {
+        // rows of a later pass: query ids fetched now
+        __syncthreads();
         if (tid < prow) {
           const int32_t ur = pass0 + tid;
           const int32_t qi = P.edges[2 * (int64_t)(e0 + ur / qhead)];
           s_qoff[tid] = ((int64_t)qi * A.hq + (int64_t)h * qhead + ur % qhead) * D;
-          s_lim[tid] = A.causal ? qi + unit.delta : INT32_MAX;
+          s_lim[tid] = A.causal ? qi + cur.delta : INT32_MAX;
         }
+      }
+      if (tid < kRowsPerPass) {
+        s_m[tid] = -INFINITY;
+        s_l[tid] = 0.f;
       }
       for (int x = tid; x < kRowsPerPass * D4P; x += 256)
         s_o[x / D4P][x % D4P] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -137,13 +192,15 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
         const int32_t pg0 = (int32_t)div_magic((uint32_t)cp, A.ps_magic);
         const int32_t last = (cp + KC < nkeys ? cp + KC : nkeys) - 1;
         const int32_t npg = (int32_t)div_magic((uint32_t)last, A.ps_magic) - pg0 + 1;
-        if (cp > 0) __syncthreads();                           // s_pg of the last chunk read
-        for (int x = tid; x < npg; x += 256) {
-          const int32_t page = A.block_tables[bt_row + pg0 + x];
-          s_pg[x] = (page >= 0 && page < A.num_pages) ? (int64_t)page * page_stride + head_off : -1;
+        if (!(staged && cp == 0 && npg <= 256)) {
+          __syncthreads();                                     // s_pg no longer read
+          for (int x = tid; x < npg; x += 256) {
+            const int32_t page = A.block_tables[bt_row + pg0 + x];
+            s_pg[x] = (page >= 0 && page < A.num_pages) ? (int64_t)page * page_stride + head_off : -1;
+          }
         }
         __syncthreads();
-        // ---- round trip 2: K, V (this chunk) and, on the first chunk, q
+        // ---- K, V (this chunk) and, on the first chunk, q
         float4 kr[NI], vr[NI];
         {
           const int32_t tb = cp + kq;
@@ -172,6 +229,12 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
             s_q[r][c] = c < D4 ? ld4(A.q + s_qoff[r] + c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
           }
           __syncthreads();
+          if (pass0 == 0 && un < num_units) {
+            // The next unit's record has arrived with this chunk's loads; its
+            // first-chunk loads now overlap this unit's compute.
+            pre = stage_load(nxt);
+            have_pre = true;
+          }
         }
 
         for (int32_t g0 = 0; g0 < prow; g0 += kRowsPerGroup) {
@@ -279,12 +342,33 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
         A.m[row0 + pass0 + tid] = (m2 == -INFINITY) ? -INFINITY : m2 * kLn2;
         A.l[row0 + pass0 + tid] = s_l[tid];
       }
+      staged = false;
     }
+    // ---- hand over to the next unit
+    __syncthreads();                                          // all LDS reads of cur done
+    if (un < num_units) {
+      if (!have_pre) pre = stage_load(nxt);                   // cur had no keys or rows
+      stage_store(nxt, pre);
+      staged = pre.ok;
+    }
+    cur = nxt;
+    u = un;
   }
 }
 
 template <int D4P>
-hipError_t launch_wave_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned grid) {
+hipError_t launch_wave_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned max_grid) {
+  // Persistent grid: as many workgroups as fit on the device at once.
+  static thread_local int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_wave<D4P>, 256, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  unsigned grid = (unsigned)per_cu * cu_count();
+  if (grid > max_grid) grid = max_grid;
+  if (grid < 1) grid = 1;
   hipLaunchKernelGGL(k_fwd_wave<D4P>, dim3(grid), dim3(256), 0, s, P, a);
   return hipGetLastError();
 }

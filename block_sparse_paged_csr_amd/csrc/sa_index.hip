@@ -44,17 +44,17 @@ __device__ inline int4 wave_incl_scan4(int4 v) {
   return v;
 }
 
-// Units of a slot with c edges: k = ceil(c / cap) near-equal parts. Part i
-// spans [floor(i*c/k), floor((i+1)*c/k)), so sizes are floor(c/k) or one
-// more. A part goes to the MFMA kernel iff its size is at least thr_e.
-__device__ inline void unit_split(int c, int cap, int thr_e, int* n_wave, int* n_mfma) {
-  if (c <= 0) { *n_wave = 0; *n_mfma = 0; return; }
-  const int k = (c + cap - 1) / cap;
-  const int lo = c / k;
-  const int n_hi = c % k;
-  if (lo >= thr_e) { *n_wave = 0; *n_mfma = k; }
-  else if (lo + 1 >= thr_e) { *n_wave = k - n_hi; *n_mfma = n_hi; }
-  else { *n_wave = k; *n_mfma = 0; }
+// Units of a slot with c edges. A slot with at least thr_e edges (rows >=
+// the MFMA minimum) becomes ceil(c / cap) MFMA units; a smaller one becomes
+// ceil(c / wave_cap) wavefront units. Part i of k spans
+// [floor(i*c/k), floor((i+1)*c/k)), so the parts of a slot are near-equal.
+__device__ inline void unit_split(int c, int cap, int wave_cap, int thr_e, int* n_wave,
+                                  int* n_mfma) {
+  *n_wave = 0;
+  *n_mfma = 0;
+  if (c <= 0) return;
+  if (c >= thr_e) *n_mfma = (c + cap - 1) / cap;
+  else *n_wave = (c + wave_cap - 1) / wave_cap;
 }
 
 __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kScanThreads) void k_index_scan(IndexPtrs P, BuildA
     }
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
-      unit_split(c[k], cap, thr_e, &nw[k], &nm[k]);
+      unit_split(c[k], cap, A.wave_cap_edges, thr_e, &nw[k], &nm[k]);
       mine = add4(mine, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
     }
     const int4 incl = wave_incl_scan4(mine);
@@ -376,29 +376,17 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
   // Work units of this wave's slot, in CSR order within each kind.
   const SlotInfo si = s_slot[w];
   if (si.n == 0) return;
-  const int32_t cap = A.cap_edges;
   const int32_t thr_e = (int32_t)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
+  const bool is_m = si.n >= thr_e;
+  const int32_t cap = is_m ? A.cap_edges : A.wave_cap_edges;
   const int32_t k_units = (si.n + cap - 1) / cap;
-  int32_t uw = si.uw, um = si.um;
+  Unit* dst = is_m ? P.units_mfma + si.um : P.units_wave + si.uw;
   const int64_t e_base = si.base + si.off0;
-  for (int32_t i0 = 0; i0 < k_units; i0 += 64) {
-    const int32_t i = i0 + lane;
-    const bool active = i < k_units;
-    int32_t s0 = 0, s1 = 0;
-    if (active) {
-      s0 = (int32_t)(((int64_t)i * si.n) / k_units);
-      s1 = (int32_t)(((int64_t)(i + 1) * si.n) / k_units);
-    }
-    const bool is_m = active && (s1 - s0) >= thr_e;
-    const bool is_w = active && !is_m;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const uint64_t bm = __ballot(is_m), bw = __ballot(is_w);
-    const Unit u{si.h, si.j, (int32_t)(e_base + s0), (int32_t)(e_base + s1),
-                 si.b, si.blk, si.lk, si.delta};
-    if (is_m) P.units_mfma[um + __popcll(bm & below)] = u;
-    if (is_w) P.units_wave[uw + __popcll(bw & below)] = u;
-    um += __popcll(bm);
-    uw += __popcll(bw);
+  for (int32_t i = lane; i < k_units; i += 64) {
+    const int32_t s0 = (int32_t)(((int64_t)i * si.n) / k_units);
+    const int32_t s1 = (int32_t)(((int64_t)(i + 1) * si.n) / k_units);
+    dst[i] = Unit{si.h, si.j, (int32_t)(e_base + s0), (int32_t)(e_base + s1),
+                  si.b, si.blk, si.lk, si.delta};
   }
 }
 

@@ -112,7 +112,7 @@ struct BuildArgs {
   int64_t nbs;
   int64_t num_pages;
   int32_t hkv, topk, batch, max_pages, block_size, page_size, ppb, msb;
-  int32_t qhead, cap_edges, mfma_min_rows;
+  int32_t qhead, cap_edges, wave_cap_edges, mfma_min_rows;
 };
 
 struct FwdArgs {
@@ -149,15 +149,23 @@ ScratchLayout scratch_layout(const sa_index* idx);
 
 // Whether the MFMA forward kernel is part of this build.
 bool mfma_enabled();
+// Compute units of the current device (cached per host thread).
+unsigned cu_count();
 
 // Launchers (enqueue only; return hipSuccess or the launch error).
 hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s);
 hipError_t launch_forward(const sa_index* idx, const FwdArgs& a, hipStream_t s);
 hipError_t launch_combine(const sa_index* idx, const CombineArgs& a, hipStream_t s);
 hipError_t launch_forward_wave(const sa_index* idx, const FwdArgs& a, hipStream_t s,
-                               unsigned grid);
+                               unsigned max_grid);
 hipError_t launch_forward_mfma(const sa_index* idx, const FwdArgs& a, hipStream_t s,
                                unsigned grid);
+hipError_t launch_forward_small(const sa_index* idx, const FwdArgs& a, hipStream_t s,
+                                unsigned max_grid);
+// The small-unit kernel: head_dim 128, blocks of <= 64 keys, qhead <= 16;
+// its units hold at most small_kernel_rows() rows.
+bool small_kernel_fits(int head_dim, int block_size, int page_size, int qhead);
+int small_kernel_rows();
 
 // Exact n / d for n * d < 2^40 with magic = ceil(2^40 / d).
 __host__ __device__ inline uint32_t div_magic(uint32_t n, uint64_t magic) {

@@ -90,8 +90,9 @@ typedef struct sa_index {
   int64_t nbs;               /* batch * msb */
   int64_t max_edges;         /* tq * hkv * topk */
   int64_t max_units;
-  int32_t cap_edges;         /* most edges in one work unit */
-  int32_t mfma_min_rows;     /* units with at least this many rows use MFMA */
+  int32_t cap_edges;         /* most edges in one MFMA work unit */
+  int32_t wave_cap_edges;    /* most edges in one wavefront-path work unit */
+  int32_t mfma_min_rows;     /* slots with at least this many rows use MFMA */
   size_t off_header, off_sel_slots, off_sel_offsets, off_num_sel, off_edge_head_base,
          off_edges, off_inv, off_units_wave, off_units_mfma, off_scratch;
 } sa_index;
@@ -145,9 +146,9 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch,
  * (SELECTED_RANGE); the first block-table entry >= num_pages, in memory
  * order, among pages that a kept block's valid range touches (SHAPE
  * "block_tables page id").
- * Work units split each slot into ceil(n / cap_edges) near-equal ranges
- * (consecutive in CSR order); units with at least mfma_min_rows rows are
- * listed for the MFMA kernel, the others for the wavefront kernel. */
+ * Work units split each slot of n edges into near-equal, consecutive ranges:
+ * ceil(n / cap_edges) units for the MFMA kernel if n*(hq/hkv) >= mfma_min_rows,
+ * else ceil(n / wave_cap_edges) units for the wavefront kernels. */
 sa_status sa_build_index(const int32_t* selected, int64_t selected_len,
                          const int32_t* block_tables, int64_t block_tables_len,
                          const int64_t* cu_seqlens_q, int64_t cu_len,
