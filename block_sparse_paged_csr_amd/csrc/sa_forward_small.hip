@@ -6,21 +6,29 @@
 // process_work_unit over the block's valid, causally alive positions, like the
 // other forward kernels.
 //
-// One workgroup of 4 waves per unit. Wave w owns keys 16w..16w+15 of the block,
-// and the unit's (up to) 16 rows form one 16x16 tile on fp32 matrix cores
-// (v_mfma_f32_16x16x4f32):
-//   S^T[key, row] = K[key, :] . Q[row, :]   lane group g = lane/16 takes d = 32g..32g+31
-//   O^T[d, row] += V[key, d] * P[row, key]  output row i of an MFMA block stands for
-//                                           d = 8*i + db, so a lane's V reads and O
-//                                           writes are contiguous
-// Each wave then holds a partial (o, m, l) over its 16 keys. The four are
-// merged with the log-sum-exp rule through LDS, so no lane reduction crosses
-// waves until the end.
+// One wavefront per unit, no workgroup barriers: the four waves of a
+// workgroup run independent unit streams (units w0, w0 + NW, w0 + 2 NW, ... for
+// NW waves in the grid). The unit's (up to) 16 rows form one 16x16 tile on
+// fp32 matrix cores (v_mfma_f32_16x16x4f32) and its block is streamed in
+// pieces of 16 keys: first the K pieces (scores of all keys stay in registers),
+// then the exact softmax over the block, then the V pieces. The contraction
+// index d is permuted so that loads cover whole cache lines:
+//   S^T[key, row] = K[key, :] . Q[row, :]   MFMA t, component c, lane group g = lane/16
+//                                           takes d = 16t + 4g + c: the four lanes of a
+//                                           key read 64 contiguous bytes per load
+//   O^T[d, row] += V[key, d] * P[row, key]  output row i of MFMA block db stands for
+//                                           d = 4i + (db & 3) + 64 (db >> 2): the 16
+//                                           lanes of a key read 256 contiguous bytes
 //
-// Latency: workgroups are persistent (units round-robin) and pipelined over
-// three stages. While unit u computes, the block-table entries and query ids
-// of unit u+G and the record of unit u+2G are in flight. Unit u+G therefore
-// starts with its K, V and q loads, one round trip.
+// Latency: the next piece (the next unit's first K piece at the end of a unit)
+// is in flight while a piece computes, and the next unit's query rows load
+// during the V pieces. Unit metadata runs further ahead through small per-wave
+// LDS rings: at a unit's first piece the record of unit j+3 and the
+// block-table entries and query ids of unit j+2 are fetched. A unit's pieces
+// are unrolled, so every load count is static and the compiler waits for
+// exactly the piece it needs.
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -28,22 +36,43 @@ namespace sa {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+// Pointers into device global memory, so loads through them (also through a
+// pointer chosen between two of them) stay global_load rather than flat_load.
+typedef const __attribute__((address_space(1))) float gfloat;
+typedef const __attribute__((address_space(1))) floatx4 gfloatx4;
+typedef const __attribute__((address_space(1))) int32_t gint;
 
 constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+constexpr int kPiece = 16;          // keys per piece
 constexpr int kMaxKeys = 64;        // block_size <= 64
 constexpr int kRows = 16;           // rows per unit
-constexpr int kMaxPages = 64;       // block_size / page_size <= 64
+constexpr int kRecRing = 4;         // records of units j .. j+3
+constexpr int kMetaRing = 3;        // key offsets / validity / query ids of units j .. j+2
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// What a unit needs before its K/V/q loads: its record, page offsets
-// (element offset of page slot pl for head h, or -1) and query ids per row.
-struct Meta {
-  int32_t rec[8];                   // a Unit
-  int64_t pg[kMaxPages];
-  int32_t qi[kRows];
+// A lane with nothing to load reads this zero line instead and gets zeros,
+// so every load is issued and the loads stay countable.
+__device__ const float g_zero[kD] = {};
+__device__ inline gfloat* zero_line() { return (gfloat*)g_zero; }
+
+struct WaveLds {
+  int32_t rec[kRecRing][8];         // Unit records
+  int64_t ko[kMetaRing][kMaxKeys];  // element offset of each key's K/V row, or -1
+  uint64_t vm[kMetaRing];           // bit t: key t of the block is inside it and on a page
+  int32_t qi[kMetaRing][kRows];     // query id of each row
 };
+
+// One piece of a unit in registers: 8 float4 a lane.
+//   K piece c: x[t] = K[key 16c + li][16t + 4g .. +3]
+//   V piece c: x[2r + h] = V[key 16c + 4g + r][4li + 64h .. +3]
+struct Piece {
+  floatx4 x[8];
+};
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 __device__ inline Unit as_unit(const int32_t* r) {
   return Unit{r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]};
@@ -53,237 +82,281 @@ __device__ inline floatx4 zero4() {
   z[0] = z[1] = z[2] = z[3] = 0.f;
   return z;
 }
+__device__ inline int32_t unit_keys(const Unit& U, int32_t block_size) {
+  const int64_t start = (int64_t)U.blk * block_size;
+  int64_t end = start + block_size;
+  end = end < U.lk ? end : (int64_t)U.lk;
+  return end > start ? (int32_t)(end - start) : 0;
+}
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_fwd_small(IndexPtrs P, FwdArgs A) {
-  __shared__ Meta s_meta[2];
-  __shared__ __align__(16) float s_ow[kWaves][kRows][kD];   // per-wave partial o
-  __shared__ float s_mw[kWaves][kRows], s_lw[kWaves][kRows];
+// Element offset of key t of unit U (head U.h) on page `page`, or -1 when t is
+// past the block's keys or the page id is outside [0, num_pages).
+__device__ inline int64_t key_offset(const FwdArgs& A, int64_t page_stride, const Unit& U, int t,
+                                     int32_t page) {
+  const int32_t pl = (int32_t)div_magic((uint32_t)t, A.ps_magic);
+  return (t < unit_keys(U, A.block_size) && page >= 0 && page < A.num_pages)
+             ? (int64_t)page * page_stride + ((int64_t)U.h * A.page_size + (t - pl * A.page_size)) * kD
+             : -1;
+}
+// Block-table entry holding key t of unit U (t clamped into the block).
+__device__ inline gint* page_id_ptr(const FwdArgs& A, const Unit& U, int t) {
+  const int32_t tt = t < A.block_size ? t : 0;
+  const int32_t pl = (int32_t)div_magic((uint32_t)tt, A.ps_magic);
+  return (gint*)(A.block_tables + (int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb + pl);
+}
+
+// NCH = pieces per block side (ceil(block_size / 16)); a unit takes 2 NCH steps.
+template <int NCH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_small(IndexPtrs P, FwdArgs A) {
+  __shared__ WaveLds s_wave[kWaves];
 
   const DevHeader* hdr = P.hdr;
   if (hdr->status != SA_OK) return;
   const int32_t num_units = hdr->num_units_wave;
-  const int32_t G = gridDim.x;
-  int32_t u = blockIdx.x;
-  if (u >= num_units) return;
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
+  const int32_t NW = (int32_t)gridDim.x * kWaves;
+  const int32_t u0 = (int32_t)blockIdx.x * kWaves + w;
+  if (u0 >= num_units) return;       // waves never synchronise with each other
+  WaveLds& S = s_wave[w];
+
   const int32_t qhead = A.qhead;
   const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
   const int32_t* units = reinterpret_cast<const int32_t*>(P.units_wave);
+  const int32_t n_units = (num_units - u0 + NW - 1) / NW;
+  gint* zi = (gint*)zero_line();
 
-  // page offsets of a unit, one per thread t < ppb
-  auto page_off = [&](const Unit& U, int t) -> int64_t {
-    const int32_t page = A.block_tables[(int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb + t];
-    return (page >= 0 && page < A.num_pages)
-               ? (int64_t)page * page_stride + (int64_t)U.h * A.page_size * kD : -1;
+  auto rec_ptr = [&](int32_t j, bool ok) -> gint* {
+    return ok ? (gint*)(units + 8 * (int64_t)(u0 + j * NW) + (lane & 7)) : zi;
   };
-  auto query_of = [&](const Unit& U, int r) -> int32_t {
-    return P.edges[2 * (int64_t)(U.e0 + r / qhead)];
+  auto qid_ptr = [&](const Unit& U, bool ok) -> gint* {
+    const int r = lane < kRows ? lane : 0;
+    return (ok && r < (U.e1 - U.e0) * qhead) ? (gint*)(P.edges + 2 * (int64_t)(U.e0 + r / qhead)) : zi;
+  };
+  auto stage_meta = [&](int ms, const Unit& U, int32_t page, int32_t qid) {
+    const int64_t ko = key_offset(A, page_stride, U, lane, page);
+    S.ko[ms][lane] = ko;
+    const uint64_t vm = __ballot(ko >= 0);
+    if (lane == 0) S.vm[ms] = vm;
+    if (lane < kRows) S.qi[ms][lane] = qid;
+  };
+  // Issue piece pk (K pieces 0..NCH-1, then V pieces) of the unit in meta slot ms.
+  auto load_piece = [&](auto pkc, int ms, bool live, Piece& pc) __attribute__((always_inline)) {
+    constexpr int pk = decltype(pkc)::value;
+    if constexpr (pk < NCH) {
+      const int64_t kb = S.ko[ms][kPiece * pk + li];
+      gfloat* kp = (live && kb >= 0 ? (gfloat*)(A.k + kb) : zero_line()) + 4 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pc.x[t] = *(gfloatx4*)(kp + 16 * t);
+    } else {
+      constexpr int c = pk - NCH;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t kb = S.ko[ms][kPiece * c + 4 * g + r];
+        gfloat* vp = (live && kb >= 0 ? (gfloat*)(A.v + kb) : zero_line()) + 4 * li;
+        pc.x[2 * r] = *(gfloatx4*)vp;
+        pc.x[2 * r + 1] = *(gfloatx4*)(vp + 64);
+      }
+    }
+  };
+  // The B operand of the unit in record slot rs / meta slot ms: row li,
+  // d = 16t + 4g .. +3 in q[t]; zero past its rows.
+  auto load_q = [&](int rs, int ms, bool live, floatx4 (&q)[8]) __attribute__((always_inline)) {
+    const Unit U = as_unit(S.rec[rs]);
+    const int32_t rows = live ? (U.e1 - U.e0) * qhead : 0;
+    const int64_t qrow = (int64_t)S.qi[ms][li] * A.hq + (int64_t)U.h * qhead + li % qhead;
+    gfloat* src = (li < rows ? (gfloat*)(A.q + qrow * kD) : zero_line()) + 4 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = *(gfloatx4*)(src + 16 * t);
   };
 
-  // ---- prologue: unit u staged in slot 0, record of u + G in slot 1
-  int cur = 0;
+  // ---- prologue: records of units 0..2, metadata of units 0 and 1, q and the first piece of unit 0
   {
-    if (tid < 8) s_meta[0].rec[tid] = units[8 * (int64_t)u + tid];
-    if (tid < 8 && u + G < num_units) s_meta[1].rec[tid] = units[8 * (int64_t)(u + G) + tid];
-    __syncthreads();
-    const Unit U = as_unit(s_meta[0].rec);
-    if (tid < A.ppb) s_meta[0].pg[tid] = page_off(U, tid);
-    if (tid < kRows && tid < (U.e1 - U.e0) * qhead) s_meta[0].qi[tid] = query_of(U, tid);
-    __syncthreads();
+    int32_t rv[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) rv[j] = *rec_ptr(j, j < n_units);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (lane < 8) S.rec[j][lane] = rv[j];
+    int32_t pg[2], qv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const Unit U = as_unit(S.rec[j]);
+      pg[j] = *(j < n_units ? page_id_ptr(A, U, lane) : zi);
+      qv[j] = *qid_ptr(U, j < n_units);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) stage_meta(j, as_unit(S.rec[j]), pg[j], qv[j]);
   }
+  floatx4 qreg[8];
+  load_q(0, 0, true, qreg);
+  Piece bufA, bufB;
+  load_piece(IC<0>{}, 0, true, bufA);
 
-  while (true) {
-    const Meta& M = s_meta[cur];
-    const Unit U = as_unit(M.rec);
+  for (int32_t j = 0; j < n_units; ++j) {
+    const int rs = j & (kRecRing - 1), ms = j % kMetaRing;
+    const int rs1 = (j + 1) & (kRecRing - 1), ms1 = (j + 1) % kMetaRing;
+    const int rs2 = (j + 2) & (kRecRing - 1), ms2 = (j + 2) % kMetaRing;
+    const bool ok1 = j + 1 < n_units;
+
+    const Unit U = as_unit(S.rec[rs]);
     const int32_t rows = (U.e1 - U.e0) * qhead;
-    const int64_t row0 = (int64_t)U.e0 * qhead;
-    const int64_t block_start = (int64_t)U.blk * A.block_size;
-    int64_t block_end = block_start + A.block_size;
-    block_end = block_end < U.lk ? block_end : (int64_t)U.lk;
-    const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
-
-    // ---- K (this wave's 16 keys, d = 32g..32g+31) and V (keys 16w+4g+r, d = 8li..8li+7)
-    float4 kr[8];
-    {
-      const int32_t key = 16 * w + li;
-      int64_t base = -1;
-      if (key < nkeys) {
-        const int32_t pl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
-        base = M.pg[pl];
-        if (base >= 0) base += (int64_t)(key - pl * A.page_size) * kD;
-      }
-      const float* kp = A.k + base + 32 * g;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        kr[t] = base >= 0 ? *reinterpret_cast<const float4*>(kp + 4 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float4 vr[4][2];
-    uint32_t vvalid = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int32_t key = 16 * w + 4 * g + r;
-      int64_t base = -1;
-      if (key < nkeys) {
-        const int32_t pl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
-        base = M.pg[pl];
-        if (base >= 0) base += (int64_t)(key - pl * A.page_size) * kD;
-      }
-      const float* vp = A.v + base + 8 * li;
-      vr[r][0] = base >= 0 ? *reinterpret_cast<const float4*>(vp) : make_float4(0.f, 0.f, 0.f, 0.f);
-      vr[r][1] = base >= 0 ? *reinterpret_cast<const float4*>(vp + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      vvalid |= (base >= 0 ? 1u : 0u) << r;
-    }
-    // ---- q rows of the tile (B operand): row li, d = 32g..32g+31
-    float4 qr[8];
     const bool row_ok = li < rows;
-    const int32_t qi = row_ok ? M.qi[li] : 0;
-    {
-      const float* qp = A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + (row_ok ? li % qhead : 0)) * kD + 32 * g;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        qr[t] = row_ok ? *reinterpret_cast<const float4*>(qp + 4 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    // ---- prefetch: metadata of unit u + G, record of unit u + 2G
-    const int nxt = cur ^ 1;
-    const bool has_n = u + G < num_units;
-    int64_t pre_pg = -1;
-    int32_t pre_qi = 0, pre_rec = 0;
-    Unit Un{};
-    if (has_n) {
-      Un = as_unit(s_meta[nxt].rec);
-      if (tid < A.ppb) pre_pg = page_off(Un, tid);
-      if (tid < kRows && tid < (Un.e1 - Un.e0) * qhead) pre_qi = query_of(Un, tid);
-    }
-    const bool has_nn = u + 2 * G < num_units;
-    if (has_nn && tid < 8) pre_rec = units[8 * (int64_t)(u + 2 * G) + tid];
-
-    // ---- S^T = K . Q^T
-    floatx4 sacc = zero4();
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[t].x, qr[t].x, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[t].y, qr[t].y, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[t].z, qr[t].z, sacc, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[t].w, qr[t].w, sacc, 0, 0, 0);
-    }
-    // ---- mask and this wave's softmax stats for row li (base 2)
-    int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
+    const int64_t block_start = (int64_t)U.blk * A.block_size;
+    const int32_t nkeys = unit_keys(U, A.block_size);
+    const uint64_t vm = S.vm[ms];
+    int64_t klim = A.causal ? (int64_t)S.qi[ms][li] + U.delta - block_start : (int64_t)nkeys - 1;
     klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
-    const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim) - (16 * w + 4 * g);
-    float mw = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool alive = row_ok && ((vvalid >> r) & 1u) && r <= kmax;
-      sacc[r] = alive ? sacc[r] * A.scale_log2 : -INFINITY;
-      mw = fmaxf(mw, sacc[r]);
-    }
-    mw = fmaxf(mw, __shfl_xor(mw, 16, 64));
-    mw = fmaxf(mw, __shfl_xor(mw, 32, 64));
-    float lw = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = sacc[r] == -INFINITY ? 0.f : exp2f(sacc[r] - mw);
-      sacc[r] = p;
-      lw += p;
-    }
-    lw += __shfl_xor(lw, 16, 64);
-    lw += __shfl_xor(lw, 32, 64);
+    const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);   // last alive key of row li
 
-    // ---- O^T = V^T . P^T (row i of block db stands for d = 8i + db)
+    float sreg[NCH][4];
     floatx4 oacc[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[db] = zero4();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32((&vr[r][0].x)[db], sacc[r], oacc[db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        oacc[4 + db] = __builtin_amdgcn_mfma_f32_16x16x4f32((&vr[r][1].x)[db], sacc[r], oacc[4 + db], 0, 0, 0);
-    }
-    // lane (li, g) holds row li, d = 32g + 8v + db in oacc[db][v]
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float* dst = &s_ow[w][li][32 * g + 8 * v];
-      *reinterpret_cast<float4*>(dst) = make_float4(oacc[0][v], oacc[1][v], oacc[2][v], oacc[3][v]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(oacc[4][v], oacc[5][v], oacc[6][v], oacc[7][v]);
-    }
-    if (g == 0) {
-      s_mw[w][li] = mw;
-      s_lw[w][li] = lw;
-    }
-    __syncthreads();
+    float m_row = -INFINITY, l_row = 0.f;
+    int32_t pre_rec = 0, pre_page = 0, pre_qi = 0;
 
-    // ---- merge the four waves' partials, store the unit's rows
+    auto step = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k < 2 * NCH) {
+        Piece& cur = (k & 1) ? bufB : bufA;
+        Piece& nxt = (k & 1) ? bufA : bufB;
+        // ---- loads ahead: metadata (first step), the next piece, the next unit's q
+        if constexpr (k == 0) {
+          const Unit U2 = as_unit(S.rec[rs2]);
+          pre_rec = *rec_ptr(j + 3, j + 3 < n_units);
+          pre_page = *(j + 2 < n_units ? page_id_ptr(A, U2, lane) : zi);
+          pre_qi = *qid_ptr(U2, j + 2 < n_units);
+        }
+        if constexpr (k + 1 < 2 * NCH) load_piece(IC<k + 1>{}, ms, true, nxt);
+        else load_piece(IC<0>{}, ms1, ok1, nxt);
+        if constexpr (k == NCH) load_q(rs1, ms1, ok1, qreg);
+        // keep the loads above the math: the scheduler would otherwise sink
+        // them below it to share registers with `cur`
+        __builtin_amdgcn_sched_barrier(0);
+
+        if constexpr (k < NCH) {
+          // ---- scores of piece k: S^T = K . Q^T
+          floatx4 sa0 = zero4(), sa1 = zero4();
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int x = tid + k * kThreads;              // (row, float4 column)
-      const int j = x >> 5, c = x & 31;
-      if (j < rows) {
-        float big = s_mw[0][j];
+          for (int t = 0; t < 8; t += 2) {
+            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].x, qreg[t].x, sa0, 0, 0, 0);
+            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].x, qreg[t + 1].x, sa1, 0, 0, 0);
+            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].y, qreg[t].y, sa0, 0, 0, 0);
+            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].y, qreg[t + 1].y, sa1, 0, 0, 0);
+            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].z, qreg[t].z, sa0, 0, 0, 0);
+            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].z, qreg[t + 1].z, sa1, 0, 0, 0);
+            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].w, qreg[t].w, sa0, 0, 0, 0);
+            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].w, qreg[t + 1].w, sa1, 0, 0, 0);
+          }
+          const floatx4 s = sa0 + sa1;    // lane (li, g), reg r: key 16k + 4g + r, row li
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) big = fmaxf(big, s_mw[ww][j]);
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        float lsum = 0.f;
-        if (big != -INFINITY) {
+          for (int r = 0; r < 4; ++r) {
+            const int key = kPiece * k + 4 * g + r;
+            const bool alive = row_ok && ((vm >> key) & 1ull) && key <= kmax;
+            sreg[k][r] = alive ? s[r] * A.scale_log2 : -INFINITY;
+          }
+          if constexpr (k == NCH - 1) {
+            // ---- softmax of row li over the whole block (base 2)
+            float mx = -INFINITY;
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) {
-            const float mwv = s_mw[ww][j];
-            const float f = mwv == -INFINITY ? 0.f : exp2f(mwv - big);
-            const float4 ov = *reinterpret_cast<const float4*>(&s_ow[ww][j][4 * c]);
-            o = make_float4(fmaf(ov.x, f, o.x), fmaf(ov.y, f, o.y), fmaf(ov.z, f, o.z), fmaf(ov.w, f, o.w));
-            lsum = fmaf(s_lw[ww][j], f, lsum);
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sreg[c][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            float ls = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float p = sreg[c][r] == -INFINITY ? 0.f : exp2f(sreg[c][r] - mx);
+                sreg[c][r] = p;
+                ls += p;
+              }
+            ls += __shfl_xor(ls, 16, 64);
+            ls += __shfl_xor(ls, 32, 64);
+            m_row = mx;
+            l_row = ls;
+          }
+        } else {
+          // ---- O^T += V^T . P^T for piece c (row i of block db: d = 4i + (db & 3) + 64 (db >> 2))
+          constexpr int c = k - NCH;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+              const floatx4 acc = (c == 0 && r == 0) ? zero4() : oacc[db];
+              oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[2 * r + (db >> 2)][db & 3], sreg[c][r],
+                                                              acc, 0, 0, 0);
+            }
           }
         }
-        *reinterpret_cast<float4*>(A.o + (row0 + j) * kD + 4 * c) = o;
-        if (c == 0) {
-          A.m[row0 + j] = big == -INFINITY ? -INFINITY : big * kLn2;
-          A.l[row0 + j] = lsum;
+
+        if constexpr (k == 1) {
+          // ---- stage the metadata fetched at the first step
+          if (lane < 8) S.rec[(j + 3) & (kRecRing - 1)][lane] = pre_rec;
+          stage_meta(ms2, as_unit(S.rec[rs2]), pre_page, pre_qi);
+        }
+        if constexpr (k == 2 * NCH - 1) {
+          // ---- the unit's partials: lane (li, g) holds row li,
+          // d = 16g + 4v + (db & 3) + 64 (db >> 2) in oacc[db][v]
+          if (row_ok) {
+            const int64_t row = (int64_t)U.e0 * qhead + li;
+            float* dst = A.o + row * kD + 16 * g;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              *reinterpret_cast<floatx4*>(dst + 4 * v) =
+                  floatx4{oacc[0][v], oacc[1][v], oacc[2][v], oacc[3][v]};
+              *reinterpret_cast<floatx4*>(dst + 64 + 4 * v) =
+                  floatx4{oacc[4][v], oacc[5][v], oacc[6][v], oacc[7][v]};
+            }
+            if (g == 0) {
+              A.m[row] = m_row == -INFINITY ? -INFINITY : m_row * kLn2;
+              A.l[row] = l_row;
+            }
+          }
         }
       }
-    }
-
-    // ---- hand over: stage unit u + G, keep the record of u + 2G
-    if (!has_n) break;
-    if (has_n) {
-      if (tid < A.ppb) s_meta[nxt].pg[tid] = pre_pg;
-      if (tid < kRows && tid < (Un.e1 - Un.e0) * qhead) s_meta[nxt].qi[tid] = pre_qi;
-    }
-    __syncthreads();                                  // s_meta[cur] and s_ow reads done
-    if (has_nn && tid < 8) s_meta[cur].rec[tid] = pre_rec;
-    __syncthreads();
-    cur = nxt;
-    u += G;
+    };
+    step(IC<0>{}); step(IC<1>{}); step(IC<2>{}); step(IC<3>{});
+    step(IC<4>{}); step(IC<5>{}); step(IC<6>{}); step(IC<7>{});
   }
+}
+
+template <int NCH>
+hipError_t launch_nch(const sa_index* idx, const FwdArgs& a, hipStream_t s, unsigned max_units) {
+  static thread_local int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_small<NCH>, kThreads, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  // one wave per unit stream
+  unsigned grid = (unsigned)per_cu * cu_count();
+  const unsigned need = (max_units + kWaves - 1) / kWaves;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k_fwd_small<NCH>, dim3(grid), dim3(kThreads), 0, s, index_ptrs(idx), a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 bool small_kernel_fits(int head_dim, int block_size, int page_size, int qhead) {
-  return head_dim == kD && block_size <= kMaxKeys && block_size / page_size <= kMaxPages &&
-         qhead <= kRows;
+  (void)page_size;
+  return head_dim == kD && block_size <= kMaxKeys && qhead <= kRows;
 }
 
 int small_kernel_rows() { return kRows; }
 
 hipError_t launch_forward_small(const sa_index* idx, const FwdArgs& a, hipStream_t s,
-                                unsigned max_grid) {
-  static thread_local int per_cu = 0;
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_small, kThreads, 0) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
+                                unsigned max_units) {
+  switch ((a.block_size + kPiece - 1) / kPiece) {
+    case 1: return launch_nch<1>(idx, a, s, max_units);
+    case 2: return launch_nch<2>(idx, a, s, max_units);
+    case 3: return launch_nch<3>(idx, a, s, max_units);
+    default: return launch_nch<4>(idx, a, s, max_units);
   }
-  unsigned grid = (unsigned)per_cu * cu_count();
-  if (grid > max_grid) grid = max_grid;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_fwd_small, dim3(grid), dim3(kThreads), 0, s, index_ptrs(idx), a);
-  return hipGetLastError();
 }
 
 }  // namespace sa
