@@ -2,6 +2,8 @@
 // checks in the order of the pages' kvouter_forward (alice-llm 2.0.0
 // forward.rs) and of the builder's field docs (types.rs), dispatch of the
 // kernels on the caller's stream, and the device-status readback.
+#include <atomic>
+#include <chrono>
 #include <climits>
 #include <cstdio>
 #include <cstring>
@@ -11,6 +13,22 @@
 namespace {
 
 thread_local sa_error_detail g_last = {SA_OK, "", 0, 0};
+
+// Build epochs: distinct per build call in this process, started at a value
+// mixed from the clock and an address so that flags left in a reused buffer
+// by another process do not match.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{[] {
+    uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    x ^= (uint64_t)(uintptr_t)&g_last * 0x9E3779B97F4A7C15ull;
+    x ^= x >> 31;
+    x *= 0xBF58476D1CE4E5B9ull;
+    x ^= x >> 29;
+    return x | 1ull;
+  }()};
+  uint64_t e = counter.fetch_add(2, std::memory_order_relaxed);
+  return e == 0 ? 1 : e;
+}
 
 sa_status fail(sa_status st, const char* what = "", int64_t expected = 0, int64_t got = 0) {
   g_last.status = st;
@@ -92,6 +110,9 @@ sa::BuildArgs build_args(const sa_index* idx, const int32_t* selected, const int
   a.cap_edges = idx->cap_edges;
   a.wave_cap_edges = idx->wave_cap_edges;
   a.mfma_min_rows = idx->mfma_min_rows;
+  a.epoch = next_epoch();
+  a.cap_magic = sa::make_div_magic((uint32_t)(a.cap_edges > 0 ? a.cap_edges : 1));
+  a.wave_cap_magic = sa::make_div_magic((uint32_t)(a.wave_cap_edges > 0 ? a.wave_cap_edges : 1));
   return a;
 }
 
@@ -111,6 +132,7 @@ ScratchLayout scratch_layout(const sa_index* idx) {
   L.head_um = o; o = align256(o + 4 * (size_t)idx->hkv);
   L.keys = o;    o = align256(o + 4 * (size_t)idx->max_edges);
   L.qinfo = o;   o = align256(o + 8 * (size_t)idx->tq);
+  L.agg = o;     o = align256(o + sizeof(HeadAgg) * (size_t)idx->hkv);
   L.end = o;
   return L;
 }
@@ -136,6 +158,7 @@ IndexPtrs index_ptrs(const sa_index* idx) {
   P.head_um = reinterpret_cast<int32_t*>(b + L.head_um);
   P.keys = reinterpret_cast<int32_t*>(b + L.keys);
   P.qinfo = reinterpret_cast<int2*>(b + L.qinfo);
+  P.agg = reinterpret_cast<HeadAgg*>(b + L.agg);
   return P;
 }
 

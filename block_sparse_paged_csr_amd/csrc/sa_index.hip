@@ -14,6 +14,15 @@
 //   k_index_rank     per compact slot: rank of each key inside the segment
 //                    (keys are unique) -> edges and inv in (q, r) order, then
 //                    the slot's work units; workgroup 0 fills the header
+//
+// Small problems (a head's tq * topk entries and its slots fit one
+// workgroup's LDS, as in decode) take one kernel instead, k_index_fused: a
+// workgroup per head runs the same steps on LDS counters and member lists, and
+// the heads' edge and unit bases come from a decoupled look-back over per-head
+// totals that each workgroup publishes.
+#include <cstddef>
+#include <cstdlib>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -225,6 +234,32 @@ __global__ __launch_bounds__(256) void k_index_scatter(IndexPtrs P, BuildArgs A)
   P.keys[hb + pos] = (int32_t)(q * A.topk + r);
 }
 
+// Status and error details from the smallest error key (~0ull: none).
+__device__ void set_status(DevHeader* hd, const BuildArgs& A, unsigned long long key) {
+  if (key == ~0ull) { hd->status = SA_OK; return; }
+  const uint64_t rank = key >> 56;
+  const int64_t pos = (int64_t)(key & ((1ull << 56) - 1));
+  if (rank == kRankCuContent) {
+    hd->status = SA_ERR_CU_SEQLENS;
+  } else if (rank == kRankCuTotal) {
+    hd->status = SA_ERR_SHAPE;
+    hd->what_code = kWhatCuTotal;
+    hd->err_expected = A.tq;
+    hd->err_got = A.cu[A.batch];
+  } else if (rank == kRankSelected) {
+    hd->status = SA_ERR_SELECTED_RANGE;
+    hd->err_expected = A.msb;
+    hd->err_got = A.selected[pos];
+  } else if (rank == kRankPage) {
+    hd->status = SA_ERR_SHAPE;
+    hd->what_code = kWhatPageId;
+    hd->err_expected = A.num_pages;
+    hd->err_got = A.block_tables[pos];
+  } else {
+    hd->status = SA_ERR_GPU_RUNTIME;
+  }
+}
+
 __device__ void finalize_header(const IndexPtrs& P, const BuildArgs& A) {
   int64_t e = 0, ns = 0;
   int32_t uw = 0, um = 0;
@@ -241,27 +276,7 @@ __device__ void finalize_header(const IndexPtrs& P, const BuildArgs& A) {
   hd->num_units_wave = uw;
   hd->num_units_mfma = um;
   hd->num_slots = ns;
-  const unsigned long long key = hd->err_key;
-  if (key == ~0ull) { hd->status = SA_OK; return; }
-  const uint64_t rank = key >> 56;
-  const int64_t pos = (int64_t)(key & ((1ull << 56) - 1));
-  if (rank == kRankCuContent) {
-    hd->status = SA_ERR_CU_SEQLENS;
-  } else if (rank == kRankCuTotal) {
-    hd->status = SA_ERR_SHAPE;
-    hd->what_code = kWhatCuTotal;
-    hd->err_expected = A.tq;
-    hd->err_got = A.cu[A.batch];
-  } else if (rank == kRankSelected) {
-    hd->status = SA_ERR_SELECTED_RANGE;
-    hd->err_expected = A.msb;
-    hd->err_got = A.selected[pos];
-  } else {
-    hd->status = SA_ERR_SHAPE;
-    hd->what_code = kWhatPageId;
-    hd->err_expected = A.num_pages;
-    hd->err_got = A.block_tables[pos];
-  }
+  set_status(hd, A, hd->err_key);
 }
 
 constexpr int kRankChunk = 2048;   // keys staged in LDS per pass
@@ -390,6 +405,397 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
   }
 }
 
+// ------------------------------------------------------------ fused build
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedItems = 4;                       // entries per thread and head
+constexpr int64_t kFusedMaxSlots = 16384;
+constexpr int64_t kFusedMaxQ = 2048;
+constexpr int32_t kFusedMaxBatch = 2048;
+constexpr size_t kFusedMaxLds = 150 * 1024;            // dynamic LDS of the fused build
+constexpr int kLookbackSpins = 1 << 22;              // then the build reports a runtime error
+constexpr uint64_t kRankLookback = 5;                // error rank: a head's totals never appeared
+
+// Inclusive wave64 scans on DPP: row_shr 1, 2, 4, 8 inside each row of 16
+// lanes, then row_bcast 15 and 31 carry row totals across rows (rows the
+// broadcast does not write keep the identity).
+__device__ inline uint32_t wave_incl_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+__device__ inline int wave_incl_max(int v) {
+  int t;
+  t = __builtin_amdgcn_update_dpp(-1, v, 0x111, 0xf, 0xf, false); v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(-1, v, 0x112, 0xf, 0xf, false); v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(-1, v, 0x114, 0xf, 0xf, false); v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(-1, v, 0x118, 0xf, 0xf, false); v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(-1, v, 0x142, 0xa, 0xf, false); v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(-1, v, 0x143, 0xc, 0xf, false); v = v > t ? v : t;
+  return v;
+}
+
+// Exclusive scan of two packed sums over the workgroup (kFusedThreads);
+// *ta / *tb get the totals.
+__device__ uint2 block_excl_scan2(uint32_t a, uint32_t b, uint2* s_w, uint32_t* ta, uint32_t* tb) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t ia = wave_incl_sum(a), ib = wave_incl_sum(b);
+  if (lane == 63) s_w[wid] = make_uint2(ia, ib);
+  __syncthreads();
+  if (wid == 0) {
+    const uint2 w = lane < kFusedThreads / 64 ? s_w[lane] : make_uint2(0u, 0u);
+    const uint32_t wa = wave_incl_sum(w.x), wb = wave_incl_sum(w.y);
+    if (lane < kFusedThreads / 64) s_w[lane] = make_uint2(wa, wb);
+  }
+  __syncthreads();
+  uint2 ex = make_uint2(ia - a, ib - b);
+  if (wid > 0) {
+    ex.x += s_w[wid - 1].x;
+    ex.y += s_w[wid - 1].y;
+  }
+  *ta = s_w[kFusedThreads / 64 - 1].x;
+  *tb = s_w[kFusedThreads / 64 - 1].y;
+  __syncthreads();
+  return ex;
+}
+
+// Max over the values of lower threads (-1 if none).
+__device__ int block_excl_max(int v, int* s_w) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int incl = wave_incl_max(v);
+  if (lane == 63) s_w[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < kFusedThreads / 64 ? s_w[lane] : -1;
+    w = wave_incl_max(w);
+    if (lane < kFusedThreads / 64) s_w[lane] = w;
+  }
+  __syncthreads();
+  int ex = __builtin_amdgcn_update_dpp(-1, incl, 0x138, 0xf, 0xf, false);   // wave_shr:1
+  if (wid > 0) ex = ex > s_w[wid - 1] ? ex : s_w[wid - 1];
+  __syncthreads();
+  return ex;
+}
+
+// Packed per-slot sums for the fused scans: (edges | nonempty << 16) and
+// (wavefront units | MFMA units << 16); a head has at most 4096 entries, so
+// no field carries into the next.
+__device__ inline uint2 slot_sums(int c, const BuildArgs& A, int thr_e) {
+  if (c <= 0) return make_uint2(0u, 0u);
+  const bool is_m = c >= thr_e;
+  const uint32_t n = is_m ? div_magic((uint32_t)(c + A.cap_edges - 1), A.cap_magic)
+                          : div_magic((uint32_t)(c + A.wave_cap_edges - 1), A.wave_cap_magic);
+  return make_uint2((uint32_t)c | (1u << 16), is_m ? n << 16 : n);
+}
+
+// Per (h, raw slot) counts of kept entries, their exclusive offsets, the
+// member list of each slot and each entry's rank in it, the compact slot list
+// and the slot's units, all for head h = blockIdx.x. Entry i = q * topk + r
+// of the head is handled by thread i % 1024. Dynamic LDS (int32): counts, then
+// offsets [nbs]; member lists [tq*topk]; compact slot list and unit offsets
+// [min(nbs, tq*topk)] each; batch of each query [tq]; lk and causal delta per
+// sequence [batch] each.
+__global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, BuildArgs A) {
+  extern __shared__ int32_t s_dyn[];
+  __shared__ uint2 s_w2[kFusedThreads / 64];
+  __shared__ int s_w1[kFusedThreads / 64];
+  __shared__ unsigned long long s_err;
+  __shared__ unsigned long long s_base_e, s_base_ns;
+  __shared__ int32_t s_base_uw, s_base_um;
+
+  const int32_t h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nbs = A.nbs;
+  const int32_t tq = (int32_t)A.tq, topk = A.topk, hkv = A.hkv, batch = A.batch;
+  const int32_t items = tq * topk;
+  const int32_t nslots = (int32_t)nbs;          // nbs <= kFusedMaxSlots
+  const int32_t nlist = nslots < items ? nslots : items;   // nonempty slots <= both
+  int32_t* s_cnt = s_dyn;                       // [nbs]   counts, then offsets
+  int32_t* s_mem = s_cnt + nslots;              // [items] member lists
+  int32_t* s_list = s_mem + items;              // [nlist] raw slot of compact slot j
+  uint32_t* s_uoff = reinterpret_cast<uint32_t*>(s_list + nlist);  // [nlist] unit offsets
+  int32_t* s_qb = reinterpret_cast<int32_t*>(s_uoff + nlist);      // [tq]
+  int32_t* s_lkb = s_qb + tq;                   // [batch]
+  int32_t* s_dlb = s_lkb + batch;               // [batch]
+
+  // this thread's entries of `selected`, loaded first so that their latency
+  // overlaps the per-sequence setup
+  int32_t v_k[kFusedItems];
+#pragma unroll
+  for (int k = 0; k < kFusedItems; ++k) {
+    const int32_t i = tid + kFusedThreads * k;
+    const int32_t q = i / topk, r = i - q * topk;
+    v_k[k] = i < items ? A.selected[((int64_t)q * hkv + h) * topk + r] : -1;
+  }
+
+  // ---- per-sequence lk and causal delta; batch of each query; cu checks
+  for (int32_t x = tid; x < nslots; x += kFusedThreads) s_cnt[x] = 0;
+  for (int32_t q = tid; q < tq; q += kFusedThreads) s_qb[q] = -1;
+  if (tid == 0) {
+    s_err = ~0ull;
+    s_base_e = 0;
+    s_base_ns = 0;
+    s_base_uw = 0;
+    s_base_um = 0;
+  }
+  __syncthreads();
+  for (int32_t b = tid; b < batch; b += kFusedThreads) {
+    const int64_t c0 = A.cu[b], c1 = A.cu[b + 1];
+    const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
+    const int64_t qo_len = c1 - c0;
+    s_lkb[b] = (int32_t)lk;
+    s_dlb[b] = (int32_t)((lk >= qo_len ? lk - qo_len : 0) - c0);
+    // cu_seqlens content (types.rs CuSeqlensQ::new): non-decreasing
+    if (h == 0 && c1 < c0) atomicMin(&s_err, err_key(kRankCuContent, b + 1));
+    if (c0 < c1 && c0 >= 0 && c0 < tq) s_qb[c0] = b;   // first query of a nonempty sequence
+  }
+  if (h == 0 && tid == 0) {
+    if (A.cu[0] != 0) atomicMin(&s_err, err_key(kRankCuContent, 0));
+    if (A.cu[batch] != A.tq) atomicMin(&s_err, err_key(kRankCuTotal, 0));
+  }
+  __syncthreads();
+  {
+    // batch of q = last sequence starting at or before q (types.rs batch_of)
+    int v[4], m = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int32_t q = 4 * tid + k;
+      v[k] = q < tq ? s_qb[q] : -1;
+      m = v[k] > m ? v[k] : m;
+      v[k] = m;
+    }
+    const int pre = block_excl_max(m, s_w1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int32_t q = 4 * tid + k;
+      if (q < tq) s_qb[q] = v[k] > pre ? v[k] : pre;
+    }
+  }
+  __syncthreads();
+
+  // ---- entries: drop padding and blocks past lk, flag bad ids and pages, count
+  int32_t slot_k[kFusedItems], arr_k[kFusedItems];
+#pragma unroll
+  for (int k = 0; k < kFusedItems; ++k) {
+    slot_k[k] = -1;
+    arr_k[k] = 0;
+    const int32_t i = tid + kFusedThreads * k;
+    if (i >= items) continue;
+    const int32_t q = i / topk, r = i - q * topk;
+    const int64_t idx = ((int64_t)q * hkv + h) * topk + r;
+    const int32_t v = v_k[k];
+    if (v == -1) continue;
+    if (v < -1 || v >= A.msb) {
+      atomicMin(&s_err, err_key(kRankSelected, (uint64_t)idx));
+      continue;
+    }
+    const int32_t b = s_qb[q];
+    if (b < 0) continue;                              // only with a cu error
+    const int64_t lk = s_lkb[b];
+    const int64_t block_start = (int64_t)v * A.block_size;
+    if (block_start >= lk) continue;
+    if (A.num_pages >= 0) {
+      const int64_t block_end = block_start + A.block_size < lk ? block_start + A.block_size : lk;
+      const int64_t col0 = (int64_t)b * A.max_pages + (int64_t)v * A.ppb;
+      int64_t bad = INT64_MAX;
+      for (int32_t pl = 0; pl < A.ppb; ++pl) {
+        const bool touched = block_start + (int64_t)pl * A.page_size < block_end;
+        const int32_t page = touched ? A.block_tables[col0 + pl] : -1;
+        if (page >= A.num_pages && col0 + pl < bad) bad = col0 + pl;
+      }
+      if (bad != INT64_MAX) atomicMin(&s_err, err_key(kRankPage, (uint64_t)bad));
+    }
+    const int32_t slot = b * A.msb + v;
+    slot_k[k] = slot;
+    arr_k[k] = atomicAdd(&s_cnt[slot], 1);            // arrival order, made stable below
+  }
+  __syncthreads();
+
+  // ---- one scan over the slots: counts -> exclusive offsets (in place), the
+  // compact list of nonempty slots with their unit offsets, head totals
+  const int32_t thr_e = (int32_t)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
+  const int32_t per = (nslots + kFusedThreads - 1) / kFusedThreads;   // slots [tid*per, +per)
+  int32_t e_h, ns_h, uw_h, um_h;
+  {
+    uint2 mine = make_uint2(0u, 0u);
+    for (int32_t x = 0; x < per; ++x) {
+      const int32_t sl = tid * per + x;
+      const uint2 t = slot_sums(sl < nslots ? s_cnt[sl] : 0, A, thr_e);
+      mine.x += t.x;
+      mine.y += t.y;
+    }
+    uint32_t ta, tb;
+    uint2 run = block_excl_scan2(mine.x, mine.y, s_w2, &ta, &tb);
+    e_h = (int32_t)(ta & 0xffffu);
+    ns_h = (int32_t)(ta >> 16);
+    uw_h = (int32_t)(tb & 0xffffu);
+    um_h = (int32_t)(tb >> 16);
+    for (int32_t x = 0; x < per; ++x) {
+      const int32_t sl = tid * per + x;
+      if (sl >= nslots) break;
+      const int32_t c = s_cnt[sl];
+      s_cnt[sl] = (int32_t)(run.x & 0xffffu);
+      if (c > 0) {
+        const int32_t j = (int32_t)(run.x >> 16);
+        s_list[j] = sl;
+        s_uoff[j] = run.y;
+      }
+      const uint2 t = slot_sums(c, A, thr_e);
+      run.x += t.x;
+      run.y += t.y;
+    }
+  }
+  // publish this head's totals (all of its error keys are in by now)
+  if (tid == 0) {
+    HeadAgg* ag = P.agg + h;
+    ag->e = e_h;
+    ag->ns = ns_h;
+    ag->uw = uw_h;
+    ag->um = um_h;
+    ag->err = s_err;
+    __hip_atomic_store(&ag->flag, A.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+
+  // ---- member list of each slot (arrival order)
+#pragma unroll
+  for (int k = 0; k < kFusedItems; ++k)
+    if (slot_k[k] >= 0) s_mem[s_cnt[slot_k[k]] + arr_k[k]] = tid + kFusedThreads * k;
+  __syncthreads();
+
+  // ---- head-local outputs, before waiting for the other heads: the rank of
+  // each entry in its slot (members with a smaller entry index) gives inv;
+  // compact slots and plateaued offsets
+  int32_t inv_k[kFusedItems];
+#pragma unroll
+  for (int k = 0; k < kFusedItems; ++k) {
+    const int32_t i = tid + kFusedThreads * k;
+    inv_k[k] = -1;
+    if (i >= items) continue;
+    const int32_t q = i / topk, r = i - q * topk;
+    if (slot_k[k] >= 0) {
+      const int32_t sl = slot_k[k];
+      const int32_t off = s_cnt[sl];
+      const int32_t end = sl + 1 < nslots ? s_cnt[sl + 1] : e_h;
+      int32_t rank = 0;
+      for (int32_t x = off; x < end; ++x) rank += s_mem[x] < i;
+      inv_k[k] = off + rank;
+    }
+    P.inv[((int64_t)h * tq + q) * topk + r] = inv_k[k];
+  }
+  for (int32_t j = tid; j < ns_h; j += kFusedThreads) {
+    const int32_t sl = s_list[j];
+    P.sel_slots[(int64_t)h * nbs + j] = sl;
+    P.sel_offsets[(int64_t)h * (nbs + 1) + j] = s_cnt[sl];
+  }
+  for (int64_t j = ns_h + tid; j < nbs; j += kFusedThreads) P.sel_slots[(int64_t)h * nbs + j] = -1;
+  for (int64_t j = ns_h + tid; j <= nbs; j += kFusedThreads)
+    P.sel_offsets[(int64_t)h * (nbs + 1) + j] = e_h;
+
+  // ---- look-back: totals of the heads before h (all heads for the last one)
+  for (int32_t hh = tid; hh < h; hh += kFusedThreads) {
+    const HeadAgg* ag = P.agg + hh;
+    int spins = 0;
+    while (__hip_atomic_load(&ag->flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != A.epoch &&
+           spins < kLookbackSpins) {
+      __builtin_amdgcn_s_sleep(1);
+      ++spins;
+    }
+    if (spins >= kLookbackSpins) {
+      atomicMin(&s_err, err_key(kRankLookback, 0));
+      continue;
+    }
+    // bytes 0..31 of the HeadAgg in two 16-byte loads: w0 = (e lo, e hi, ns, uw),
+    // w1 = (um, pad, err lo, err hi)
+    static_assert(offsetof(HeadAgg, ns) == 8 && offsetof(HeadAgg, um) == 16 &&
+                  offsetof(HeadAgg, err) == 24, "HeadAgg layout");
+    const int4 w0 = *reinterpret_cast<const int4*>(ag);
+    const int4 w1 = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ag) + 16);
+    const unsigned long long e = (unsigned long long)(uint32_t)w0.x | ((unsigned long long)(uint32_t)w0.y << 32);
+    const unsigned long long err = (unsigned long long)(uint32_t)w1.z | ((unsigned long long)(uint32_t)w1.w << 32);
+    atomicAdd(&s_base_e, e);
+    atomicAdd(&s_base_ns, (unsigned long long)w0.z);
+    atomicAdd(&s_base_uw, w0.w);
+    atomicAdd(&s_base_um, w1.x);
+    atomicMin(&s_err, err);
+  }
+  __syncthreads();
+  const int64_t hb = (int64_t)s_base_e;
+  const int32_t uw0 = s_base_uw, um0 = s_base_um;
+
+  // ---- edges in (q, r) order inside each slot
+#pragma unroll
+  for (int k = 0; k < kFusedItems; ++k) {
+    if (inv_k[k] < 0) continue;
+    const int32_t i = tid + kFusedThreads * k;
+    const int32_t q = i / topk, r = i - q * topk;
+    *reinterpret_cast<int2*>(P.edges + 2 * (hb + inv_k[k])) = make_int2(q, r);
+  }
+  // ---- the slots' units: ceil(c / cap) near-equal parts
+  for (int32_t j = tid; j < ns_h; j += kFusedThreads) {
+    const int32_t sl = s_list[j];
+    const int32_t off = s_cnt[sl];
+    const int32_t c = (j + 1 < ns_h ? s_cnt[s_list[j + 1]] : e_h) - off;
+    const uint32_t t = slot_sums(c, A, thr_e).y, uo = s_uoff[j];
+    const bool is_m = c >= thr_e;
+    const int32_t k_units = is_m ? (int32_t)(t >> 16) : (int32_t)(t & 0xffffu);
+    Unit* dst = is_m ? P.units_mfma + um0 + (int32_t)(uo >> 16) : P.units_wave + uw0 + (int32_t)(uo & 0xffffu);
+    const int32_t b = sl / A.msb, blk = sl - b * A.msb;
+    const int32_t e_base = (int32_t)(hb + off);
+    const int32_t lk = s_lkb[b], dl = s_dlb[b];
+    // part u of k_units spans [u * c / k_units, (u + 1) * c / k_units): c <= 4096
+    for (int32_t u = 0; u < k_units; ++u) {
+      const int32_t s0 = (u * c) / k_units, s1 = ((u + 1) * c) / k_units;
+      dst[u] = Unit{h, j, e_base + s0, e_base + s1, b, blk, lk, dl};
+    }
+  }
+  if (tid == 0) {
+    P.num_sel[h] = ns_h;
+    P.edge_head_base[h] = hb;
+    if (h == hkv - 1) {
+      // the last head has looked back over all others: the header
+      P.edge_head_base[hkv] = hb + e_h;
+      DevHeader* hd = P.hdr;
+      hd->what_code = kWhatNone;
+      hd->err_expected = 0;
+      hd->err_got = 0;
+      hd->total_edges = hb + e_h;
+      hd->num_units_wave = uw0 + uw_h;
+      hd->num_units_mfma = um0 + um_h;
+      hd->num_slots = (int64_t)s_base_ns + ns_h;
+      hd->queue_mfma = 0;
+      hd->done_mfma = 0;
+      hd->queue_wave = 0;
+      hd->done_wave = 0;
+      hd->geom[0] = (int32_t)A.tq;
+      hd->geom[1] = A.hkv;
+      hd->geom[2] = A.topk;
+      hd->geom[3] = A.batch;
+      hd->geom[4] = A.max_pages;
+      hd->geom[5] = A.block_size;
+      hd->geom[6] = A.page_size;
+      hd->geom[7] = A.qhead;
+      hd->err_key = s_err;
+      set_status(hd, A, s_err);
+    }
+  }
+}
+
+size_t fused_lds_bytes(const BuildArgs& a) {
+  const size_t items = (size_t)a.tq * a.topk;
+  const size_t nlist = (size_t)a.nbs < items ? (size_t)a.nbs : items;
+  return 4 * ((size_t)a.nbs + items + 2 * nlist + (size_t)a.tq + 2 * (size_t)a.batch);
+}
+
+bool fused_fits(const BuildArgs& a) {
+  return a.tq * a.topk <= (int64_t)kFusedThreads * kFusedItems && a.nbs <= kFusedMaxSlots &&
+         a.tq <= kFusedMaxQ && a.batch <= kFusedMaxBatch && a.hkv <= 65535 &&
+         fused_lds_bytes(a) <= kFusedMaxLds;
+}
+
 inline unsigned grid_for(int64_t n, int per) {
   int64_t g = (n + per - 1) / per;
   return (unsigned)(g < 1 ? 1 : g);
@@ -399,6 +805,21 @@ inline unsigned grid_for(int64_t n, int per) {
 
 hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) {
   const IndexPtrs P = index_ptrs(idx);
+  // SA_BUILD_MULTIKERNEL=1 keeps small problems on the multi-kernel build
+  // (both paths produce the same index; tests cover each).
+  const char* force_multi = std::getenv("SA_BUILD_MULTIKERNEL");
+  const bool multi = force_multi != nullptr && force_multi[0] == '1';
+  if (!multi && fused_fits(a)) {
+    static bool attr_set = false;
+    const size_t lds = fused_lds_bytes(a);
+    if (!attr_set) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(k_index_fused),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(k_index_fused, dim3((unsigned)a.hkv), dim3(kFusedThreads), lds, s, P, a);
+    return hipGetLastError();
+  }
   const int64_t slots = (int64_t)a.hkv * a.nbs;
   int64_t init_grid = ((slots > a.tq ? slots : a.tq) + 255) / 256;
   if (init_grid > 2048) init_grid = 2048;

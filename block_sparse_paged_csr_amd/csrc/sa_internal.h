@@ -79,7 +79,17 @@ struct ScratchLayout {
   size_t head_um;    // int32 [hkv]
   size_t keys;       // int32 [max_edges] scattered (q*topk + r), unordered per slot
   size_t qinfo;      // int2  [tq]        (sequence b, resolved kv length lk_b) per query
+  size_t agg;        // HeadAgg [hkv]     per-head totals published by the fused build
   size_t end;
+};
+
+// Totals of one head, published by the fused build's workgroup for that head
+// (flag == that build's epoch once the fields are written).
+struct alignas(64) HeadAgg {
+  int64_t e;                  // edges
+  int32_t ns, uw, um, pad;    // nonempty slots, wavefront units, MFMA units
+  unsigned long long err;     // smallest error key seen by the head (~0ull: none)
+  uint64_t flag;
 };
 
 // Plain pointers into one index buffer.
@@ -101,6 +111,7 @@ struct IndexPtrs {
   int32_t* head_um;
   int32_t* keys;
   int2* qinfo;
+  HeadAgg* agg;
 };
 
 struct BuildArgs {
@@ -113,6 +124,9 @@ struct BuildArgs {
   int64_t num_pages;
   int32_t hkv, topk, batch, max_pages, block_size, page_size, ppb, msb;
   int32_t qhead, cap_edges, wave_cap_edges, mfma_min_rows;
+  uint64_t epoch;            // distinct per build call; tags the fused build's HeadAgg flags
+  uint64_t cap_magic;        // make_div_magic(cap_edges)
+  uint64_t wave_cap_magic;   // make_div_magic(wave_cap_edges)
 };
 
 struct FwdArgs {

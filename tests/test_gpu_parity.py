@@ -55,6 +55,17 @@ def _check_output(w, out, lse, queries=None):
     return err
 
 
+@pytest.fixture(params=["fused", "multi"])
+def build_path(request, monkeypatch):
+    """Small problems build in one fused kernel; SA_BUILD_MULTIKERNEL=1 keeps
+    them on the multi-kernel build that large problems take."""
+    if request.param == "multi":
+        monkeypatch.setenv("SA_BUILD_MULTIKERNEL", "1")
+    else:
+        monkeypatch.delenv("SA_BUILD_MULTIKERNEL", raising=False)
+    return request.param
+
+
 # ------------------------------------------------------------------ small cases
 
 @pytest.mark.parametrize("seed", range(24))
@@ -64,6 +75,42 @@ def test_random_small_end_to_end(seed):
                       page_size=[1, 2, 4][seed % 3], pages_per_block=1 + seed % 3,
                       topk=1 + seed % 5)
     _print_case("random_small", seed=seed, tq=w.tq, d=w.head_dim)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+    out, lse = run_attention(w, d)
+    _check_output(w, out, lse)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_small_index_multikernel(seed, monkeypatch):
+    monkeypatch.setenv("SA_BUILD_MULTIKERNEL", "1")
+    w = W.make_random(500 + seed, batch=1 + seed % 3, qo_max=5, kv_max=40,
+                      hkv=1 + seed % 2, qhead=1 + seed % 4, head_dim=8,
+                      page_size=[1, 2, 4][seed % 3], pages_per_block=1 + seed % 3,
+                      topk=1 + seed % 5)
+    _print_case("random_small_multikernel", seed=seed, tq=w.tq)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+
+
+# head_dim 128 with blocks of at most 64 keys: the one-wave-per-unit forward,
+# with 1..4 pieces of 16 keys per block, partial pieces and up to 16 rows a unit
+D128_GEOM = [(4, 1), (2, 8), (8, 2), (16, 1), (4, 6), (8, 4), (16, 3), (16, 4), (2, 3), (32, 2)]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_d128_end_to_end(seed):
+    ps, ppb = D128_GEOM[seed % len(D128_GEOM)]
+    w = W.make_random(1300 + seed, batch=1 + seed % 4, qo_max=6, kv_max=260,
+                      hkv=1 + seed % 3, qhead=[1, 2, 4, 8, 16][seed % 5], head_dim=128,
+                      page_size=ps, pages_per_block=ppb, topk=1 + seed % 6)
+    _print_case("random_d128", seed=seed, tq=w.tq, bs=w.block_size, qhead=w.hq // w.hkv)
     d = dev_inputs(w)
     idx = run_index(w, d)
     ref = oracle_index(w)
@@ -116,7 +163,7 @@ def test_tiny_workload():
 
 @pytest.mark.parametrize("name", ["pages_small_fixture_index.json", "pages_gqa_fixture_index.json",
                                   "handmade_index.json"])
-def test_golden_index_on_gpu(golden_dir, name):
+def test_golden_index_on_gpu(golden_dir, name, build_path):
     import json
     import os
     with open(os.path.join(golden_dir, name)) as f:
@@ -165,7 +212,7 @@ def _oracle_error(w, **over):
     return ei.value
 
 
-def test_device_error_selected_out_of_range():
+def test_device_error_selected_out_of_range(build_path):
     w = W.make_random(31, batch=2, hkv=2, topk=3)
     msb = w.max_pages // (w.block_size // w.page_size)
     sel = w.selected.copy()
@@ -178,7 +225,7 @@ def test_device_error_selected_out_of_range():
     assert (got.got, got.expected) == (ref.got, ref.expected) == (-3, msb)
 
 
-def test_device_error_cu_seqlens():
+def test_device_error_cu_seqlens(build_path):
     w = W.make_random(32, batch=3, hkv=1, topk=2)
     d = dev_inputs(w)
     cu = w.cu_seqlens_q.copy()
@@ -192,7 +239,7 @@ def test_device_error_cu_seqlens():
                                                            w.tq, int(cu[-1]))
 
 
-def test_device_error_page_id(golden_dir):
+def test_device_error_page_id(golden_dir, build_path):
     import json
     import os
     with open(os.path.join(golden_dir, "handmade_index.json")) as f:
