@@ -6,11 +6,12 @@
 // inv[h, q, r] >= 0 it reads partial row p = (edge_head_base[h] + inv)*qhead + qh
 // and forms M = max m_p, L = sum l_p e^(m_p - M), O = sum o_p e^(m_p - M) / L.
 //
-// Ranks go in tiles of kRankTile. A tile's partial-row offsets and (m, l)
-// are staged in LDS first, so the o reads of a tile do not depend on each
-// other and are all in flight together. Across tiles the running (M, L, O)
-// is rescaled. The qhead rows of one edge are contiguous, so each rank is one
-// coalesced read of qhead*D floats.
+// Latency: the index reads (status, head base, the ranks' inv) are issued
+// together; then, per tile of kRankTile ranks, every item loads its rows' m,
+// l and o float4 at once (none of them waits on another), so a tile costs one
+// round trip. The running (M, L, O) is rescaled across tiles. The qhead rows
+// of one edge are contiguous, so each rank is one coalesced read of
+// qhead*D floats by the workgroup.
 #include "sa_internal.h"
 
 namespace sa {
@@ -18,94 +19,74 @@ namespace sa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRankTile = 64;
-constexpr int kMaxItems = 1;          // work items per thread (qhead * D4 <= blockDim <= 1024)
+constexpr int kRankTile = 16;
+constexpr int kMaxBlock = 1024;      // qhead * D4 <= 1024: one item per thread
 
-__global__ __launch_bounds__(1024) void k_combine(IndexPtrs P, CombineArgs A) {
-  if (P.hdr->status != SA_OK) return;
-  extern __shared__ __align__(16) unsigned char smem[];
+__global__ __launch_bounds__(kMaxBlock) void k_combine(IndexPtrs P, CombineArgs A) {
   const int32_t qhead = A.qhead;
-  int64_t* s_row = reinterpret_cast<int64_t*>(smem);                     // [kRankTile]
-  float* s_m = reinterpret_cast<float*>(smem + 8 * kRankTile);           // [kRankTile][qhead]
-  float* s_l = s_m + kRankTile * qhead;                                  // [kRankTile][qhead]
-
   const int64_t q = blockIdx.x / A.hkv;
   const int32_t h = blockIdx.x % A.hkv;
   const int32_t D4 = A.head_dim >> 2;
-  const int32_t n_items = qhead * D4;
-  const int64_t head_base = P.edge_head_base[h];
+  const int x = threadIdx.x;
+  const int qh = x / D4, c = x - qh * D4;
+  const bool item = qh < qhead;
   const int32_t* inv = P.inv + ((int64_t)h * A.tq + q) * A.topk;
-  const int tid = threadIdx.x, nthr = blockDim.x;
 
-  float big[kMaxItems], total[kMaxItems];
-  float4 acc[kMaxItems];
-#pragma unroll
-  for (int k = 0; k < kMaxItems; ++k) {
-    big[k] = -INFINITY;
-    total[k] = 0.f;
-    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  // independent reads first
+  const int32_t status = P.hdr->status;
+  const int64_t head_base = P.edge_head_base[h];
+  if (status != SA_OK) return;
 
+  float big = -INFINITY, total = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int32_t r0 = 0; r0 < A.topk; r0 += kRankTile) {
-    const int32_t nr = A.topk - r0 < kRankTile ? A.topk - r0 : kRankTile;
-    __syncthreads();
-    for (int t = tid; t < nr; t += nthr) {
-      const int32_t p = inv[r0 + t];
-      s_row[t] = p >= 0 ? (head_base + p) * qhead : -1;
-    }
-    __syncthreads();
-    for (int x = tid; x < nr * qhead; x += nthr) {
-      const int t = x / qhead, qh = x % qhead;
-      const int64_t row = s_row[t];
-      s_m[x] = row >= 0 ? A.m[row + qh] : -INFINITY;
-      s_l[x] = row >= 0 ? A.l[row + qh] : 0.f;
-    }
-    __syncthreads();
+    int64_t row[kRankTile];
 #pragma unroll
-    for (int k = 0; k < kMaxItems; ++k) {
-      const int x = tid + k * nthr;
-      if (x >= n_items) break;
-      const int qh = x / D4, c = x % D4;
-      float mt = -INFINITY;
-      for (int t = 0; t < nr; ++t) mt = fmaxf(mt, s_m[t * qhead + qh]);
-      const float m_new = fmaxf(big[k], mt);
-      if (m_new == -INFINITY) continue;
-      const float keep = big[k] == -INFINITY ? 0.f : exp2f((big[k] - m_new) * kLog2e);
-      float4 a = make_float4(acc[k].x * keep, acc[k].y * keep, acc[k].z * keep, acc[k].w * keep);
-      float lsum = total[k] * keep;
-#pragma unroll 8
-      for (int t = 0; t < nr; ++t) {
-        const float mp = s_m[t * qhead + qh];
-        const float w = mp == -INFINITY ? 0.f : exp2f((mp - m_new) * kLog2e);
-        const int64_t row = s_row[t];
-        const float4 o = w > 0.f ? *reinterpret_cast<const float4*>(
-                                       A.o + (row + qh) * A.head_dim + c * 4)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-        a = make_float4(fmaf(o.x, w, a.x), fmaf(o.y, w, a.y), fmaf(o.z, w, a.z), fmaf(o.w, w, a.w));
-        lsum = fmaf(s_l[t * qhead + qh], w, lsum);
-      }
-      acc[k] = a;
-      total[k] = lsum;
-      big[k] = m_new;
+    for (int t = 0; t < kRankTile; ++t) {
+      const int32_t p = r0 + t < A.topk ? inv[r0 + t] : -1;
+      row[t] = (p >= 0 && item) ? (head_base + p) * qhead + qh : -1;
     }
+    float mv[kRankTile], lv[kRankTile];
+    float4 ov[kRankTile];
+#pragma unroll
+    for (int t = 0; t < kRankTile; ++t) {
+      const bool ok = row[t] >= 0;
+      const int64_t rr = ok ? row[t] : 0;
+      mv[t] = ok ? A.m[rr] : -INFINITY;
+      lv[t] = ok ? A.l[rr] : 0.f;
+      ov[t] = ok ? *reinterpret_cast<const float4*>(A.o + rr * A.head_dim + 4 * c)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kRankTile; ++t) mt = fmaxf(mt, mv[t]);
+    const float m_new = fmaxf(big, mt);
+    if (m_new == -INFINITY) continue;
+    const float keep = big == -INFINITY ? 0.f : exp2f((big - m_new) * kLog2e);
+    float4 a = make_float4(acc.x * keep, acc.y * keep, acc.z * keep, acc.w * keep);
+    float lsum = total * keep;
+#pragma unroll
+    for (int t = 0; t < kRankTile; ++t) {
+      const float w = mv[t] == -INFINITY ? 0.f : exp2f((mv[t] - m_new) * kLog2e);
+      a = make_float4(fmaf(ov[t].x, w, a.x), fmaf(ov[t].y, w, a.y), fmaf(ov[t].z, w, a.z),
+                      fmaf(ov[t].w, w, a.w));
+      lsum = fmaf(lv[t], w, lsum);
+    }
+    acc = a;
+    total = lsum;
+    big = m_new;
   }
-#pragma unroll
-  for (int k = 0; k < kMaxItems; ++k) {
-    const int x = tid + k * nthr;
-    if (x >= n_items) break;
-    const int qh = x / D4, c = x % D4;
-    const int64_t out_off = (q * A.hq + (int64_t)h * qhead + qh) * A.head_dim + c * 4;
-    if (big[k] == -INFINITY) {
-      *reinterpret_cast<float4*>(A.out + out_off) = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (A.lse != nullptr && c == 0) A.lse[q * A.hq + (int64_t)h * qhead + qh] = -INFINITY;
-    } else {
-      const float inv_total = 1.f / total[k];
-      *reinterpret_cast<float4*>(A.out + out_off) =
-          make_float4(acc[k].x * inv_total, acc[k].y * inv_total, acc[k].z * inv_total,
-                      acc[k].w * inv_total);
-      if (A.lse != nullptr && c == 0)
-        A.lse[q * A.hq + (int64_t)h * qhead + qh] = big[k] + logf(total[k]);
-    }
+  if (!item) return;
+  const int64_t out_off = (q * A.hq + (int64_t)h * qhead + qh) * A.head_dim + c * 4;
+  if (big == -INFINITY) {
+    *reinterpret_cast<float4*>(A.out + out_off) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (A.lse != nullptr && c == 0) A.lse[q * A.hq + (int64_t)h * qhead + qh] = -INFINITY;
+  } else {
+    const float inv_total = 1.f / total;
+    *reinterpret_cast<float4*>(A.out + out_off) =
+        make_float4(acc.x * inv_total, acc.y * inv_total, acc.z * inv_total, acc.w * inv_total);
+    if (A.lse != nullptr && c == 0)
+      A.lse[q * A.hq + (int64_t)h * qhead + qh] = big + logf(total);
   }
 }
 
@@ -116,10 +97,8 @@ hipError_t launch_combine(const sa_index* idx, const CombineArgs& a, hipStream_t
   const int64_t grid = a.tq * a.hkv;
   const int n_items = a.qhead * (a.head_dim / 4);
   int block = (n_items + 63) / 64 * 64;
-  if (block > 1024) block = 1024;
-  if (n_items > block * kMaxItems) return hipErrorInvalidValue;   // plan rejects this
-  const size_t smem = 8 * kRankTile + 2 * 4 * (size_t)kRankTile * a.qhead;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)grid), dim3(block), smem, s, P, a);
+  if (block > kMaxBlock) return hipErrorInvalidValue;             // plan rejects this
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)grid), dim3(block), 0, s, P, a);
   return hipGetLastError();
 }
 
