@@ -9,10 +9,11 @@ therefore does not find its blocks in the 256 MB Infinity Cache from the
 step before.
 
 Prints ONE JSON line. ``value`` is kept edges per second of whole steps.
-``roofline`` is for the forward kernel, the dominant one. Its average
-duration is measured with HIP events recorded on the stream the kernel is
-launched on, inside the timed region, and its algorithmic bytes are counted
-from the built index. ``cpu_baseline`` is the CPU oracle timed on this host.
+``roofline`` is for the forward pass (sa_forward), the dominant part of a
+step. Its average duration is measured with HIP events recorded on the
+stream it is launched on, inside the timed region; its algorithmic bytes and
+flops are counted from the built index. ``cpu_baseline`` is the CPU oracle
+timed on this host.
 
     python bench.py [--steps K] [--warmup W] [--config decode|tiny|prefill|ragged|skewed]
     python bench.py --copy-calibration   # plain copy kernel of known size, for PMC scaling
@@ -257,7 +258,7 @@ def main():
     total_bytes = np.mean([p["total_bytes"] for p in per])
     flops = np.mean([p["flops"] for p in per])
     fc_s = (float(np.mean(fwd_ms)) + float(np.mean(comb_ms))) / 1e3
-    achieved = fwd_bytes / fwd_avg_s / 1e9
+    roofline = forward_roofline(base, fwd_bytes, flops, fwd_avg_s)
 
     result = {
         "metric": METRIC,
@@ -274,10 +275,7 @@ def main():
         "data": "synthetic",
         "config": {**base.describe(), "edges_per_batch": int(np.mean([p["edges"] for p in per])),
                    "rotated_batches": len(sets), "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "k_fwd_wave", "alg_bytes_per_launch": int(fwd_bytes),
-                     "avg_launch_us": fwd_avg_s * 1e6},
+        "roofline": roofline,
         "forward_plus_combine": {
             "us": fc_s * 1e6,
             "edges_per_s": edges / args.steps / fc_s,
@@ -294,6 +292,63 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def forward_kernels(w):
+    """The kernels one sa_forward launches for this geometry, dominant first."""
+    qhead = w.hq // w.hkv
+    if w.head_dim == 128 and w.block_size <= 64 and qhead <= 16:
+        small = f"k_fwd_small<{(w.block_size + 15) // 16}>"
+    else:
+        small = "k_fwd_wave"
+    return small, "k_fwd_mfma"
+
+
+def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s):
+    """Roofline of the forward pass (sa_forward: the wavefront kernel for
+    units under 32 rows, then the MFMA kernel, which exits at once when the
+    build made no such unit). Bound by HBM when the algorithmic intensity is
+    below the fp32 MFMA ridge (157.3 TFLOP/s / 8 TB/s = 19.7 flop/B), else by
+    fp32 MFMA. `traffic` comes from the committed FETCH_SIZE + WRITE_SIZE
+    summary for this workload, and only while the kernel's source is the one
+    the counters were taken on."""
+    small, mfma = forward_kernels(w)
+    ridge = FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if fwd_flops / fwd_bytes < ridge:
+        achieved, peak, unit, bound = fwd_bytes / fwd_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
+        kernels = f"{small} + {mfma}"
+    else:
+        achieved, peak, unit, bound = fwd_flops / fwd_s / 1e12, FP32_MFMA_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        kernels = f"{mfma} + {small}"
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": measured_traffic(w.name, small),
+            "kernel": f"sa_forward ({kernels})", "alg_bytes_per_launch": int(fwd_bytes),
+            "alg_flops_per_launch": int(fwd_flops), "avg_launch_us": fwd_s * 1e6}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per forward launch from profiles/<workload>_forward_traffic.md
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE runs scaled by a plain copy of known
+    size), or None when there is no such summary or the forward sources have
+    changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_forward_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("TRAFFIC_JSON:"):
+                rec = json.loads(line[len("TRAFFIC_JSON:"):])
+    if rec is None or rec.get("kernel") != kernel:
+        return None
+    h = hashlib.sha256()
+    for name in rec.get("sources", []):
+        with open(os.path.join(ROOT, "block_sparse_paged_csr_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return rec["bytes_per_launch"]
 
 
 def graph_step_us(sets, step, steps):
