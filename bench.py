@@ -149,9 +149,9 @@ def _cpu_baseline(oracle, w, target_s):
     inv = idx["inv"]
     done_q, edges_done, t_attn = 0, 0, 0.0
     order = np.random.default_rng(0).permutation(w.tq)
-    min_s = min(2.0, target_s)
-    # whole passes over the batch while they are short, else a prefix of one pass
-    while (done_q < w.tq and t_attn < target_s) or (done_q % w.tq == 0 and t_attn < min_s):
+    # whole passes over the batch while they are short (stop at a pass boundary
+    # once target_s is spent), else a prefix of the first pass
+    while t_attn < target_s or (done_q > w.tq and done_q % w.tq != 0):
         at = done_q % w.tq
         chunk = order[at:at + max(1, min(64, w.tq - at))]
         t0 = time.perf_counter()

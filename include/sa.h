@@ -10,8 +10,9 @@
  *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless the comment says "host". The caller
- *    allocates and owns every buffer; the library allocates nothing and
- *    keeps no state between calls.
+ *    allocates and owns every buffer; the library allocates no memory and
+ *    keeps no data between calls (a process-wide build counter aside, which
+ *    tags the device-side handshake of one build).
  *  - All GPU work is enqueued on `stream` and runs asynchronously. Only
  *    sa_index_status() waits for the stream.
  *  - Scalar and length checks run on the host before anything is enqueued.
