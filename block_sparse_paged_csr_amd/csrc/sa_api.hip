@@ -231,7 +231,19 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch, in
   idx->cap_edges = sa::kCapRows / qhead > 0 ? sa::kCapRows / qhead : 1;
   const bool mfma_ok = head_dim == sa::kMfmaHeadDim && block_size <= sa::kMfmaMaxBlock &&
                        sa::mfma_enabled();
-  idx->mfma_min_rows = mfma_ok ? sa::kMfmaMinRows : INT32_MAX;
+  // Small problems on the one-wave-per-unit kernel keep every unit there: a
+  // slot with many edges becomes several 16-row units (at most tq*topk <= 4096
+  // edges a head, so the extra block reads stay small) and the forward needs
+  // no MFMA-kernel launch.
+  const bool all_small = sa::small_kernel_fits(head_dim, block_size, page_size, qhead) &&
+                         sa::fused_build_fits(tq, topk, (int64_t)batch * (max_pages / (block_size / page_size)),
+                                              batch, hkv);
+  // With the one-wave kernel a slot that does not fit one of its units (16
+  // rows) goes to the MFMA path whole instead of being split, so no block is
+  // read twice; otherwise slots of 32 rows or more do.
+  const int32_t min_rows = sa::small_kernel_fits(head_dim, block_size, page_size, qhead)
+                               ? sa::small_kernel_rows() + 1 : sa::kMfmaMinRows;
+  idx->mfma_min_rows = (mfma_ok && !all_small) ? min_rows : INT32_MAX;
   idx->wave_cap_edges = sa::small_kernel_fits(head_dim, block_size, page_size, qhead)
                             ? (sa::small_kernel_rows() / qhead > 0 ? sa::small_kernel_rows() / qhead : 1)
                             : idx->cap_edges;

@@ -4,11 +4,14 @@
 // GQA lane qh, (o, m, l) of alice-llm 2.0.0 forward.rs process_work_unit over
 // the block's valid, causally alive positions.
 //
-// One workgroup (8 waves) per CU takes units from a device queue. For each
-// unit it gathers the block's K and V rows once into LDS (row pitch padded
-// so the MFMA operand reads do not conflict). Each wave then takes 32-row
-// tiles of the unit and computes them on fp32 matrix cores
-// (v_mfma_f32_32x32x2f32):
+// Persistent workgroups take units from a device queue: 8 waves, one per CU,
+// for blocks of up to 128 keys; 4 waves and two per CU for blocks of up to 64
+// keys (LDS sized to the block), so one workgroup gathers while the other
+// computes. For each unit the workgroup first resolves each key's K/V row
+// offset through the block table, then gathers the block's K and V rows once
+// into LDS with all loads in flight (row pitch padded so the MFMA operand
+// reads do not conflict). Each wave then takes 32-row tiles of the unit and
+// computes them on fp32 matrix cores (v_mfma_f32_32x32x2f32):
 //
 //   S^T[key, row] = K[key, :] . Q[row, :]       A = K from LDS, B = Q^T in registers
 //   O^T[d, row]  += V[key, d] * P[row, key]      A = V^T from LDS, B = P^T in registers
@@ -35,19 +38,22 @@ __device__ inline floatx16 zero16() {
   return z;
 }
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kD = 128;                 // head_dim of this kernel
 constexpr int kMaxKeys = 128;           // block_size <= 128
 constexpr int kKPitch = kD + 4;         // floats; 16-byte aligned rows, conflict-free b128 reads
 constexpr int kVPitch = kD + 8;         // floats; the two key rows of a PV operand use disjoint banks
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int NKB>   // 32-key blocks per KV block (block_size <= 32 * NKB)
-__global__ __launch_bounds__(kThreads) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
-  __shared__ __align__(16) float s_k[kMaxKeys * kKPitch];
-  __shared__ __align__(16) float s_v[kMaxKeys * kVPitch];
-  __shared__ int s_valid[kMaxKeys];
+// NKB: 32-key blocks per KV block (block_size <= 32 * NKB); WAVES per workgroup.
+template <int NKB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
+  constexpr int kWaves = WAVES;
+  constexpr int kThreads = WAVES * 64;
+  constexpr int kKeys = NKB * 32;
+  __shared__ __align__(16) float s_k[kKeys * kKPitch];
+  __shared__ __align__(16) float s_v[kKeys * kVPitch];
+  __shared__ int64_t s_off[kKeys];
+  __shared__ int s_valid[kKeys];
   __shared__ int s_unit;
 
   DevHeader* hdr = P.hdr;
@@ -73,22 +79,37 @@ __global__ __launch_bounds__(kThreads) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
     const int64_t bt_row = (int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb;
     const int64_t head_off = (int64_t)U.h * A.page_size * kD;
 
-    // ---- gather K and V of the block into LDS (zero rows past the valid range)
-    for (int x = tid; x < NKB * 32 * (kD / 4); x += kThreads) {
-      const int key = x / (kD / 4), c4 = x % (kD / 4);
-      bool valid = key < nkeys;
-      int64_t off = 0;
-      if (valid) {
+    // ---- row offset of each key (-1: past the valid range or no page)
+    for (int key = tid; key < kKeys; key += kThreads) {
+      int64_t off = -1;
+      if (key < nkeys) {
         const int32_t pgl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
         const int32_t page = A.block_tables[bt_row + pgl];
-        valid = page >= 0 && page < A.num_pages;
-        off = (int64_t)page * page_stride + head_off + (int64_t)(key - pgl * A.page_size) * kD + c4 * 4;
+        if (page >= 0 && page < A.num_pages)
+          off = (int64_t)page * page_stride + head_off + (int64_t)(key - pgl * A.page_size) * kD;
       }
-      const float4 kv = valid ? *reinterpret_cast<const float4*>(A.k + off) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 vv = valid ? *reinterpret_cast<const float4*>(A.v + off) : make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4*>(&s_k[key * kKPitch + c4 * 4]) = kv;
-      *reinterpret_cast<float4*>(&s_v[key * kVPitch + c4 * 4]) = vv;
-      if (c4 == 0) s_valid[key] = valid;
+      s_off[key] = off;
+      s_valid[key] = off >= 0;
+    }
+    __syncthreads();
+    // ---- gather K and V of the block into LDS (zero rows past the valid range)
+    {
+      constexpr int kIters = kKeys * (kD / 4) / kThreads;
+      static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
+      float4 kv[kIters], vv[kIters];
+#pragma unroll
+      for (int i = 0; i < kIters; ++i) {
+        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
+        const int64_t off = s_off[key];
+        kv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.k + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.v + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kIters; ++i) {
+        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
+        *reinterpret_cast<float4*>(&s_k[key * kKPitch + c4 * 4]) = kv[i];
+        *reinterpret_cast<float4*>(&s_v[key * kVPitch + c4 * 4]) = vv[i];
+      }
     }
     __syncthreads();
 
@@ -219,9 +240,223 @@ __global__ __launch_bounds__(kThreads) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
   }
 }
 
+// Blocks of up to 64 keys: 16-row tiles on v_mfma_f32_16x16x4f32, so that
+// units of 17..64 rows (most units of mixed batches) keep 2..4 waves busy.
+// The block's K and V are staged in LDS once per unit as above; each wave then
+// computes whole 16-row tiles against every key, with the same operand
+// layout as the one-wave decode kernel:
+//   S^T[key, row]: MFMA t, component c, lane group g takes d = 16t + 4g + c
+//   O^T[d, row]:   output row i of MFMA block db stands for d = 4i + (db & 3) + 64 (db >> 2)
+// and an exact softmax over the block from register-resident scores.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline floatx4 zero4v() {
+  floatx4 z;
+  z[0] = z[1] = z[2] = z[3] = 0.f;
+  return z;
+}
+
 template <int NKB>
-hipError_t launch_mfma_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned grid) {
-  hipLaunchKernelGGL(k_fwd_mfma<NKB>, dim3(grid), dim3(kThreads), 0, s, P, a);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_mfma16(IndexPtrs P, FwdArgs A) {
+  constexpr int kWaves = 4;
+  constexpr int kThreads = 256;
+  constexpr int kKeys = NKB * 32;
+  constexpr int kChunks = kKeys / 16;     // 16-key chunks
+  __shared__ __align__(16) float s_k[kKeys * kKPitch];
+  __shared__ __align__(16) float s_v[kKeys * kVPitch];
+  __shared__ int64_t s_off[kKeys];
+  __shared__ int s_unit;
+
+  DevHeader* hdr = P.hdr;
+  if (hdr->status != SA_OK) return;
+  const int32_t num_units = hdr->num_units_mfma;
+  if ((int32_t)blockIdx.x >= num_units) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int32_t qhead = A.qhead;
+  const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
+
+  for (int32_t u = blockIdx.x;;) {
+    if (u >= num_units) break;
+    const Unit U = P.units_mfma[u];
+    const int64_t lk = U.lk;
+    const int64_t block_start = (int64_t)U.blk * A.block_size;
+    int64_t block_end = block_start + A.block_size;
+    block_end = block_end < lk ? block_end : lk;
+    const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
+    const int64_t bt_row = (int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb;
+    const int64_t head_off = (int64_t)U.h * A.page_size * kD;
+
+    // ---- row offset of each key (-1: past the valid range or no page), then the gather
+    for (int key = tid; key < kKeys; key += kThreads) {
+      int64_t off = -1;
+      if (key < nkeys) {
+        const int32_t pgl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
+        const int32_t page = A.block_tables[bt_row + pgl];
+        if (page >= 0 && page < A.num_pages)
+          off = (int64_t)page * page_stride + head_off + (int64_t)(key - pgl * A.page_size) * kD;
+      }
+      s_off[key] = off;
+    }
+    __syncthreads();
+    {
+      constexpr int kIters = kKeys * (kD / 4) / kThreads;
+      static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
+      float4 kv[kIters], vv[kIters];
+#pragma unroll
+      for (int i = 0; i < kIters; ++i) {
+        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
+        const int64_t off = s_off[key];
+        kv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.k + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.v + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kIters; ++i) {
+        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
+        *reinterpret_cast<float4*>(&s_k[key * kKPitch + c4 * 4]) = kv[i];
+        *reinterpret_cast<float4*>(&s_v[key * kVPitch + c4 * 4]) = vv[i];
+      }
+    }
+    __syncthreads();
+
+    const int32_t rows = (U.e1 - U.e0) * qhead;
+    const int64_t row0 = (int64_t)U.e0 * qhead;
+    const int32_t ntiles = (rows + 15) / 16;
+    for (int32_t tile = wv; tile < ntiles; tile += kWaves) {
+      const int32_t row = tile * 16 + li;
+      const bool row_ok = row < rows;
+      int32_t qi = 0;
+      if (row_ok) qi = P.edges[2 * (int64_t)(U.e0 + row / qhead)];
+      const float* qp = A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + (row_ok ? row % qhead : 0)) * kD + 4 * g;
+      floatx4 qr[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        qr[t] = row_ok ? *reinterpret_cast<const floatx4*>(qp + 16 * t) : zero4v();
+      int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
+      klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
+      const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
+
+      // ---- scores of every key: S^T = K . Q^T per 16-key chunk
+      float sreg[kChunks][4];
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        floatx4 sa0 = zero4v(), sa1 = zero4v();
+        const float* kr = &s_k[(16 * c + li) * kKPitch + 4 * g];
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          const floatx4 ka = *reinterpret_cast<const floatx4*>(kr + 16 * t);
+          const floatx4 kb = *reinterpret_cast<const floatx4*>(kr + 16 * (t + 1));
+          sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[t].x, sa0, 0, 0, 0);
+          sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.x, qr[t + 1].x, sa1, 0, 0, 0);
+          sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[t].y, sa0, 0, 0, 0);
+          sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.y, qr[t + 1].y, sa1, 0, 0, 0);
+          sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[t].z, sa0, 0, 0, 0);
+          sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.z, qr[t + 1].z, sa1, 0, 0, 0);
+          sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[t].w, sa0, 0, 0, 0);
+          sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.w, qr[t + 1].w, sa1, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // bound how far LDS reads run ahead
+        const floatx4 sv = sa0 + sa1;   // lane (li, g), reg r: key 16c + 4g + r, row li
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * c + 4 * g + r;
+          const bool alive = row_ok && key <= kmax && s_off[key] >= 0;
+          sreg[c][r] = alive ? sv[r] * A.scale_log2 : -INFINITY;
+        }
+      }
+      // ---- softmax of row li over the block (base 2)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sreg[c][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float ls = 0.f;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = sreg[c][r] == -INFINITY ? 0.f : exp2f(sreg[c][r] - mx);
+          sreg[c][r] = p;
+          ls += p;
+        }
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+
+      // ---- O^T = V^T . P^T
+      floatx4 oacc[8];
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float* vr = &s_v[(16 * c + 4 * g + r) * kVPitch + 4 * li];
+          const floatx4 v0 = *reinterpret_cast<const floatx4*>(vr);
+          const floatx4 v1 = *reinterpret_cast<const floatx4*>(vr + 64);
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const floatx4 acc = (c == 0 && r == 0) ? zero4v() : oacc[db];
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(db < 4 ? v0[db & 3] : v1[db & 3], sreg[c][r],
+                                                            acc, 0, 0, 0);
+          }
+          if (r & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // ---- the tile's partial rows: lane (li, g) holds row li,
+      // d = 16g + 4v + (db & 3) + 64 (db >> 2) in oacc[db][v]
+      if (row_ok) {
+        float* dst = A.o + (row0 + row) * kD + 16 * g;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          *reinterpret_cast<floatx4*>(dst + 4 * v) = floatx4{oacc[0][v], oacc[1][v], oacc[2][v], oacc[3][v]};
+          *reinterpret_cast<floatx4*>(dst + 64 + 4 * v) = floatx4{oacc[4][v], oacc[5][v], oacc[6][v], oacc[7][v]};
+        }
+        if (g == 0) {
+          A.m[row0 + row] = mx == -INFINITY ? -INFINITY : mx * kLn2;
+          A.l[row0 + row] = ls;
+        }
+      }
+    }
+    __syncthreads();                       // LDS of this unit no longer read
+    if (tid == 0) s_unit = (int)gridDim.x + (int)atomicAdd(&hdr->queue_mfma, 1u);
+    __syncthreads();
+    u = s_unit;
+  }
+  if (tid == 0) {
+    __threadfence();
+    const unsigned active = num_units < (int32_t)gridDim.x ? (unsigned)num_units : gridDim.x;
+    const unsigned done = atomicAdd(&hdr->done_mfma, 1u);
+    if (done == active - 1) {
+      atomicExch(&hdr->queue_mfma, 0u);
+      atomicExch(&hdr->done_mfma, 0u);
+    }
+  }
+}
+
+template <int NKB>
+hipError_t launch_mfma16_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+  static thread_local int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma16<NKB>, 256, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  hipLaunchKernelGGL(k_fwd_mfma16<NKB>, dim3((unsigned)per_cu * cus), dim3(256), 0, s, P, a);
+  return hipGetLastError();
+}
+
+template <int NKB, int WAVES>
+hipError_t launch_mfma_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+  static thread_local int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma<NKB, WAVES>, WAVES * 64, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  hipLaunchKernelGGL((k_fwd_mfma<NKB, WAVES>), dim3((unsigned)per_cu * cus), dim3(WAVES * 64), 0, s, P, a);
   return hipGetLastError();
 }
 
@@ -234,10 +469,10 @@ hipError_t launch_forward_mfma(const sa_index* idx, const FwdArgs& a, hipStream_
   if (a.head_dim != kD || a.block_size > kMaxKeys) return hipErrorInvalidValue;
   const IndexPtrs P = index_ptrs(idx);
   const int nkb = (a.block_size + 31) / 32;
-  if (nkb <= 1) return launch_mfma_t<1>(P, a, s, grid);
-  if (nkb <= 2) return launch_mfma_t<2>(P, a, s, grid);
-  if (nkb <= 3) return launch_mfma_t<3>(P, a, s, grid);
-  return launch_mfma_t<4>(P, a, s, grid);
+  if (nkb <= 1) return launch_mfma16_t<1>(P, a, s, grid);
+  if (nkb <= 2) return launch_mfma16_t<2>(P, a, s, grid);
+  if (nkb <= 3) return launch_mfma_t<3, 8>(P, a, s, grid);
+  return launch_mfma_t<4, 8>(P, a, s, grid);
 }
 
 }  // namespace sa

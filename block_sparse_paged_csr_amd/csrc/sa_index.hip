@@ -784,16 +784,15 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   }
 }
 
-size_t fused_lds_bytes(const BuildArgs& a) {
-  const size_t items = (size_t)a.tq * a.topk;
-  const size_t nlist = (size_t)a.nbs < items ? (size_t)a.nbs : items;
-  return 4 * ((size_t)a.nbs + items + 2 * nlist + (size_t)a.tq + 2 * (size_t)a.batch);
+size_t fused_lds_bytes(int64_t tq, int32_t topk, int64_t nbs, int32_t batch) {
+  const size_t items = (size_t)tq * topk;
+  const size_t nlist = (size_t)nbs < items ? (size_t)nbs : items;
+  return 4 * ((size_t)nbs + items + 2 * nlist + (size_t)tq + 2 * (size_t)batch);
 }
+size_t fused_lds_bytes(const BuildArgs& a) { return fused_lds_bytes(a.tq, a.topk, a.nbs, a.batch); }
 
 bool fused_fits(const BuildArgs& a) {
-  return a.tq * a.topk <= (int64_t)kFusedThreads * kFusedItems && a.nbs <= kFusedMaxSlots &&
-         a.tq <= kFusedMaxQ && a.batch <= kFusedMaxBatch && a.hkv <= 65535 &&
-         fused_lds_bytes(a) <= kFusedMaxLds;
+  return fused_build_fits(a.tq, a.topk, a.nbs, a.batch, a.hkv);
 }
 
 inline unsigned grid_for(int64_t n, int per) {
@@ -802,6 +801,12 @@ inline unsigned grid_for(int64_t n, int per) {
 }
 
 }  // namespace
+
+bool fused_build_fits(int64_t tq, int32_t topk, int64_t nbs, int32_t batch, int32_t hkv) {
+  return tq * topk <= (int64_t)kFusedThreads * kFusedItems && nbs <= kFusedMaxSlots &&
+         tq <= kFusedMaxQ && batch <= kFusedMaxBatch && hkv <= 65535 &&
+         fused_lds_bytes(tq, topk, nbs, batch) <= kFusedMaxLds;
+}
 
 hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) {
   const IndexPtrs P = index_ptrs(idx);

@@ -169,6 +169,8 @@ unsigned cu_count();
 // Launchers (enqueue only; return hipSuccess or the launch error).
 hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s);
 hipError_t launch_forward(const sa_index* idx, const FwdArgs& a, hipStream_t s);
+// True when one workgroup per head can build the index in LDS (k_index_fused).
+bool fused_build_fits(int64_t tq, int32_t topk, int64_t nbs, int32_t batch, int32_t hkv);
 hipError_t launch_combine(const sa_index* idx, const CombineArgs& a, hipStream_t s);
 hipError_t launch_forward_wave(const sa_index* idx, const FwdArgs& a, hipStream_t s,
                                unsigned max_grid);
