@@ -229,6 +229,7 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch, in
   idx->nbs = (int64_t)batch * idx->msb;
   idx->max_edges = max_edges;
   idx->cap_edges = sa::kCapRows / qhead > 0 ? sa::kCapRows / qhead : 1;
+  if (idx->cap_edges > sa::kCapUnitEdges) idx->cap_edges = sa::kCapUnitEdges;
   const bool mfma_ok = head_dim == sa::kMfmaHeadDim && block_size <= sa::kMfmaMaxBlock &&
                        sa::mfma_enabled();
   // Small problems on the one-wave-per-unit kernel keep every unit there: a

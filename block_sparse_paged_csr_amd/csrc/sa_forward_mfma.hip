@@ -43,6 +43,8 @@ constexpr int kMaxKeys = 128;           // block_size <= 128
 constexpr int kKPitch = kD + 4;         // floats; 16-byte aligned rows, conflict-free b128 reads
 constexpr int kVPitch = kD + 8;         // floats; the two key rows of a PV operand use disjoint banks
 constexpr float kLn2 = 0.69314718055994530942f;
+// Most edges in one MFMA unit (cap_edges <= kMaxUnitEdges, see the plan).
+constexpr int kMaxUnitEdges = kCapUnitEdges;
 
 // NKB: 32-key blocks per KV block (block_size <= 32 * NKB); WAVES per workgroup.
 template <int NKB, int WAVES>
@@ -262,76 +264,124 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   constexpr int kThreads = 256;
   constexpr int kKeys = NKB * 32;
   constexpr int kChunks = kKeys / 16;     // 16-key chunks
+  constexpr int kIters = kKeys * (kD / 4) / kThreads;   // gather float4 per thread (K and V each)
+  static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
   __shared__ __align__(16) float s_k[kKeys * kKPitch];
   __shared__ __align__(16) float s_v[kKeys * kVPitch];
-  __shared__ int64_t s_off[kKeys];
-  __shared__ int s_unit;
+  __shared__ int64_t s_off[2][kKeys];     // key row offsets (-1: none) of units j and j+1
+  __shared__ int32_t s_rec[3][8];         // records of units j, j+1, j+2
+  __shared__ int32_t s_qid[2][kMaxUnitEdges];   // query id of each edge of units j and j+1
 
   DevHeader* hdr = P.hdr;
   if (hdr->status != SA_OK) return;
   const int32_t num_units = hdr->num_units_mfma;
-  if ((int32_t)blockIdx.x >= num_units) return;
+  const int32_t G = gridDim.x;
+  const int32_t u0 = blockIdx.x;
+  if (u0 >= num_units) return;
+  const int32_t n_units = (num_units - u0 + G - 1) / G;   // units u0, u0 + G, ...
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int32_t qhead = A.qhead;
   const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
+  const int32_t* units = reinterpret_cast<const int32_t*>(P.units_mfma);
 
-  for (int32_t u = blockIdx.x;;) {
-    if (u >= num_units) break;
-    const Unit U = P.units_mfma[u];
-    const int64_t lk = U.lk;
+  auto unit_of = [&](int slot) { const int32_t* r = s_rec[slot]; return Unit{r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]}; };
+  auto keys_of = [&](const Unit& U) -> int32_t {
+    const int64_t start = (int64_t)U.blk * A.block_size;
+    int64_t end = start + A.block_size;
+    end = end < U.lk ? end : (int64_t)U.lk;
+    return end > start ? (int32_t)(end - start) : 0;
+  };
+  // block-table entry of key `key` (clamped into the block) and the key's row offset
+  auto page_of = [&](const Unit& U, int key) -> int32_t {
+    const int kk = key < A.block_size ? key : 0;
+    const int32_t pgl = (int32_t)div_magic((uint32_t)kk, A.ps_magic);
+    return A.block_tables[(int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb + pgl];
+  };
+  auto key_off = [&](const Unit& U, int key, int32_t page) -> int64_t {
+    if (key >= keys_of(U) || page < 0 || page >= A.num_pages) return -1;
+    const int32_t pgl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
+    return (int64_t)page * page_stride + (int64_t)U.h * A.page_size * kD + (int64_t)(key - pgl * A.page_size) * kD;
+  };
+  auto load_kv = [&](int sl, float4 (&kv)[kIters], float4 (&vv)[kIters]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
+      const int64_t off = s_off[sl][key];
+      kv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.k + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.v + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  // ---- prologue: records of units 0..2, key offsets of units 0 and 1, K/V of unit 0
+  if (tid < 8) {
+    s_rec[0][tid] = units[8 * (int64_t)u0 + tid];
+    if (n_units > 1) s_rec[1][tid] = units[8 * (int64_t)(u0 + G) + tid];
+    if (n_units > 2) s_rec[2][tid] = units[8 * (int64_t)(u0 + 2 * G) + tid];
+  }
+  __syncthreads();
+  for (int key = tid; key < kKeys; key += kThreads) {
+    const Unit U0 = unit_of(0);
+    s_off[0][key] = key_off(U0, key, page_of(U0, key));
+    if (n_units > 1) {
+      const Unit U1 = unit_of(1);
+      s_off[1][key] = key_off(U1, key, page_of(U1, key));
+    }
+  }
+  for (int e = tid; e < kMaxUnitEdges; e += kThreads) {
+    const Unit U0 = unit_of(0);
+    if (e < U0.e1 - U0.e0) s_qid[0][e] = P.edges[2 * (int64_t)(U0.e0 + e)];
+    if (n_units > 1) {
+      const Unit U1 = unit_of(1);
+      if (e < U1.e1 - U1.e0) s_qid[1][e] = P.edges[2 * (int64_t)(U1.e0 + e)];
+    }
+  }
+  __syncthreads();
+  float4 kv[kIters], vv[kIters];
+  load_kv(0, kv, vv);
+
+  for (int32_t j = 0; j < n_units; ++j) {
+    const int cur = j & 1, nxt = cur ^ 1;
+    const int rs = j % 3, rs2 = (j + 2) % 3;
+    // ---- K/V of unit j into LDS
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
+      *reinterpret_cast<float4*>(&s_k[key * kKPitch + c4 * 4]) = kv[i];
+      *reinterpret_cast<float4*>(&s_v[key * kVPitch + c4 * 4]) = vv[i];
+    }
+    __syncthreads();
+    // ---- ahead: K/V of unit j+1, block-table entries of unit j+2, record of unit j+3
+    if (j + 1 < n_units) load_kv(nxt, kv, vv);
+    int32_t pre_page = 0, pre_rec = 0;
+    int32_t pre_qid[kMaxUnitEdges / kThreads];
+    const bool has2 = j + 2 < n_units, has3 = j + 3 < n_units;
+    if (has2) {
+      const Unit U2 = unit_of(rs2);
+      if (tid < kKeys) pre_page = page_of(U2, tid);
+#pragma unroll
+      for (int k = 0; k < kMaxUnitEdges / kThreads; ++k) {
+        const int e = tid + k * kThreads;
+        pre_qid[k] = e < U2.e1 - U2.e0 ? P.edges[2 * (int64_t)(U2.e0 + e)] : 0;
+      }
+    }
+    if (has3 && tid < 8) pre_rec = units[8 * (int64_t)(u0 + (j + 3) * G) + tid];
+
+    // ---- the tiles of unit j
+    const Unit U = unit_of(rs);
+    const int32_t nkeys = keys_of(U);
     const int64_t block_start = (int64_t)U.blk * A.block_size;
-    int64_t block_end = block_start + A.block_size;
-    block_end = block_end < lk ? block_end : lk;
-    const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
-    const int64_t bt_row = (int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb;
-    const int64_t head_off = (int64_t)U.h * A.page_size * kD;
-
-    // ---- row offset of each key (-1: past the valid range or no page), then the gather
-    for (int key = tid; key < kKeys; key += kThreads) {
-      int64_t off = -1;
-      if (key < nkeys) {
-        const int32_t pgl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
-        const int32_t page = A.block_tables[bt_row + pgl];
-        if (page >= 0 && page < A.num_pages)
-          off = (int64_t)page * page_stride + head_off + (int64_t)(key - pgl * A.page_size) * kD;
-      }
-      s_off[key] = off;
-    }
-    __syncthreads();
-    {
-      constexpr int kIters = kKeys * (kD / 4) / kThreads;
-      static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
-      float4 kv[kIters], vv[kIters];
-#pragma unroll
-      for (int i = 0; i < kIters; ++i) {
-        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
-        const int64_t off = s_off[key];
-        kv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.k + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        vv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.v + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < kIters; ++i) {
-        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
-        *reinterpret_cast<float4*>(&s_k[key * kKPitch + c4 * 4]) = kv[i];
-        *reinterpret_cast<float4*>(&s_v[key * kVPitch + c4 * 4]) = vv[i];
-      }
-    }
-    __syncthreads();
-
     const int32_t rows = (U.e1 - U.e0) * qhead;
     const int64_t row0 = (int64_t)U.e0 * qhead;
     const int32_t ntiles = (rows + 15) / 16;
     for (int32_t tile = wv; tile < ntiles; tile += kWaves) {
       const int32_t row = tile * 16 + li;
       const bool row_ok = row < rows;
-      int32_t qi = 0;
-      if (row_ok) qi = P.edges[2 * (int64_t)(U.e0 + row / qhead)];
+      const int32_t qi = row_ok ? s_qid[cur][row / qhead] : 0;   // staged with the unit
       const float* qp = A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + (row_ok ? row % qhead : 0)) * kD + 4 * g;
       floatx4 qr[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        qr[t] = row_ok ? *reinterpret_cast<const floatx4*>(qp + 16 * t) : zero4v();
+      for (int t = 0; t < 8; ++t) qr[t] = row_ok ? *reinterpret_cast<const floatx4*>(qp + 16 * t) : zero4v();
       int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
       klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
       const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
@@ -360,7 +410,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = 16 * c + 4 * g + r;
-          const bool alive = row_ok && key <= kmax && s_off[key] >= 0;
+          const bool alive = row_ok && key <= kmax && s_off[cur][key] >= 0;
           sreg[c][r] = alive ? sv[r] * A.scale_log2 : -INFINITY;
         }
       }
@@ -417,19 +467,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
       }
     }
-    __syncthreads();                       // LDS of this unit no longer read
-    if (tid == 0) s_unit = (int)gridDim.x + (int)atomicAdd(&hdr->queue_mfma, 1u);
-    __syncthreads();
-    u = s_unit;
-  }
-  if (tid == 0) {
-    __threadfence();
-    const unsigned active = num_units < (int32_t)gridDim.x ? (unsigned)num_units : gridDim.x;
-    const unsigned done = atomicAdd(&hdr->done_mfma, 1u);
-    if (done == active - 1) {
-      atomicExch(&hdr->queue_mfma, 0u);
-      atomicExch(&hdr->done_mfma, 0u);
+    __syncthreads();   // every read of s_k, s_v, s_off[cur], s_qid[cur] and s_rec[rs] is done
+    // ---- stage unit j+2's key offsets and query ids, and unit j+3's record
+    if (has2) {
+      if (tid < kKeys) s_off[cur][tid] = key_off(unit_of(rs2), tid, pre_page);
+#pragma unroll
+      for (int k = 0; k < kMaxUnitEdges / kThreads; ++k) s_qid[cur][tid + k * kThreads] = pre_qid[k];
     }
+    if (has3 && tid < 8) s_rec[rs][tid] = pre_rec;
   }
 }
 

@@ -14,6 +14,7 @@ namespace sa {
 // Most rows (edges * qhead) in one work unit. A slot with more edges is split
 // into near-equal units so that one hot block does not serialise the grid.
 constexpr int kCapRows = 2048;
+constexpr int kCapUnitEdges = 512;   // most edges in one MFMA unit
 // Smallest unit (in rows) that goes to the MFMA kernel. Smaller ones use the
 // wavefront-reduction kernel.
 constexpr int kMfmaMinRows = 32;
