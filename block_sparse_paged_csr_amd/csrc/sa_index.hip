@@ -815,13 +815,18 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
   const char* force_multi = std::getenv("SA_BUILD_MULTIKERNEL");
   const bool multi = force_multi != nullptr && force_multi[0] == '1';
   if (!multi && fused_fits(a)) {
-    static bool attr_set = false;
-    const size_t lds = fused_lds_bytes(a);
-    if (!attr_set) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(k_index_fused),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
-      attr_set = true;
+    // the LDS limit is a per-device attribute of the kernel: set once per device
+    static thread_local int attr_dev = -1;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (attr_dev != dev) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_index_fused),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFusedMaxLds);
+      if (e != hipSuccess) return e;
+      attr_dev = dev;
     }
+    const size_t lds = fused_lds_bytes(a);
     hipLaunchKernelGGL(k_index_fused, dim3((unsigned)a.hkv), dim3(kFusedThreads), lds, s, P, a);
     return hipGetLastError();
   }
