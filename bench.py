@@ -295,19 +295,19 @@ def main():
 
 
 def forward_kernels(w):
-    """The kernels one sa_forward launches for this geometry, dominant first."""
+    """The kernels one sa_forward launches for this geometry: the one-wave
+    kernel alone where it fits (head_dim 128, blocks <= 64 keys, qhead <= 16),
+    else the wavefront-reduction kernel and the MFMA kernel."""
     qhead = w.hq // w.hkv
     if w.head_dim == 128 and w.block_size <= 64 and qhead <= 16:
-        small = f"k_fwd_small<{(w.block_size + 15) // 16}>"
-    else:
-        small = "k_fwd_wave"
-    return small, "k_fwd_mfma"
+        return f"k_fwd_small<{(w.block_size + 15) // 16}>", None
+    return "k_fwd_wave", "k_fwd_mfma"
 
 
 def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s):
-    """Roofline of the forward pass (sa_forward: the wavefront kernel for
-    units under 32 rows, then the MFMA kernel, which exits at once when the
-    build made no such unit). Bound by HBM when the algorithmic intensity is
+    """Roofline of the forward pass (sa_forward: the one-wave kernel where
+    it fits, else the wavefront kernel for units under 32 rows, then the MFMA
+    kernel, which exits at once when the build made no such unit). Bound by HBM when the algorithmic intensity is
     below the fp32 MFMA ridge (157.3 TFLOP/s / 8 TB/s = 19.7 flop/B), else by
     fp32 MFMA. `traffic` comes from the committed FETCH_SIZE + WRITE_SIZE
     summary for this workload, and only while the kernel's source is the one
@@ -316,12 +316,14 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s):
     ridge = FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if fwd_flops / fwd_bytes < ridge:
         achieved, peak, unit, bound = fwd_bytes / fwd_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
-        kernels = f"{small} + {mfma}"
+        kernels = small if mfma is None else f"{small} + {mfma}"
+        dominant = small
     else:
         achieved, peak, unit, bound = fwd_flops / fwd_s / 1e12, FP32_MFMA_PEAK_TFLOPS, "TFLOP/s", "mfma"
-        kernels = f"{mfma} + {small}"
+        kernels = small if mfma is None else f"{mfma} + {small}"
+        dominant = small if mfma is None else mfma
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": measured_traffic(w.name, small),
+            "frac": achieved / peak, "traffic": measured_traffic(w.name, dominant),
             "kernel": f"sa_forward ({kernels})", "alg_bytes_per_launch": int(fwd_bytes),
             "alg_flops_per_launch": int(fwd_flops), "avg_launch_us": fwd_s * 1e6}
 

@@ -232,20 +232,16 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch, in
   if (idx->cap_edges > sa::kCapUnitEdges) idx->cap_edges = sa::kCapUnitEdges;
   const bool mfma_ok = head_dim == sa::kMfmaHeadDim && block_size <= sa::kMfmaMaxBlock &&
                        sa::mfma_enabled();
-  // Small problems on the one-wave-per-unit kernel keep every unit there: a
-  // slot with many edges becomes several 16-row units (at most tq*topk <= 4096
-  // edges a head, so the extra block reads stay small) and the forward needs
-  // no MFMA-kernel launch.
-  const bool all_small = sa::small_kernel_fits(head_dim, block_size, page_size, qhead) &&
-                         sa::fused_build_fits(tq, topk, (int64_t)batch * (max_pages / (block_size / page_size)),
-                                              batch, hkv);
-  // With the one-wave kernel a slot that does not fit one of its units (16
-  // rows) goes to the MFMA path whole instead of being split, so no block is
-  // read twice; otherwise slots of 32 rows or more do.
-  const int32_t min_rows = sa::small_kernel_fits(head_dim, block_size, page_size, qhead)
-                               ? sa::small_kernel_rows() + 1 : sa::kMfmaMinRows;
-  idx->mfma_min_rows = (mfma_ok && !all_small) ? min_rows : INT32_MAX;
-  idx->wave_cap_edges = sa::small_kernel_fits(head_dim, block_size, page_size, qhead)
+  // Where the one-wave-per-unit kernel fits (head_dim 128, blocks of at most
+  // 64 keys, qhead <= 16) it takes every slot: a slot with more than 16 rows
+  // becomes several 16-row units that read the same block close together in
+  // time, so the repeat reads mostly hit L2 / MALL. Measured on MI355X this
+  // beats the LDS-staged MFMA kernel on the ragged mixed batch (forward 446 ->
+  // 382 us) and on slots shared by hundreds of queries; the MFMA kernels
+  // take the other geometries, from kMfmaMinRows rows a slot.
+  const bool small_fit = sa::small_kernel_fits(head_dim, block_size, page_size, qhead);
+  idx->mfma_min_rows = (mfma_ok && !small_fit) ? sa::kMfmaMinRows : INT32_MAX;
+  idx->wave_cap_edges = small_fit
                             ? (sa::small_kernel_rows() / qhead > 0 ? sa::small_kernel_rows() / qhead : 1)
                             : idx->cap_edges;
   const int64_t slots = (int64_t)hkv * idx->nbs;

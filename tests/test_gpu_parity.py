@@ -121,19 +121,43 @@ def test_random_d128_end_to_end(seed):
 
 
 # Larger random batches (more than 4096 entries a head) on head_dim 128 and
-# blocks of at most 64 keys: slots that outgrow one 16-row unit take the MFMA
-# kernel for such blocks (16-row tiles staged through LDS).
-MFMA16_GEOM = [(4, 1), (8, 2), (16, 1), (16, 3), (16, 4), (32, 2), (2, 8), (8, 4)]
-MFMA16_SEEDS = [0, 1, 3, 4, 5, 6, 7, 8, 9, 10, 11, 13]
+# blocks of at most 64 keys: every slot stays on the one-wave kernel, a slot
+# with more than 16 rows split into several 16-row units over the same block.
+SPLIT_GEOM = [(4, 1), (8, 2), (16, 1), (16, 3), (16, 4), (32, 2), (2, 8), (8, 4)]
+SPLIT_SEEDS = [0, 1, 3, 4, 5, 6, 7, 8, 9, 10, 11, 13]
 
 
-@pytest.mark.parametrize("seed", MFMA16_SEEDS)
-def test_random_d128_mfma_units(seed):
-    ps, ppb = MFMA16_GEOM[seed % len(MFMA16_GEOM)]
+@pytest.mark.parametrize("seed", SPLIT_SEEDS)
+def test_random_d128_split_units(seed):
+    ps, ppb = SPLIT_GEOM[seed % len(SPLIT_GEOM)]
     w = W.make_random(2100 + seed, batch=2 + seed % 2, qo_max=700, kv_max=900, hkv=1 + seed % 2,
                       qhead=[2, 4, 8, 16][seed % 4], head_dim=128, page_size=ps,
                       pages_per_block=ppb, topk=8)
-    _print_case("random_d128_mfma", seed=seed, tq=w.tq, bs=w.block_size, qhead=w.hq // w.hkv)
+    _print_case("random_d128_split", seed=seed, tq=w.tq, bs=w.block_size, qhead=w.hq // w.hkv)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    assert info["num_units_mfma"] == 0
+    assert info["num_units_wave"] > int(ref["num_sel"].sum())     # some slots were split
+    check_units(arrs, info, ref, idx.c.wave_cap_edges, w)
+    out, lse = run_attention(w, d)
+    _check_output(w, out, lse)
+
+
+# More than 16 query heads per KV head on head_dim 128 and blocks of at most
+# 64 keys: slots of 32 rows or more take the MFMA kernel for such blocks
+# (16-row tiles staged through LDS), the rest the wavefront-reduction kernel.
+WIDE_GEOM = [(16, 4), (8, 2), (16, 1), (4, 8), (32, 2), (16, 3)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_d128_wide_gqa_mfma_units(seed):
+    ps, ppb = WIDE_GEOM[seed % len(WIDE_GEOM)]
+    w = W.make_random(2300 + seed, batch=2, qo_max=300, kv_max=700, hkv=1 + seed % 2,
+                      qhead=[17, 20, 24, 32][seed % 4], head_dim=128, page_size=ps,
+                      pages_per_block=ppb, topk=6)
+    _print_case("random_d128_wide_gqa", seed=seed, tq=w.tq, bs=w.block_size, qhead=w.hq // w.hkv)
     d = dev_inputs(w)
     idx = run_index(w, d)
     ref = oracle_index(w)
