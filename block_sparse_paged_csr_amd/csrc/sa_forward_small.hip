@@ -6,9 +6,9 @@
 // process_work_unit over the block's valid, causally alive positions, like the
 // other forward kernels.
 //
-// One wavefront per unit, no workgroup barriers: the four waves of a
-// workgroup run independent unit streams (units w0, w0 + NW, w0 + 2 NW, ... for
-// NW waves in the grid). The unit's (up to) 16 rows form one 16x16 tile on
+// One wavefront per unit: the four waves of a workgroup run their own unit
+// streams (units w0, w0 + NW, w0 + 2 NW, ... for NW waves in the grid), kept
+// in step by one workgroup barrier per unit and sharing nothing else. The unit's (up to) 16 rows form one 16x16 tile on
 // fp32 matrix cores (v_mfma_f32_16x16x4f32) and its block is streamed in
 // pieces of 16 keys: first the K pieces (scores of all keys stay in registers),
 // then the exact softmax over the block, then the V pieces. The contraction
@@ -117,7 +117,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int li = lane & 15, g = lane >> 4;
   const int32_t NW = (int32_t)gridDim.x * kWaves;
   const int32_t u0 = (int32_t)blockIdx.x * kWaves + w;
-  if (u0 >= num_units) return;       // waves never synchronise with each other
+  // The four waves of a workgroup take four neighbouring units at each step
+  // of their loops (the split units of one slot read the same block), and a
+  // workgroup barrier per unit keeps them in step, so that the second read
+  // of a block finds it in cache. Every wave passes the same number of
+  // barriers: that of the workgroup's first wave, which has the most units.
+  const int32_t ub = u0 - w;
+  const int32_t n_bar = ub < num_units ? (num_units - ub + NW - 1) / NW : 0;
+  if (u0 >= num_units) {
+    for (int32_t i = 0; i < n_bar; ++i) __builtin_amdgcn_s_barrier();
+    return;
+  }
   WaveLds& S = s_wave[w];
 
   const int32_t qhead = A.qhead;
@@ -194,6 +204,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   load_piece(IC<0>{}, 0, true, bufA);
 
   for (int32_t j = 0; j < n_units; ++j) {
+    __builtin_amdgcn_s_barrier();
     const int rs = j & (kRecRing - 1), ms = j % kMetaRing;
     const int rs1 = (j + 1) & (kRecRing - 1), ms1 = (j + 1) % kMetaRing;
     const int rs2 = (j + 2) & (kRecRing - 1), ms2 = (j + 2) % kMetaRing;
@@ -320,6 +331,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     step(IC<0>{}); step(IC<1>{}); step(IC<2>{}); step(IC<3>{});
     step(IC<4>{}); step(IC<5>{}); step(IC<6>{}); step(IC<7>{});
   }
+  for (int32_t i = n_units; i < n_bar; ++i) __builtin_amdgcn_s_barrier();
 }
 
 template <int NCH>
