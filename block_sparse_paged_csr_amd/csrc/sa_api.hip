@@ -133,6 +133,8 @@ ScratchLayout scratch_layout(const sa_index* idx) {
   L.keys = o;    o = align256(o + 4 * (size_t)idx->max_edges);
   L.qinfo = o;   o = align256(o + 8 * (size_t)idx->tq);
   L.agg = o;     o = align256(o + sizeof(HeadAgg) * (size_t)idx->hkv);
+  L.chunk_agg = o;
+  o = align256(o + sizeof(ChunkAgg) * (size_t)idx->hkv * (size_t)scan_chunks(idx->nbs));
   L.end = o;
   return L;
 }
@@ -159,6 +161,7 @@ IndexPtrs index_ptrs(const sa_index* idx) {
   P.keys = reinterpret_cast<int32_t*>(b + L.keys);
   P.qinfo = reinterpret_cast<int2*>(b + L.qinfo);
   P.agg = reinterpret_cast<HeadAgg*>(b + L.agg);
+  P.chunk_agg = reinterpret_cast<ChunkAgg*>(b + L.chunk_agg);
   return P;
 }
 

@@ -6,12 +6,14 @@
 //   k_index_hist     one thread per (q, h, r): drop padding / past-lk ranks,
 //                    flag ids outside [-1, msb), check the block's touched
 //                    page ids, count edges per (h, raw slot)
-//   k_index_scan     one workgroup per head: exclusive scans of the counts,
-//                    compaction of nonempty slots, plateaued offsets, unit
-//                    counts per slot
+//   k_index_scan     a workgroup per chunk of 2048 slots of a head, chained by
+//                    a decoupled look-back: exclusive scans of the counts,
+//                    compaction of nonempty slots, unit counts per slot
 //   k_index_scatter  one thread per kept (q, h, r): atomic cursor per slot,
 //                    key q*topk + r into the slot's segment (unordered)
-//   k_index_rank     per compact slot: rank of each key inside the segment
+//   k_index_rank     persistent over the nonempty slots of all heads: rank
+//                    of each key inside its slot's segment; the plateau of
+//                    sel_slots / sel_offsets past the nonempty slots
 //                    (keys are unique) -> edges and inv in (q, r) order, then
 //                    the slot's work units; workgroup 0 fills the header
 //
@@ -29,8 +31,10 @@ namespace sa {
 
 namespace {
 
-constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 4;
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = kScanChunkSlots / kScanThreads;   // slots per thread
+constexpr int kLookbackSpins = 1 << 22;              // then the build reports a runtime error
+constexpr uint64_t kRankLookback = 5;                // error rank: a head's totals never appeared
 
 __device__ inline int4 add4(int4 a, int4 b) {
   return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
@@ -57,13 +61,16 @@ __device__ inline int4 wave_incl_scan4(int4 v) {
 // the MFMA minimum) becomes ceil(c / cap) MFMA units; a smaller one becomes
 // ceil(c / wave_cap) wavefront units. Part i of k spans
 // [floor(i*c/k), floor((i+1)*c/k)), so the parts of a slot are near-equal.
-__device__ inline void unit_split(int c, int cap, int wave_cap, int thr_e, int* n_wave,
+__device__ inline void unit_split(int c, const BuildArgs& A, int thr_e, int* n_wave,
                                   int* n_mfma) {
-  *n_wave = 0;
-  *n_mfma = 0;
-  if (c <= 0) return;
-  if (c >= thr_e) *n_mfma = (c + cap - 1) / cap;
-  else *n_wave = (c + wave_cap - 1) / wave_cap;
+  const bool is_m = c >= thr_e;
+  const int cap = is_m ? A.cap_edges : A.wave_cap_edges;
+  const uint32_t n = (uint32_t)(c + cap - 1);
+  // the magic division is exact while n * cap < 2^40 (caps are <= 2048)
+  const uint32_t k = n < (1u << 24) ? div_magic(n, is_m ? A.cap_magic : A.wave_cap_magic)
+                                    : n / (uint32_t)cap;
+  *n_wave = c > 0 && !is_m ? (int)k : 0;
+  *n_mfma = c > 0 && is_m ? (int)k : 0;
 }
 
 __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
@@ -146,69 +153,108 @@ __global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
   atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
 }
 
+// Workgroup (h, c) scans chunk c (kScanChunkSlots slots) of head h: its
+// counts, loaded together, give the local sums; the chunk's offset within
+// the head comes from a decoupled look-back over the chunks before it
+// (chunk aggregates and inclusive sums tagged with this build's epoch).
+// Chunks of a head are dispatched in order, so every chunk waited on is
+// already running or done; a spin limit turns a missing chunk into a
+// runtime error instead of a hang. Outputs per nonempty slot: its compact
+// position, CSR offset, unit offsets, and the scatter cursor. The last chunk
+// writes the head totals and sel_offsets at the end of the compact list; the
+// rank kernel fills the rest of the plateau.
 __global__ __launch_bounds__(kScanThreads) void k_index_scan(IndexPtrs P, BuildArgs A) {
-  const int32_t h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  __shared__ int4 s_wave[kScanThreads / 64];
-  __shared__ int4 s_carry;
-  if (tid == 0) s_carry = make_int4(0, 0, 0, 0);
-  __syncthreads();
   const int64_t nbs = A.nbs;
+  const int32_t nch = (int32_t)scan_chunks(nbs);
+  const int32_t h = (int32_t)blockIdx.x / nch, ch = (int32_t)blockIdx.x - h * nch;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int kWavesScan = kScanThreads / 64;
+  __shared__ int4 s_wave[kWavesScan];
+  __shared__ int4 s_excl;
   int32_t* cnt = P.cnt + (int64_t)h * nbs;
-  const int cap = A.cap_edges;
   const int thr_e = (int)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
-  for (int64_t base = 0; base < nbs; base += kScanThreads * kScanItems) {
-    int c[kScanItems], nw[kScanItems], nm[kScanItems];
-    int4 mine = make_int4(0, 0, 0, 0);    // edges, nonempty slots, wave units, mfma units
+  const int64_t base = (int64_t)ch * kScanChunkSlots + (int64_t)tid * kScanItems;
+  // clamped loads, none behind its own branch: all of them in flight together
+  int c[kScanItems] = {};
+  if (nbs > 0) {
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
-      const int64_t raw = base + (int64_t)tid * kScanItems + k;
-      c[k] = raw < nbs ? cnt[raw] : 0;
+      const int64_t raw = base + k;
+      const int v = cnt[raw < nbs ? raw : nbs - 1];
+      c[k] = raw < nbs ? v : 0;
     }
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      unit_split(c[k], cap, A.wave_cap_edges, thr_e, &nw[k], &nm[k]);
-      mine = add4(mine, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
-    }
-    const int4 incl = wave_incl_scan4(mine);
-    if (lane == 63) s_wave[wid] = incl;
-    __syncthreads();
-    if (wid == 0) {
-      int4 w = lane < kScanThreads / 64 ? s_wave[lane] : make_int4(0, 0, 0, 0);
-      w = wave_incl_scan4(w);
-      if (lane < kScanThreads / 64) s_wave[lane] = w;
-    }
-    __syncthreads();
-    const int4 carry = s_carry;
-    int4 run = add4(carry, sub4(incl, mine));
-    if (wid > 0) run = add4(run, s_wave[wid - 1]);
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      const int64_t raw = base + (int64_t)tid * kScanItems + k;
-      if (c[k] > 0) {
-        const int64_t j = run.y;
-        P.sel_slots[(int64_t)h * nbs + j] = (int32_t)raw;
-        P.sel_offsets[(int64_t)h * (nbs + 1) + j] = run.x;
-        P.slot_uw[(int64_t)h * nbs + j] = run.z;
-        P.slot_um[(int64_t)h * nbs + j] = run.w;
-        cnt[raw] = run.x;                               // scatter cursor
-      }
-      run = add4(run, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
-    }
-    __syncthreads();
-    if (tid == 0) s_carry = add4(carry, s_wave[kScanThreads / 64 - 1]);
-    __syncthreads();
   }
-  const int4 tot = s_carry;
+  int nw[kScanItems], nm[kScanItems];
+  int4 mine = make_int4(0, 0, 0, 0);        // edges, nonempty slots, wave units, mfma units
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    unit_split(c[k], A, thr_e, &nw[k], &nm[k]);
+    mine = add4(mine, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
+  }
+  const int4 incl = wave_incl_scan4(mine);
+  if (lane == 63) s_wave[wid] = incl;
+  __syncthreads();
+  int4 pre = make_int4(0, 0, 0, 0), agg = make_int4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < kWavesScan; ++i) {
+    const int4 t = s_wave[i];
+    if (i < wid) pre = add4(pre, t);
+    agg = add4(agg, t);
+  }
   if (tid == 0) {
-    P.num_sel[h] = tot.y;
-    P.head_e[h] = tot.x;
-    P.head_uw[h] = tot.z;
-    P.head_um[h] = tot.w;
+    ChunkAgg* my = P.chunk_agg + (int64_t)h * nch + ch;
+    int4 excl = make_int4(0, 0, 0, 0);
+    if (ch > 0) {
+      my->agg = agg;
+      __hip_atomic_store(&my->flag, A.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      for (int32_t p = ch - 1; p >= 0; --p) {
+        const ChunkAgg* pa = P.chunk_agg + (int64_t)h * nch + p;
+        uint64_t f = 0;
+        int spins = 0;
+        while (true) {
+          f = __hip_atomic_load(&pa->flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+          if (f == A.epoch || f == A.epoch + 1 || spins >= kLookbackSpins) break;
+          __builtin_amdgcn_s_sleep(1);
+          ++spins;
+        }
+        if (f != A.epoch && f != A.epoch + 1) {
+          atomicMin(&P.hdr->err_key, err_key(kRankLookback, 0));
+          break;
+        }
+        if (f == A.epoch + 1) {
+          excl = add4(excl, pa->incl);
+          break;
+        }
+        excl = add4(excl, pa->agg);
+      }
+    }
+    my->incl = add4(excl, agg);
+    __hip_atomic_store(&my->flag, A.epoch + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    s_excl = excl;
+    if (ch == nch - 1) {
+      const int4 tot = add4(excl, agg);
+      P.num_sel[h] = tot.y;
+      P.head_e[h] = tot.x;
+      P.head_uw[h] = tot.z;
+      P.head_um[h] = tot.w;
+      P.sel_offsets[(int64_t)h * (nbs + 1) + tot.y] = tot.x;
+    }
   }
-  for (int64_t j = tot.y + tid; j < nbs; j += kScanThreads) P.sel_slots[(int64_t)h * nbs + j] = -1;
-  for (int64_t j = tot.y + tid; j <= nbs; j += kScanThreads)
-    P.sel_offsets[(int64_t)h * (nbs + 1) + j] = tot.x;
+  __syncthreads();
+  int4 run = add4(add4(s_excl, pre), sub4(incl, mine));
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t raw = base + k;
+    if (c[k] > 0) {
+      const int64_t j = run.y;
+      P.sel_slots[(int64_t)h * nbs + j] = (int32_t)raw;
+      P.sel_offsets[(int64_t)h * (nbs + 1) + j] = run.x;
+      P.slot_uw[(int64_t)h * nbs + j] = run.z;
+      P.slot_um[(int64_t)h * nbs + j] = run.w;
+      cnt[raw] = run.x;                               // scatter cursor
+    }
+    run = add4(run, make_int4(c[k], c[k] > 0, nw[k], nm[k]));
+  }
 }
 
 __device__ inline int64_t head_edge_base(const IndexPtrs& P, int32_t h) {
@@ -295,113 +341,136 @@ struct SlotInfo {
   int64_t base;
 };
 
-// Each workgroup owns 4 consecutive compact-slot ids g = 4*blockIdx + wave
-// over all heads (h = g / nbs, j = g % nbs). Slots with <= 64 keys are ranked
-// by their wave with lane shuffles. If any of the 4 has more, the whole
-// workgroup ranks them one after another through LDS.
+// Persistent over the nonempty slots of all heads, numbered densely head by
+// head (g = sum of num_sel over heads before h, plus j): each pass of a
+// workgroup takes 4 consecutive ids g = 4*gg + wave. Slots with <= 64 keys
+// are ranked by their wave with lane shuffles. If any of the 4 has more, the
+// whole workgroup ranks them one after another through LDS.
 __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
   if (blockIdx.x == 0 && threadIdx.x == 0) finalize_header(P, A);
   if (A.nbs == 0) return;                          // no slots at all (msb == 0)
   __shared__ SlotInfo s_slot[4];
   __shared__ __align__(16) int32_t s_keys[kRankChunk];
+  __shared__ int64_t s_total;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t g = (int64_t)blockIdx.x * 4 + w;
-  if (lane == 0) {
-    SlotInfo si{};
-    const int32_t h = (int32_t)(g / A.nbs);
-    const int64_t j = g % A.nbs;
-    if (h < A.hkv) {
-      // all loads independent of each other
-      const int32_t nsel = P.num_sel[h];
-      const int32_t o0 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j];
-      const int32_t o1 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j + 1];
-      const int32_t raw = P.sel_slots[(int64_t)h * A.nbs + j];
-      int32_t uw = P.slot_uw[(int64_t)h * A.nbs + j], um = P.slot_um[(int64_t)h * A.nbs + j];
-      int64_t hb = 0;
-      for (int32_t i = 0; i < h; ++i) {
-        hb += P.head_e[i];
-        uw += P.head_uw[i];
-        um += P.head_um[i];
-      }
-      if (j < nsel) {
+  if (tid == 0) {
+    int64_t t = 0;
+    for (int32_t h = 0; h < A.hkv; ++h) t += P.num_sel[h];
+    s_total = t;
+  }
+  // plateau past each head's nonempty slots: sel_slots -1, sel_offsets E_h
+  // (the scan wrote sel_offsets at num_sel itself)
+  {
+    const int64_t gsz = (int64_t)gridDim.x * 256, gid = (int64_t)blockIdx.x * 256 + tid;
+    for (int32_t h = 0; h < A.hkv; ++h) {
+      const int32_t ns = P.num_sel[h];
+      const int32_t eh = P.head_e[h];
+      for (int64_t j = ns + gid; j < A.nbs; j += gsz) P.sel_slots[(int64_t)h * A.nbs + j] = -1;
+      for (int64_t j = ns + 1 + gid; j <= A.nbs; j += gsz)
+        P.sel_offsets[(int64_t)h * (A.nbs + 1) + j] = eh;
+    }
+  }
+  __syncthreads();
+  const int64_t total = s_total;
+  const int32_t thr_e = (int32_t)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
+  for (int64_t gg = blockIdx.x; 4 * gg < total; gg += gridDim.x) {
+    const int64_t g = 4 * gg + w;
+    if (lane == 0) {
+      SlotInfo si{};
+      if (g < total) {
+        // head of dense id g and the totals of the heads before it
+        int64_t j = g, hb = 0;
+        int32_t h = 0, uw = 0, um = 0;
+        for (; h < A.hkv; ++h) {
+          const int32_t ns = P.num_sel[h];
+          if (j < ns) break;
+          j -= ns;
+          hb += P.head_e[h];
+          uw += P.head_uw[h];
+          um += P.head_um[h];
+        }
+        const int32_t o0 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j];
+        const int32_t o1 = P.sel_offsets[(int64_t)h * (A.nbs + 1) + j + 1];
+        const int32_t raw = P.sel_slots[(int64_t)h * A.nbs + j];
         si.n = o1 - o0;
         si.off0 = o0;
         si.base = hb;
-        si.uw = uw;
-        si.um = um;
+        si.uw = uw + P.slot_uw[(int64_t)h * A.nbs + j];
+        si.um = um + P.slot_um[(int64_t)h * A.nbs + j];
         si.b = raw / A.msb;
         si.blk = raw % A.msb;
         const int64_t q0 = A.cu[si.b], qo_len = A.cu[si.b + 1] - q0;
         const int64_t lk = kv_len_dev(A.used, si.b, A.msb, A.block_size);
         si.lk = (int32_t)lk;
         si.delta = (int32_t)((lk >= qo_len ? lk - qo_len : 0) - q0);
+        si.h = h;
+        si.j = (int32_t)j;
       }
+      s_slot[w] = si;
     }
-    si.h = h;
-    si.j = (int32_t)j;
-    s_slot[w] = si;
-  }
-  __syncthreads();
-  const bool block_mode =
-      s_slot[0].n > 64 || s_slot[1].n > 64 || s_slot[2].n > 64 || s_slot[3].n > 64;
-  if (!block_mode) {
-    const int32_t n = s_slot[w].n;
-    if (n > 0) {
-      const int32_t* seg = P.keys + s_slot[w].base + s_slot[w].off0;
-      const int32_t key = lane < n ? seg[lane] : INT32_MAX;
-      int32_t rank = 0;
-      for (int32_t x = 0; x < n; ++x) rank += __shfl(key, x, 64) < key;
-      if (lane < n) write_edge(P, A, s_slot[w].h, s_slot[w].base, s_slot[w].off0, key, rank);
-    }
-  } else {
-    for (int s = 0; s < 4; ++s) {
-      const int32_t n = s_slot[s].n;
-      if (n == 0) continue;
-      const int32_t* seg = P.keys + s_slot[s].base + s_slot[s].off0;
-      for (int32_t pass = 0; pass < n; pass += 256 * kRankKeys) {
-        int32_t mine[kRankKeys], rank[kRankKeys];
+    __syncthreads();
+    const bool block_mode =
+        s_slot[0].n > 64 || s_slot[1].n > 64 || s_slot[2].n > 64 || s_slot[3].n > 64;
+    if (!block_mode) {
+      const int32_t n = s_slot[w].n;
+      if (n > 0) {
+        const int32_t* seg = P.keys + s_slot[w].base + s_slot[w].off0;
+        const int32_t key = lane < n ? seg[lane] : INT32_MAX;
+        int32_t rank = 0;
+        for (int32_t x = 0; x < n; ++x) rank += __shfl(key, x, 64) < key;
+        if (lane < n) write_edge(P, A, s_slot[w].h, s_slot[w].base, s_slot[w].off0, key, rank);
+      }
+    } else {
+      for (int s = 0; s < 4; ++s) {
+        const int32_t n = s_slot[s].n;
+        if (n == 0) continue;
+        const int32_t* seg = P.keys + s_slot[s].base + s_slot[s].off0;
+        for (int32_t pass = 0; pass < n; pass += 256 * kRankKeys) {
+          int32_t mine[kRankKeys], rank[kRankKeys];
 #pragma unroll
-        for (int k = 0; k < kRankKeys; ++k) {
-          const int32_t i = pass + tid + 256 * k;
-          mine[k] = i < n ? seg[i] : INT32_MAX;
-          rank[k] = 0;
-        }
-        for (int32_t c0 = 0; c0 < n; c0 += kRankChunk) {
-          const int32_t m = n - c0 < kRankChunk ? n - c0 : kRankChunk;
-          const int32_t m4 = (m + 3) & ~3;
-          __syncthreads();
-          for (int32_t x = tid; x < m4; x += 256) s_keys[x] = x < m ? seg[c0 + x] : INT32_MAX;
-          __syncthreads();
-          for (int32_t x = 0; x < m4; x += 4) {
-            const int4 kk = *reinterpret_cast<const int4*>(&s_keys[x]);
+          for (int k = 0; k < kRankKeys; ++k) {
+            const int32_t i = pass + tid + 256 * k;
+            mine[k] = i < n ? seg[i] : INT32_MAX;
+            rank[k] = 0;
+          }
+          for (int32_t c0 = 0; c0 < n; c0 += kRankChunk) {
+            const int32_t m = n - c0 < kRankChunk ? n - c0 : kRankChunk;
+            const int32_t m4 = (m + 3) & ~3;
+            __syncthreads();
+            for (int32_t x = tid; x < m4; x += 256) s_keys[x] = x < m ? seg[c0 + x] : INT32_MAX;
+            __syncthreads();
+            for (int32_t x = 0; x < m4; x += 4) {
+              const int4 kk = *reinterpret_cast<const int4*>(&s_keys[x]);
 #pragma unroll
-            for (int k = 0; k < kRankKeys; ++k)
-              rank[k] += (kk.x < mine[k]) + (kk.y < mine[k]) + (kk.z < mine[k]) + (kk.w < mine[k]);
+              for (int k = 0; k < kRankKeys; ++k)
+                rank[k] += (kk.x < mine[k]) + (kk.y < mine[k]) + (kk.z < mine[k]) + (kk.w < mine[k]);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < kRankKeys; ++k) {
+            const int32_t i = pass + tid + 256 * k;
+            if (i < n)
+              write_edge(P, A, s_slot[s].h, s_slot[s].base, s_slot[s].off0, mine[k], rank[k]);
           }
         }
-#pragma unroll
-        for (int k = 0; k < kRankKeys; ++k) {
-          const int32_t i = pass + tid + 256 * k;
-          if (i < n)
-            write_edge(P, A, s_slot[s].h, s_slot[s].base, s_slot[s].off0, mine[k], rank[k]);
-        }
       }
     }
-  }
-  // Work units of this wave's slot, in CSR order within each kind.
-  const SlotInfo si = s_slot[w];
-  if (si.n == 0) return;
-  const int32_t thr_e = (int32_t)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
-  const bool is_m = si.n >= thr_e;
-  const int32_t cap = is_m ? A.cap_edges : A.wave_cap_edges;
-  const int32_t k_units = (si.n + cap - 1) / cap;
-  Unit* dst = is_m ? P.units_mfma + si.um : P.units_wave + si.uw;
-  const int64_t e_base = si.base + si.off0;
-  for (int32_t i = lane; i < k_units; i += 64) {
-    const int32_t s0 = (int32_t)(((int64_t)i * si.n) / k_units);
-    const int32_t s1 = (int32_t)(((int64_t)(i + 1) * si.n) / k_units);
-    dst[i] = Unit{si.h, si.j, (int32_t)(e_base + s0), (int32_t)(e_base + s1),
-                  si.b, si.blk, si.lk, si.delta};
+    // Work units of this wave's slot, in CSR order within each kind.
+    const SlotInfo si = s_slot[w];
+    if (si.n > 0) {
+      const bool is_m = si.n >= thr_e;
+      const int32_t cap = is_m ? A.cap_edges : A.wave_cap_edges;
+      const int32_t k_units = (si.n + cap - 1) / cap;
+      Unit* dst = is_m ? P.units_mfma + si.um : P.units_wave + si.uw;
+      const int64_t e_base = si.base + si.off0;
+      for (int32_t i = lane; i < k_units; i += 64) {
+        const int32_t s0 = (int32_t)(((int64_t)i * si.n) / k_units);
+        const int32_t s1 = (int32_t)(((int64_t)(i + 1) * si.n) / k_units);
+        dst[i] = Unit{si.h, si.j, (int32_t)(e_base + s0), (int32_t)(e_base + s1),
+                      si.b, si.blk, si.lk, si.delta};
+      }
+    }
+    __syncthreads();                               // s_slot and s_keys are reused
   }
 }
 
@@ -412,9 +481,6 @@ constexpr int64_t kFusedMaxSlots = 16384;
 constexpr int64_t kFusedMaxQ = 2048;
 constexpr int32_t kFusedMaxBatch = 2048;
 constexpr size_t kFusedMaxLds = 150 * 1024;            // dynamic LDS of the fused build
-constexpr int kLookbackSpins = 1 << 22;              // then the build reports a runtime error
-constexpr uint64_t kRankLookback = 5;                // error rank: a head's totals never appeared
-
 // Inclusive wave64 scans on DPP: row_shr 1, 2, 4, 8 inside each row of 16
 // lanes, then row_bcast 15 and 31 carry row totals across rows (rows the
 // broadcast does not write keep the identity).
@@ -578,10 +644,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
 
   // ---- entries: drop padding and blocks past lk, flag bad ids and pages, count
   int32_t slot_k[kFusedItems], arr_k[kFusedItems];
+  int64_t col0_k[kFusedItems];                      // first block-table column of the block
+  int32_t touch_k[kFusedItems];                     // pages of the block its valid range touches
 #pragma unroll
   for (int k = 0; k < kFusedItems; ++k) {
     slot_k[k] = -1;
     arr_k[k] = 0;
+    col0_k[k] = 0;
+    touch_k[k] = 0;
     const int32_t i = tid + kFusedThreads * k;
     if (i >= items) continue;
     const int32_t q = i / topk, r = i - q * topk;
@@ -597,21 +667,46 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     const int64_t lk = s_lkb[b];
     const int64_t block_start = (int64_t)v * A.block_size;
     if (block_start >= lk) continue;
-    if (A.num_pages >= 0) {
-      const int64_t block_end = block_start + A.block_size < lk ? block_start + A.block_size : lk;
-      const int64_t col0 = (int64_t)b * A.max_pages + (int64_t)v * A.ppb;
-      int64_t bad = INT64_MAX;
-      for (int32_t pl = 0; pl < A.ppb; ++pl) {
-        const bool touched = block_start + (int64_t)pl * A.page_size < block_end;
-        const int32_t page = touched ? A.block_tables[col0 + pl] : -1;
-        if (page >= A.num_pages && col0 + pl < bad) bad = col0 + pl;
-      }
-      if (bad != INT64_MAX) atomicMin(&s_err, err_key(kRankPage, (uint64_t)bad));
-    }
-    const int32_t slot = b * A.msb + v;
-    slot_k[k] = slot;
-    arr_k[k] = atomicAdd(&s_cnt[slot], 1);            // arrival order, made stable below
+    const int64_t block_end = block_start + A.block_size < lk ? block_start + A.block_size : lk;
+    slot_k[k] = b * A.msb + v;
+    col0_k[k] = (int64_t)b * A.max_pages + (int64_t)v * A.ppb;
+    touch_k[k] = (int32_t)((block_end - block_start + A.page_size - 1) / A.page_size);
   }
+  if (A.num_pages >= 0) {
+    // The pages each kept block's valid range touches must exist (the
+    // forward's block-table check, moved into the build). The reads of all
+    // entries go out together, kPageBatch pages of each per round: clamped
+    // addresses, no load behind a branch.
+    constexpr int kPageBatch = 4;
+    int64_t bad_k[kFusedItems];
+#pragma unroll
+    for (int k = 0; k < kFusedItems; ++k) bad_k[k] = INT64_MAX;
+    for (int32_t p0 = 0; p0 < A.ppb; p0 += kPageBatch) {
+      int32_t page[kFusedItems][kPageBatch];
+#pragma unroll
+      for (int k = 0; k < kFusedItems; ++k)
+#pragma unroll
+        for (int x = 0; x < kPageBatch; ++x) {
+          const int32_t pl = p0 + x;
+          const bool touched = pl < touch_k[k];
+          page[k][x] = A.block_tables[touched ? col0_k[k] + pl : 0];
+        }
+#pragma unroll
+      for (int k = 0; k < kFusedItems; ++k)
+#pragma unroll
+        for (int x = 0; x < kPageBatch; ++x) {
+          const int32_t pl = p0 + x;
+          if (pl < touch_k[k] && page[k][x] >= A.num_pages && col0_k[k] + pl < bad_k[k])
+            bad_k[k] = col0_k[k] + pl;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kFusedItems; ++k)
+      if (bad_k[k] != INT64_MAX) atomicMin(&s_err, err_key(kRankPage, (uint64_t)bad_k[k]));
+  }
+#pragma unroll
+  for (int k = 0; k < kFusedItems; ++k)
+    if (slot_k[k] >= 0) arr_k[k] = atomicAdd(&s_cnt[slot_k[k]], 1);   // arrival order, made stable below
   __syncthreads();
 
   // ---- one scan over the slots: counts -> exclusive offsets (in place), the
@@ -837,9 +932,13 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
   hipLaunchKernelGGL(k_index_init, dim3((unsigned)init_grid), dim3(256), 0, s, P, a);
   const int64_t entries = a.tq * a.hkv * a.topk;
   hipLaunchKernelGGL(k_index_hist, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
-  hipLaunchKernelGGL(k_index_scan, dim3((unsigned)a.hkv), dim3(kScanThreads), 0, s, P, a);
+  hipLaunchKernelGGL(k_index_scan, dim3((unsigned)(a.hkv * scan_chunks(a.nbs))), dim3(kScanThreads),
+                     0, s, P, a);
   hipLaunchKernelGGL(k_index_scatter, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
-  hipLaunchKernelGGL(k_index_rank, dim3(grid_for(slots, 4)), dim3(256), 0, s, P, a);
+  // persistent: a few workgroups per CU loop over the nonempty slots
+  unsigned rank_grid = grid_for(slots, 4);
+  if (rank_grid > 8 * cu_count()) rank_grid = 8 * cu_count();
+  hipLaunchKernelGGL(k_index_rank, dim3(rank_grid), dim3(256), 0, s, P, a);
   return hipGetLastError();
 }
 

@@ -81,6 +81,7 @@ struct ScratchLayout {
   size_t keys;       // int32 [max_edges] scattered (q*topk + r), unordered per slot
   size_t qinfo;      // int2  [tq]        (sequence b, resolved kv length lk_b) per query
   size_t agg;        // HeadAgg [hkv]     per-head totals published by the fused build
+  size_t chunk_agg;  // ChunkAgg [hkv * scan_chunks(nbs)]  per-chunk sums of the slot scan
   size_t end;
 };
 
@@ -90,6 +91,23 @@ struct alignas(64) HeadAgg {
   int64_t e;                  // edges
   int32_t ns, uw, um, pad;    // nonempty slots, wavefront units, MFMA units
   unsigned long long err;     // smallest error key seen by the head (~0ull: none)
+  uint64_t flag;
+};
+
+// Slots scanned by one workgroup of the multi-kernel build.
+constexpr int kScanChunkSlots = 2048;
+// Chunks of one head's slots (at least one, which writes the head's totals).
+__host__ __device__ inline int64_t scan_chunks(int64_t nbs) {
+  return nbs > kScanChunkSlots ? (nbs + kScanChunkSlots - 1) / kScanChunkSlots : 1;
+}
+
+// Sums over one chunk of a head's slots (edges, nonempty slots, wavefront
+// units, MFMA units), published for the chunks after it: `agg` with flag ==
+// that build's epoch, then also `incl` (the sums over this chunk and all
+// before it) with flag == epoch + 1.
+struct alignas(64) ChunkAgg {
+  int4 agg;
+  int4 incl;
   uint64_t flag;
 };
 
@@ -113,6 +131,7 @@ struct IndexPtrs {
   int32_t* keys;
   int2* qinfo;
   HeadAgg* agg;
+  ChunkAgg* chunk_agg;
 };
 
 struct BuildArgs {
@@ -125,7 +144,7 @@ struct BuildArgs {
   int64_t num_pages;
   int32_t hkv, topk, batch, max_pages, block_size, page_size, ppb, msb;
   int32_t qhead, cap_edges, wave_cap_edges, mfma_min_rows;
-  uint64_t epoch;            // distinct per build call; tags the fused build's HeadAgg flags
+  uint64_t epoch;            // distinct per build call, odd; tags HeadAgg / ChunkAgg flags
   uint64_t cap_magic;        // make_div_magic(cap_edges)
   uint64_t wave_cap_magic;   // make_div_magic(wave_cap_edges)
 };
