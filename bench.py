@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--config", default=DEFAULT_CONFIG,
                    choices=["tiny", "decode", "prefill", "ragged", "skewed"])
     p.add_argument("--rotate", type=int, default=4, help="independent input batches cycled")
+    p.add_argument("--kv-dtype", default="f32", choices=["f32", "bf16", "fp16"],
+                   help="storage of the K/V pages (16-bit: sa_forward_kv16, fp32 arithmetic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle leg")
@@ -87,7 +89,7 @@ def variants(name, rotate):
     return base, out, k, v
 
 
-def algorithmic_work(w, arrs, info):
+def algorithmic_work(w, arrs, info, kv_elem_bytes=4):
     """Bytes and flops the method must move/do for this batch, from the index.
 
     forward: K and V rows of every selected block once (valid positions with a
@@ -118,7 +120,7 @@ def algorithmic_work(w, arrs, info):
             page = w.block_tables[b, blk * ppb + pl]
             valid += np.where((p1 > p0) & (page >= 0), p1 - p0, 0)
         edges_per_slot = np.diff(offs[h, :n + 1]).astype(np.int64)
-        kv_bytes += int(2 * valid.sum() * d * 4)
+        kv_bytes += int(2 * valid.sum() * d * kv_elem_bytes)
         flops += int((edges_per_slot * valid).sum() * qhead * 4 * d)
     E = info["total_edges"]
     rows = E * qhead
@@ -191,6 +193,12 @@ def main():
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
     k = t(k_all, torch.float32)
     v = t(v_all, torch.float32)
+    kv16 = args.kv_dtype != "f32"
+    if kv16:
+        # 16-bit storage of the same draws (round to nearest even)
+        dt16 = torch.bfloat16 if args.kv_dtype == "bf16" else torch.float16
+        k, v = k.to(dt16), v.to(dt16)
+        torch.cuda.empty_cache()
     num_pages = int(k_all.shape[0])
     del k_all, v_all
     sets = []
@@ -217,9 +225,9 @@ def main():
         sa.sa_build_index(s["sel"], s["bt"], s["cu"], s["used"], s["idx"])
         if ev is not None:
             ev[1].record()
-        sa.sa_forward(s["idx"], s["q"], k, v, s["bt"], s["cu"], s["used"], w.hq, w.hkv,
-                      w.head_dim, w.block_size, w.page_size, w.softmax_scale, w.causal,
-                      s["o"], s["m"], s["l"])
+        fwd = sa.sa_forward_kv16 if kv16 else sa.sa_forward
+        fwd(s["idx"], s["q"], k, v, s["bt"], s["cu"], s["used"], w.hq, w.hkv, w.head_dim,
+            w.block_size, w.page_size, w.softmax_scale, w.causal, s["o"], s["m"], s["l"])
         if ev is not None:
             ev[2].record()
         sa.sa_combine(s["idx"], s["o"], s["m"], s["l"], w.hq, w.head_dim, s["out"], s["lse"])
@@ -232,7 +240,7 @@ def main():
         step(s)
         info = sa.sa_index_status(s["idx"])
         arrs = {kk: vv.cpu().numpy() for kk, vv in sa.index_arrays(s["idx"], info).items()}
-        work.append(algorithmic_work(s["w"], arrs, info))
+        work.append(algorithmic_work(s["w"], arrs, info, 2 if kv16 else 4))
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
@@ -258,7 +266,7 @@ def main():
     total_bytes = np.mean([p["total_bytes"] for p in per])
     flops = np.mean([p["flops"] for p in per])
     fc_s = (float(np.mean(fwd_ms)) + float(np.mean(comb_ms))) / 1e3
-    roofline = forward_roofline(base, fwd_bytes, flops, fwd_avg_s)
+    roofline = forward_roofline(base, fwd_bytes, flops, fwd_avg_s, args.kv_dtype)
 
     result = {
         "metric": METRIC,
@@ -273,7 +281,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {**base.describe(), "edges_per_batch": int(np.mean([p["edges"] for p in per])),
+        "config": {**base.describe(), "kv_dtype": args.kv_dtype,
+                   "edges_per_batch": int(np.mean([p["edges"] for p in per])),
                    "rotated_batches": len(sets), "parallelism": "single-gpu"},
         "roofline": roofline,
         "forward_plus_combine": {
@@ -304,7 +313,7 @@ def forward_kernels(w):
     return "k_fwd_wave", "k_fwd_mfma"
 
 
-def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s):
+def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32"):
     """Roofline of the forward pass (sa_forward: the one-wave kernel where
     it fits, else the wavefront kernel for units under 32 rows, then the MFMA
     kernel, which exits at once when the build made no such unit). Bound by HBM when the algorithmic intensity is
@@ -313,6 +322,8 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s):
     summary for this workload, and only while the kernel's source is the one
     the counters were taken on."""
     small, mfma = forward_kernels(w)
+    if kv_dtype != "f32":
+        small = small.replace(">", f", {kv_dtype}>")
     ridge = FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if fwd_flops / fwd_bytes < ridge:
         achieved, peak, unit, bound = fwd_bytes / fwd_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
@@ -323,7 +334,9 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s):
         kernels = small if mfma is None else f"{mfma} + {small}"
         dominant = small if mfma is None else mfma
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-            "frac": achieved / peak, "traffic": measured_traffic(w.name, dominant),
+            "frac": achieved / peak,
+            "traffic": measured_traffic(w.name if kv_dtype == "f32" else f"{w.name}_{kv_dtype}",
+                                        dominant),
             "kernel": f"sa_forward ({kernels})", "alg_bytes_per_launch": int(fwd_bytes),
             "alg_flops_per_launch": int(fwd_flops), "avg_launch_us": fwd_s * 1e6}
 

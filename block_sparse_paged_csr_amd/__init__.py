@@ -92,6 +92,8 @@ def _declare(lib):
         "sa_index_status": [idxp, POINTER(SaIndexInfo), vp],
         "sa_forward": [idxp, vp, i64, vp, i64, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32,
                        c_float, i32, vp, vp, vp, vp],
+        "sa_forward_kv16": [idxp, vp, i64, vp, i64, vp, i64, i32, vp, vp, vp, i32, i32, i32, i32,
+                            i32, c_float, i32, vp, vp, vp, vp],
         "sa_combine": [idxp, vp, vp, vp, i32, i32, vp, vp, vp],
         "sa_attention_workspace_bytes": [i64, i32, i32, i32, i32, i32, i32, i32, i32,
                                          POINTER(c_size_t)],
@@ -240,6 +242,44 @@ def sa_forward(index: Index, q, k_pages, v_pages, block_tables, cu_seqlens_q, us
     return o_partial, m_partial, l_partial
 
 
+SA_KV_F32, SA_KV_BF16, SA_KV_F16 = 0, 1, 2
+_KV16_FORMATS = {torch.bfloat16: SA_KV_BF16, torch.float16: SA_KV_F16}
+
+
+def sa_forward_kv16(index: Index, q, k_pages, v_pages, block_tables, cu_seqlens_q, used_kv_lens,
+                    hq, hkv, head_dim, block_size, page_size, softmax_scale, causal,
+                    o_partial=None, m_partial=None, l_partial=None):
+    """sa_forward with K/V pages stored as bfloat16 or float16 tensors (the
+    format follows their dtype; both must match); returns the fp32 partials."""
+    _check_head_dims(q, k_pages, v_pages)
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        if not isinstance(t, torch.Tensor) or t.dtype not in _KV16_FORMATS:
+            raise TypeError(f"{name} must be a bfloat16 or float16 tensor")
+    if k_pages.dtype != v_pages.dtype:
+        raise TypeError("k_pages and v_pages must share one dtype")
+    fmt = _KV16_FORMATS[k_pages.dtype]
+    rows = index.c.max_edges * (hq // hkv if hkv > 0 else 1)
+    dev = q.device
+    if o_partial is None:
+        o_partial = torch.empty((rows, head_dim), dtype=torch.float32, device=dev)
+    if m_partial is None:
+        m_partial = torch.empty(rows, dtype=torch.float32, device=dev)
+    if l_partial is None:
+        l_partial = torch.empty(rows, dtype=torch.float32, device=dev)
+    st = lib().sa_forward_kv16(
+        ctypes.byref(index.c), _ptr(q, torch.float32, "q"), q.numel(),
+        _ptr(k_pages, k_pages.dtype, "k_pages"), k_pages.numel(),
+        _ptr(v_pages, v_pages.dtype, "v_pages"), v_pages.numel(), fmt,
+        _ptr(block_tables, torch.int32, "block_tables"),
+        _ptr(cu_seqlens_q, torch.int64, "cu_seqlens_q"),
+        _ptr(used_kv_lens, torch.int32, "used_kv_lens"),
+        hq, hkv, head_dim, block_size, page_size, float(softmax_scale), int(bool(causal)),
+        _ptr(o_partial, torch.float32, "o_partial"), _ptr(m_partial, torch.float32, "m_partial"),
+        _ptr(l_partial, torch.float32, "l_partial"), _stream(dev))
+    _check(st)
+    return o_partial, m_partial, l_partial
+
+
 def sa_combine(index: Index, o_partial, m_partial, l_partial, hq, head_dim, out=None,
                lse=None, with_lse=True):
     dev = o_partial.device
@@ -362,6 +402,7 @@ def index_arrays(index: Index, info: dict | None = None) -> dict:
 
 __all__ = [
     "SaError", "SaIndex", "Index", "Workspace", "lib", "sa_index_plan", "sa_build_index",
-    "sa_index_status", "sa_forward", "sa_combine", "sa_attention",
+    "sa_index_status", "sa_forward", "sa_forward_kv16", "sa_combine", "sa_attention",
+    "SA_KV_F32", "SA_KV_BF16", "SA_KV_F16",
     "sa_attention_workspace_bytes", "index_arrays", "STATUS_NAMES",
 ]

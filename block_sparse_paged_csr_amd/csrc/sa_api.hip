@@ -314,13 +314,20 @@ sa_status sa_index_status(const sa_index* idx, sa_index_info* out, hipStream_t s
   return ok();
 }
 
-sa_status sa_forward(const sa_index* idx, const float* q, int64_t q_len, const float* k_pages,
-                     int64_t k_len, const float* v_pages, int64_t v_len,
-                     const int32_t* block_tables,
-                     const int64_t* cu_seqlens_q, const int32_t* used_kv_lens, int32_t hq,
-                     int32_t hkv, int32_t head_dim, int32_t block_size, int32_t page_size,
-                     float softmax_scale, int32_t causal, float* o_partial, float* m_partial,
-                     float* l_partial, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// sa_forward's checks (in the page's order) and launch, for K/V pages stored
+// as fp32 or, with `kv16`, as 16-bit words of `kv_format` (`k`, `v` then
+// hold uint16 elements; formats and geometry are checked after the others).
+sa_status forward_common(const sa_index* idx, const float* q, int64_t q_len, const void* k_pages,
+                         int64_t k_len, const void* v_pages, int64_t v_len,
+                         const int32_t* block_tables, const int64_t* cu_seqlens_q,
+                         const int32_t* used_kv_lens, int32_t hq, int32_t hkv, int32_t head_dim,
+                         int32_t block_size, int32_t page_size, float softmax_scale,
+                         int32_t causal, bool kv16, int32_t kv_format, float* o_partial,
+                         float* m_partial, float* l_partial, hipStream_t stream) {
   sa_status st = check_heads_blocks(hq, hkv, head_dim, block_size, page_size);
   if (st != SA_OK) return st;
   if (idx == nullptr || idx->buffer == nullptr) return fail(SA_ERR_SHAPE, "idx (null)", 1, 0);
@@ -336,11 +343,20 @@ sa_status sa_forward(const sa_index* idx, const float* q, int64_t q_len, const f
   const int64_t num_pages = k_len / page_stride;
   if (idx->num_pages < 0 || num_pages < idx->num_pages)
     return fail(SA_ERR_SHAPE, "k_pages / v_pages pages", idx->num_pages, num_pages);
+  if (kv16) {
+    if (kv_format != SA_KV_BF16 && kv_format != SA_KV_F16)
+      return fail(SA_ERR_UNSUPPORTED, "kv_format", SA_KV_BF16, kv_format);
+    if (!sa::small_kernel_fits(head_dim, block_size, page_size, hq / hkv) ||
+        idx->mfma_min_rows != INT32_MAX)
+      return fail(SA_ERR_UNSUPPORTED, "16-bit K/V: head_dim 128, block <= 64, qhead <= 16",
+                  head_dim, block_size);
+  }
   if (!check_device()) return fail(SA_ERR_GPU_INIT, "no HIP device");
   sa::FwdArgs a{};
   a.q = q;
-  a.k = k_pages;
-  a.v = v_pages;
+  a.k = static_cast<const float*>(k_pages);
+  a.v = static_cast<const float*>(v_pages);
+  a.kv_format = kv_format;
   a.block_tables = block_tables;
   a.cu = cu_seqlens_q;
   a.used = used_kv_lens;
@@ -365,6 +381,34 @@ sa_status sa_forward(const sa_index* idx, const float* q, int64_t q_len, const f
   hipError_t e = sa::launch_forward(idx, a, stream);
   if (e != hipSuccess) return runtime_error(e, "forward launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_forward(const sa_index* idx, const float* q, int64_t q_len, const float* k_pages,
+                     int64_t k_len, const float* v_pages, int64_t v_len,
+                     const int32_t* block_tables,
+                     const int64_t* cu_seqlens_q, const int32_t* used_kv_lens, int32_t hq,
+                     int32_t hkv, int32_t head_dim, int32_t block_size, int32_t page_size,
+                     float softmax_scale, int32_t causal, float* o_partial, float* m_partial,
+                     float* l_partial, hipStream_t stream) {
+  return forward_common(idx, q, q_len, k_pages, k_len, v_pages, v_len, block_tables, cu_seqlens_q,
+                        used_kv_lens, hq, hkv, head_dim, block_size, page_size, softmax_scale,
+                        causal, false, SA_KV_F32, o_partial, m_partial, l_partial, stream);
+}
+
+sa_status sa_forward_kv16(const sa_index* idx, const float* q, int64_t q_len,
+                          const uint16_t* k_pages, int64_t k_len, const uint16_t* v_pages,
+                          int64_t v_len, int32_t kv_format, const int32_t* block_tables,
+                          const int64_t* cu_seqlens_q, const int32_t* used_kv_lens, int32_t hq,
+                          int32_t hkv, int32_t head_dim, int32_t block_size, int32_t page_size,
+                          float softmax_scale, int32_t causal, float* o_partial,
+                          float* m_partial, float* l_partial, hipStream_t stream) {
+  return forward_common(idx, q, q_len, k_pages, k_len, v_pages, v_len, block_tables, cu_seqlens_q,
+                        used_kv_lens, hq, hkv, head_dim, block_size, page_size, softmax_scale,
+                        causal, true, kv_format, o_partial, m_partial, l_partial, stream);
 }
 
 sa_status sa_combine(const sa_index* idx, const float* o_partial, const float* m_partial,

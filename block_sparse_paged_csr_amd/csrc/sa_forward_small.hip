@@ -64,12 +64,44 @@ struct WaveLds {
   int32_t qi[kMetaRing][kRows];     // query id of each row
 };
 
-// One piece of a unit in registers: 8 float4 a lane.
+// K/V storage formats: fp32 as the pages define them, or 16-bit storage
+// (bf16 / IEEE fp16) converted exactly to fp32 where it is used.
+enum KvFormat : int { kKvF32 = SA_KV_F32, kKvBf16 = SA_KV_BF16, kKvF16 = SA_KV_F16 };
+
+typedef const __attribute__((address_space(1))) uint16_t gu16;
+typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) uintx2 guint2;
+
+// One piece of a unit in registers: 8 groups of 4 elements a lane.
 //   K piece c: x[t] = K[key 16c + li][16t + 4g .. +3]
 //   V piece c: x[2r + h] = V[key 16c + 4g + r][4li + 64h .. +3]
-struct Piece {
+// fp32 keeps a float4 per group, 16-bit formats the raw 8 bytes (elements
+// 0, 1 in .x, 2, 3 in .y, low half first).
+template <int KVF>
+struct PieceT {
   floatx4 x[8];
 };
+template <>
+struct PieceT<kKvBf16> {
+  uintx2 x[8];
+};
+template <>
+struct PieceT<kKvF16> {
+  uintx2 x[8];
+};
+
+// Element c of group i as fp32 (exact for every format).
+template <int KVF>
+__device__ inline float kv_elem(const PieceT<KVF>& pc, int i, int c) {
+  if constexpr (KVF == kKvF32) {
+    return pc.x[i][c];
+  } else {
+    const uint32_t w = c < 2 ? pc.x[i].x : pc.x[i].y;
+    const uint32_t h = (c & 1) ? (w >> 16) : (w & 0xffffu);
+    if constexpr (KVF == kKvBf16) return __uint_as_float(h << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  }
+}
 
 template <int N>
 using IC = std::integral_constant<int, N>;
@@ -106,8 +138,9 @@ __device__ inline gint* page_id_ptr(const FwdArgs& A, const Unit& U, int t) {
 }
 
 // NCH = pieces per block side (ceil(block_size / 16)); a unit takes 2 NCH steps.
-template <int NCH>
+template <int NCH, int KVF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_small(IndexPtrs P, FwdArgs A) {
+  using Piece = PieceT<KVF>;
   __shared__ WaveLds s_wave[kWaves];
 
   const DevHeader* hdr = P.hdr;
@@ -153,19 +186,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // Issue piece pk (K pieces 0..NCH-1, then V pieces) of the unit in meta slot ms.
   auto load_piece = [&](auto pkc, int ms, bool live, Piece& pc) __attribute__((always_inline)) {
     constexpr int pk = decltype(pkc)::value;
-    if constexpr (pk < NCH) {
-      const int64_t kb = S.ko[ms][kPiece * pk + li];
-      gfloat* kp = (live && kb >= 0 ? (gfloat*)(A.k + kb) : zero_line()) + 4 * g;
+    if constexpr (KVF == kKvF32) {
+      if constexpr (pk < NCH) {
+        const int64_t kb = S.ko[ms][kPiece * pk + li];
+        gfloat* kp = (live && kb >= 0 ? (gfloat*)(A.k + kb) : zero_line()) + 4 * g;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) pc.x[t] = *(gfloatx4*)(kp + 16 * t);
+        for (int t = 0; t < 8; ++t) pc.x[t] = *(gfloatx4*)(kp + 16 * t);
+      } else {
+        constexpr int c = pk - NCH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t kb = S.ko[ms][kPiece * c + 4 * g + r];
+          gfloat* vp = (live && kb >= 0 ? (gfloat*)(A.v + kb) : zero_line()) + 4 * li;
+          pc.x[2 * r] = *(gfloatx4*)vp;
+          pc.x[2 * r + 1] = *(gfloatx4*)(vp + 64);
+        }
+      }
     } else {
-      constexpr int c = pk - NCH;
+      // 16-bit storage: the same element offsets, half the bytes
+      gu16* kbase = (gu16*)A.k;
+      gu16* vbase = (gu16*)A.v;
+      gu16* zero = (gu16*)zero_line();
+      if constexpr (pk < NCH) {
+        const int64_t kb = S.ko[ms][kPiece * pk + li];
+        gu16* kp = (live && kb >= 0 ? kbase + kb : zero) + 4 * g;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t kb = S.ko[ms][kPiece * c + 4 * g + r];
-        gfloat* vp = (live && kb >= 0 ? (gfloat*)(A.v + kb) : zero_line()) + 4 * li;
-        pc.x[2 * r] = *(gfloatx4*)vp;
-        pc.x[2 * r + 1] = *(gfloatx4*)(vp + 64);
+        for (int t = 0; t < 8; ++t) pc.x[t] = *(guint2*)(kp + 16 * t);
+      } else {
+        constexpr int c = pk - NCH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t kb = S.ko[ms][kPiece * c + 4 * g + r];
+          gu16* vp = (live && kb >= 0 ? vbase + kb : zero) + 4 * li;
+          pc.x[2 * r] = *(guint2*)vp;
+          pc.x[2 * r + 1] = *(guint2*)(vp + 64);
+        }
       }
     }
   };
@@ -249,14 +304,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           floatx4 sa0 = zero4(), sa1 = zero4();
 #pragma unroll
           for (int t = 0; t < 8; t += 2) {
-            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].x, qreg[t].x, sa0, 0, 0, 0);
-            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].x, qreg[t + 1].x, sa1, 0, 0, 0);
-            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].y, qreg[t].y, sa0, 0, 0, 0);
-            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].y, qreg[t + 1].y, sa1, 0, 0, 0);
-            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].z, qreg[t].z, sa0, 0, 0, 0);
-            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].z, qreg[t + 1].z, sa1, 0, 0, 0);
-            sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t].w, qreg[t].w, sa0, 0, 0, 0);
-            sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[t + 1].w, qreg[t + 1].w, sa1, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t, c), qreg[t][c], sa0, 0, 0, 0);
+              sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t + 1, c), qreg[t + 1][c], sa1,
+                                                         0, 0, 0);
+            }
           }
           const floatx4 s = sa0 + sa1;    // lane (li, g), reg r: key 16k + 4g + r, row li
 #pragma unroll
@@ -296,8 +349,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
               const floatx4 acc = (c == 0 && r == 0) ? zero4() : oacc[db];
-              oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.x[2 * r + (db >> 2)][db & 3], sreg[c][r],
-                                                              acc, 0, 0, 0);
+              oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, 2 * r + (db >> 2), db & 3),
+                                                              sreg[c][r], acc, 0, 0, 0);
             }
           }
         }
@@ -334,12 +387,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int32_t i = n_units; i < n_bar; ++i) __builtin_amdgcn_s_barrier();
 }
 
-template <int NCH>
+template <int NCH, int KVF>
 hipError_t launch_nch(const sa_index* idx, const FwdArgs& a, hipStream_t s, unsigned max_units) {
   static thread_local int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_small<NCH>, kThreads, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_small<NCH, KVF>, kThreads, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
@@ -348,7 +401,7 @@ hipError_t launch_nch(const sa_index* idx, const FwdArgs& a, hipStream_t s, unsi
   const unsigned need = (max_units + kWaves - 1) / kWaves;
   if (grid > need) grid = need;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_fwd_small<NCH>, dim3(grid), dim3(kThreads), 0, s, index_ptrs(idx), a);
+  hipLaunchKernelGGL((k_fwd_small<NCH, KVF>), dim3(grid), dim3(kThreads), 0, s, index_ptrs(idx), a);
   return hipGetLastError();
 }
 
@@ -363,11 +416,29 @@ int small_kernel_rows() { return kRows; }
 
 hipError_t launch_forward_small(const sa_index* idx, const FwdArgs& a, hipStream_t s,
                                 unsigned max_units) {
-  switch ((a.block_size + kPiece - 1) / kPiece) {
-    case 1: return launch_nch<1>(idx, a, s, max_units);
-    case 2: return launch_nch<2>(idx, a, s, max_units);
-    case 3: return launch_nch<3>(idx, a, s, max_units);
-    default: return launch_nch<4>(idx, a, s, max_units);
+  const int nch = (a.block_size + kPiece - 1) / kPiece;
+  switch (a.kv_format) {
+    case kKvBf16:
+      switch (nch) {
+        case 1: return launch_nch<1, kKvBf16>(idx, a, s, max_units);
+        case 2: return launch_nch<2, kKvBf16>(idx, a, s, max_units);
+        case 3: return launch_nch<3, kKvBf16>(idx, a, s, max_units);
+        default: return launch_nch<4, kKvBf16>(idx, a, s, max_units);
+      }
+    case kKvF16:
+      switch (nch) {
+        case 1: return launch_nch<1, kKvF16>(idx, a, s, max_units);
+        case 2: return launch_nch<2, kKvF16>(idx, a, s, max_units);
+        case 3: return launch_nch<3, kKvF16>(idx, a, s, max_units);
+        default: return launch_nch<4, kKvF16>(idx, a, s, max_units);
+      }
+    default:
+      switch (nch) {
+        case 1: return launch_nch<1, kKvF32>(idx, a, s, max_units);
+        case 2: return launch_nch<2, kKvF32>(idx, a, s, max_units);
+        case 3: return launch_nch<3, kKvF32>(idx, a, s, max_units);
+        default: return launch_nch<4, kKvF32>(idx, a, s, max_units);
+      }
   }
 }
 

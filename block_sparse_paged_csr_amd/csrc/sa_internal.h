@@ -166,6 +166,7 @@ struct FwdArgs {
   float scale_log2;          // softmax_scale * log2(e)
   uint64_t ps_magic;         // ceil(2^40 / page_size): n / page_size == (n * ps_magic) >> 40
                              // for n * page_size < 2^40
+  int32_t kv_format;         // SA_KV_F32, SA_KV_BF16 or SA_KV_F16 (k, v then point at 16-bit words)
 };
 
 struct CombineArgs {

@@ -191,6 +191,36 @@ sa_status sa_forward(const sa_index* idx,
                      float* o_partial, float* m_partial, float* l_partial,
                      hipStream_t stream);
 
+/* Storage formats of K/V pages for sa_forward_kv16. The pages define fp32
+ * pages only; 16-bit storage is converted exactly to fp32 where it is used,
+ * so the arithmetic and its tolerance are the fp32 path's on the stored
+ * values. */
+typedef enum sa_kv_format {
+  SA_KV_F32 = 0,   /* float32 (sa_forward) */
+  SA_KV_BF16 = 1,  /* bfloat16: the top 16 bits of an IEEE binary32 */
+  SA_KV_F16 = 2    /* IEEE binary16 */
+} sa_kv_format;
+
+/* sa_forward_kv16: sa_forward with K/V pages stored as 16-bit words
+ * (`kv_format` SA_KV_BF16 or SA_KV_F16; k_len / v_len count elements, as in
+ * sa_forward). Every other argument, the partials written and the host
+ * checks (in sa_forward's order) are sa_forward's. Then: SA_ERR_UNSUPPORTED
+ * "kv_format" for another format, and SA_ERR_UNSUPPORTED for a geometry
+ * outside the one-wave kernel (head_dim 128, block_size <= 64, qhead <= 16),
+ * the only kernel built for 16-bit pages. */
+sa_status sa_forward_kv16(const sa_index* idx,
+                          const float* q, int64_t q_len,
+                          const uint16_t* k_pages, int64_t k_len,
+                          const uint16_t* v_pages, int64_t v_len,
+                          int32_t kv_format,
+                          const int32_t* block_tables, const int64_t* cu_seqlens_q,
+                          const int32_t* used_kv_lens,
+                          int32_t hq, int32_t hkv, int32_t head_dim,
+                          int32_t block_size, int32_t page_size,
+                          float softmax_scale, int32_t causal,
+                          float* o_partial, float* m_partial, float* l_partial,
+                          hipStream_t stream);
+
 /* sa_combine: log-sum-exp merge of the partials (the combine pass that
  * forward.rs's module doc describes as the FlashAttention update). For every
  * (q, hq = h*qhead + qh), over ranks r with inv[h,q,r] >= 0 at partial row

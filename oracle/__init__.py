@@ -22,6 +22,9 @@ What it computes, and the passages it follows (alice-llm 2.0.0,
   and its "standard FlashAttention log-sum-exp update" are on the pages.
 * ``dense_ref.dense_masked_ref``: brute-force masked dense attention over
   every logical position. It has no union gather and serves as a pin.
+* ``kv16_ref.decode_kv16``: the float32 value of a K/V page word stored as
+  bfloat16 or IEEE binary16 (not on the pages, which store fp32; attention
+  on such pages is the fp32 oracle on the decoded values).
 
 Pins live in ``tests/test_oracle_*.py`` (``-m "not gpu"``). No function here
 is "parity unpinned".
@@ -31,6 +34,7 @@ from .index_ref import build_index_ref, validate_build_inputs, batch_of, resolve
 from .attention_ref import attention_qo_ref
 from .kvouter_ref import forward_partials_ref, combine_ref
 from .dense_ref import dense_masked_ref
+from .kv16_ref import decode_bf16, decode_fp16, decode_kv16
 
 __all__ = [
     "SparseAttentionError",

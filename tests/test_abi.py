@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     # and the binding wraps the compute entry points under the same names
     for name in ("sa_index_plan", "sa_build_index", "sa_index_status", "sa_forward",
-                 "sa_combine", "sa_attention", "sa_attention_workspace_bytes"):
+                 "sa_forward_kv16", "sa_combine", "sa_attention", "sa_attention_workspace_bytes"):
         assert callable(getattr(sa, name))
 
 
@@ -150,3 +150,46 @@ def test_missing_gpu_tensors_fail_loudly():
     t = torch.zeros(4)
     with pytest.raises(ValueError):
         sa._ptr(t, torch.float32, "q")
+
+
+def _kv16_call(idx, d, bs, ps, hq, hkv, fmt):
+    lib = sa.lib()
+    n = 4 * hkv * ps * d
+    return lib.sa_forward_kv16(ctypes.byref(idx.c), ctypes.c_void_p(16), idx.c.tq * hq * d,
+                               ctypes.c_void_p(16), n, ctypes.c_void_p(16), n, fmt,
+                               ctypes.c_void_p(16), ctypes.c_void_p(16), None, hq, hkv, d, bs,
+                               ps, 0.1, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                               ctypes.c_void_p(16), None)
+
+
+@pytest.mark.parametrize("fmt,d,bs,qhead,what", [
+    (3, 128, 64, 4, "kv_format"),                  # no such format
+    (0, 128, 64, 4, "kv_format"),                  # fp32 goes through sa_forward
+    (sa.SA_KV_BF16, 64, 64, 4, "16-bit K/V"),      # head_dim outside the one-wave kernel
+    (sa.SA_KV_F16, 128, 128, 4, "16-bit K/V"),     # block of 128 keys
+    (sa.SA_KV_BF16, 128, 64, 32, "16-bit K/V"),    # 32 query heads per KV head
+])
+def test_kv16_host_checks(fmt, d, bs, qhead, what):
+    # host checks return before any device access: a placeholder buffer suffices
+    hkv, ps = 2, 16
+    idx = sa.sa_index_plan(4, hkv, 2, 1, 16, bs, ps, hkv * qhead, d, 4)
+    idx.c.buffer = 4096
+    st = _kv16_call(idx, d, bs, ps, hkv * qhead, hkv, fmt)
+    det = sa.SaErrorDetail()
+    sa.lib().sa_last_error(ctypes.byref(det))
+    assert sa.STATUS_NAMES[st] == "Unsupported"
+    assert det.what.decode().startswith(what)
+
+
+def test_kv16_shape_checks_come_first():
+    # a wrong q length is reported before the format / geometry checks
+    hkv, ps, d, bs, qhead = 2, 16, 128, 64, 4
+    idx = sa.sa_index_plan(4, hkv, 2, 1, 16, bs, ps, hkv * qhead, d, 4)
+    idx.c.buffer = 4096
+    lib = sa.lib()
+    n = 4 * hkv * ps * d
+    st = lib.sa_forward_kv16(ctypes.byref(idx.c), ctypes.c_void_p(16), 5, ctypes.c_void_p(16), n,
+                             ctypes.c_void_p(16), n, 3, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                             None, hkv * qhead, hkv, d, bs, ps, 0.1, 1, ctypes.c_void_p(16),
+                             ctypes.c_void_p(16), ctypes.c_void_p(16), None)
+    assert sa.STATUS_NAMES[st] == "ShapeMismatch"

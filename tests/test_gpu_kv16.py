@@ -1,0 +1,133 @@
+"""GPU parity of the forward on K/V pages stored as 16-bit words
+(``sa_forward_kv16``, bfloat16 and IEEE fp16).
+
+The words come from ``workloads.encode_kv16`` (round to nearest even). The
+oracle decodes them itself (``oracle.decode_kv16``) and runs the fp32-input
+query-outer attention on the decoded values, in float64. The kernel converts
+each word exactly to fp32, so the bound is the fp32 path's:
+``max|O_gpu - O_ref| <= 1e-4 * max|O_ref|`` and lse to 1e-4. On the same
+index, the 16-bit forward and the fp32 forward on the decoded values give
+bitwise identical partials (same arithmetic on the same fp32 operands).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_paged_csr_amd as sa
+import oracle
+import workloads as W
+from _gpu import dev_inputs, max_rel_err, run_index
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 1e-4
+TOL_LSE = 1e-4
+TORCH16 = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def _pages16(w, fmt, device="cuda"):
+    k = W.encode_kv16(w.k_pages, fmt)
+    v = W.encode_kv16(w.v_pages, fmt)
+    kt = torch.from_numpy(k.view(np.int16)).to(device).view(TORCH16[fmt])
+    vt = torch.from_numpy(v.view(np.int16)).to(device).view(TORCH16[fmt])
+    return k, v, kt, vt
+
+
+def _fwd_args(w, d):
+    return (d["bt"], d["cu"], d["used"], w.hq, w.hkv, w.head_dim, w.block_size, w.page_size,
+            w.softmax_scale, w.causal)
+
+
+def _check(w, kdec, vdec, out, lse, queries=None):
+    ref_o, ref_lse = oracle.attention_qo_ref(
+        w.q, kdec, vdec, w.selected, w.block_tables, w.cu_seqlens_q, w.used_kv_lens, w.hq,
+        w.hkv, w.head_dim, w.block_size, w.page_size, w.softmax_scale, w.causal,
+        queries=queries)
+    got_o = out.cpu().numpy().astype(np.float64)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    if queries is not None:
+        got_o, got_lse = got_o[queries], got_lse[queries]
+    err, _ = max_rel_err(got_o, ref_o)
+    assert err <= TOL_O, err
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(got_lse))
+    if fin.any():
+        assert np.abs(got_lse[fin] - ref_lse[fin]).max() <= TOL_LSE
+    return err
+
+
+GEOM = [(4, 1), (2, 8), (8, 2), (16, 1), (4, 6), (8, 4), (16, 3), (16, 4)]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+@pytest.mark.parametrize("seed", range(8))
+def test_random_kv16_matches_oracle(fmt, seed):
+    ps, ppb = GEOM[seed % len(GEOM)]
+    w = W.make_random(4100 + seed, batch=1 + seed % 4, qo_max=6, kv_max=260, hkv=1 + seed % 3,
+                      qhead=[1, 2, 4, 8, 16][seed % 5], head_dim=128, page_size=ps,
+                      pages_per_block=ppb, topk=1 + seed % 6)
+    print(f"[gpu case] kv16 {fmt} seed={seed} tq={w.tq} bs={w.block_size}", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, fmt)
+    idx = run_index(w, d)
+    o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    _check(w, oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt), out, lse)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+@pytest.mark.parametrize("seed", range(3))
+def test_kv16_partials_equal_fp32_path_on_decoded_pages(fmt, seed):
+    w = W.make_random(4200 + seed, batch=2, qo_max=40, kv_max=300, hkv=2, qhead=4,
+                      head_dim=128, page_size=16, pages_per_block=4, topk=6)
+    print(f"[gpu case] kv16 bitwise {fmt} seed={seed}", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, fmt)
+    idx = run_index(w, d)
+    o16, m16, l16 = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    kd = torch.from_numpy(oracle.decode_kv16(k, fmt)).cuda()
+    vd = torch.from_numpy(oracle.decode_kv16(v, fmt)).cuda()
+    o32, m32, l32 = sa.sa_forward(idx, d["q"], kd, vd, *_fwd_args(w, d))
+    rows = sa.sa_index_status(idx)["total_edges"] * (w.hq // w.hkv)
+    assert torch.equal(o16[:rows], o32[:rows])
+    assert torch.equal(m16[:rows], m32[:rows])
+    assert torch.equal(l16[:rows], l32[:rows])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+def test_decode_workload_kv16(fmt):
+    w = W.make_config("decode")
+    print(f"[gpu case] kv16 decode {fmt}", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, fmt)
+    idx = run_index(w, d)
+    o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    torch.cuda.synchronize()
+    err = _check(w, oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt), out, lse)
+    print(f"[gpu case] kv16 decode {fmt}: O rel err {err:.3e}", flush=True)
+
+
+def test_ragged_workload_bf16_sampled():
+    w = W.make_config("ragged")
+    print("[gpu case] kv16 ragged bf16", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, "bf16")
+    idx = run_index(w, d)
+    o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    queries = np.sort(rng.choice(w.tq, size=24, replace=False))
+    _check(w, oracle.decode_kv16(k, "bf16"), oracle.decode_kv16(v, "bf16"), out, lse, queries)
+
+
+def test_kv16_rejects_other_geometry():
+    w = W.make_random(4300, batch=1, qo_max=3, kv_max=80, hkv=1, qhead=2, head_dim=64,
+                      page_size=16, pages_per_block=2, topk=2)
+    d = dev_inputs(w)
+    _, _, kt, vt = _pages16(w, "bf16")
+    idx = run_index(w, d)
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    assert ei.value.status == 10

@@ -268,6 +268,21 @@ def make_config(name: str, seed: Optional[int] = None, with_kv: bool = True) -> 
     return _MAKERS[name](seed, with_kv)
 
 
+def encode_kv16(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Store float32 K/V values as 16-bit words (uint16), rounding to nearest
+    even: ``fmt`` "bf16" keeps the top half of the binary32 pattern, "fp16"
+    is IEEE binary16. Input generation only: the oracle decodes the words
+    itself."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if fmt == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    if fmt != "bf16":
+        raise ValueError(f"unknown 16-bit format {fmt!r}")
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16          # finite inputs (N(0,1) draws)
+    return rounded.astype(np.uint16)
+
+
 def make_random(seed: int, *, batch=2, qo_max=4, kv_max=24, hkv=1, qhead=2,
                 head_dim=8, page_size=2, pages_per_block=2, topk=3,
                 pad_prob=0.25, hole_prob=0.1, causal=None, with_used=None,
