@@ -57,6 +57,16 @@ __device__ inline int4 wave_incl_scan4(int4 v) {
   return v;
 }
 
+__device__ inline int wave_incl_scan1(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
 // Units of a slot with c edges. A slot with at least thr_e edges (rows >=
 // the MFMA minimum) becomes ceil(c / cap) MFMA units; a smaller one becomes
 // ceil(c / wave_cap) wavefront units. Part i of k spans
@@ -327,6 +337,9 @@ __device__ void finalize_header(const IndexPtrs& P, const BuildArgs& A) {
 
 constexpr int kRankChunk = 2048;   // keys staged in LDS per pass
 constexpr int kRankKeys = 4;       // keys held per thread per pass
+constexpr int kRankBitmapMaxWords = 4096;   // 16 KB (key spaces of up to 131072 keys): a
+                                            // larger bitmap costs the small slots occupancy
+constexpr int kRankBitmapMinKeys = 384;     // smaller slots: pairwise counting is cheaper
 
 __device__ inline void write_edge(const IndexPtrs& P, const BuildArgs& A, int32_t h,
                                   int64_t head_base, int32_t off0, int32_t key, int32_t rank) {
@@ -349,9 +362,12 @@ struct SlotInfo {
 __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
   if (blockIdx.x == 0 && threadIdx.x == 0) finalize_header(P, A);
   if (A.nbs == 0) return;                          // no slots at all (msb == 0)
+  extern __shared__ uint32_t s_bits[];              // [rank_bitmap_words] (dynamic)
   __shared__ SlotInfo s_slot[4];
   __shared__ __align__(16) int32_t s_keys[kRankChunk];
   __shared__ int64_t s_total;
+  __shared__ int s_wsum[4];
+  __shared__ int s_runpre[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (tid == 0) {
     int64_t t = 0;
@@ -425,6 +441,43 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
         const int32_t n = s_slot[s].n;
         if (n == 0) continue;
         const int32_t* seg = P.keys + s_slot[s].base + s_slot[s].off0;
+        if (A.rank_bitmap_words > 0 && n >= kRankBitmapMinKeys) {
+          // The slot's keys as bits of a bitmap over the key space; a key's
+          // rank is the number of set bits before it: a prefix count per
+          // thread's run of words, then within the run.
+          const int32_t W = A.rank_bitmap_words;
+          const int32_t C = (W + 255) / 256;                 // words per thread
+          for (int32_t x = tid; x < W; x += 256) s_bits[x] = 0u;
+          __syncthreads();
+          for (int32_t i = tid; i < n; i += 256) {
+            const int32_t key = seg[i];
+            atomicOr(&s_bits[key >> 5], 1u << (key & 31));
+          }
+          __syncthreads();
+          int cntw = 0;
+          for (int32_t x = 0; x < C; ++x) {
+            const int32_t wd = tid * C + x;
+            cntw += wd < W ? __popc(s_bits[wd]) : 0;
+          }
+          const int incl = wave_incl_scan1(cntw);
+          if (lane == 63) s_wsum[w] = incl;
+          __syncthreads();
+          int pre = incl - cntw;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pre += i < w ? s_wsum[i] : 0;
+          s_runpre[tid] = pre;
+          __syncthreads();
+          for (int32_t i = tid; i < n; i += 256) {
+            const int32_t key = seg[i];
+            const int32_t wd = key >> 5, run = wd / C;
+            int32_t rank = s_runpre[run];
+            for (int32_t x = run * C; x < wd; ++x) rank += __popc(s_bits[x]);
+            rank += __popc(s_bits[wd] & ((1u << (key & 31)) - 1u));
+            write_edge(P, A, s_slot[s].h, s_slot[s].base, s_slot[s].off0, key, rank);
+          }
+          __syncthreads();                           // the bitmap is reused
+          continue;
+        }
         for (int32_t pass = 0; pass < n; pass += 256 * kRankKeys) {
           int32_t mine[kRankKeys], rank[kRankKeys];
 #pragma unroll
@@ -935,10 +988,15 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
   hipLaunchKernelGGL(k_index_scan, dim3((unsigned)(a.hkv * scan_chunks(a.nbs))), dim3(kScanThreads),
                      0, s, P, a);
   hipLaunchKernelGGL(k_index_scatter, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
-  // persistent: a few workgroups per CU loop over the nonempty slots
+  // persistent: a few workgroups per CU loop over the nonempty slots; large
+  // slots rank through an LDS bitmap over the tq*topk key space when it fits
+  BuildArgs ra = a;
+  const int64_t words = (a.tq * a.topk + 31) / 32;
+  ra.rank_bitmap_words = words <= kRankBitmapMaxWords ? (int32_t)words : 0;
   unsigned rank_grid = grid_for(slots, 4);
   if (rank_grid > 8 * cu_count()) rank_grid = 8 * cu_count();
-  hipLaunchKernelGGL(k_index_rank, dim3(rank_grid), dim3(256), 0, s, P, a);
+  hipLaunchKernelGGL(k_index_rank, dim3(rank_grid), dim3(256), (size_t)ra.rank_bitmap_words * 4, s,
+                     P, ra);
   return hipGetLastError();
 }
 
