@@ -57,11 +57,14 @@ constexpr float kLn2 = 0.69314718055994530942f;
 __device__ const float g_zero[kD] = {};
 __device__ inline gfloat* zero_line() { return (gfloat*)g_zero; }
 
+constexpr int kStageStride = kD + 4;  // padded row of the output staging tile
+
 struct WaveLds {
   int32_t rec[kRecRing][8];         // Unit records
   int64_t ko[kMetaRing][kMaxKeys];  // element offset of each key's K/V row, or -1
   uint64_t vm[kMetaRing];           // bit t: key t of the block is inside it and on a page
   int32_t qi[kMetaRing][kRows];     // query id of each row
+  float ostage[kRows][kStageStride];  // the unit's o tile on its way out
 };
 
 // K/V storage formats: fp32 as the pages define them, or 16-bit storage
@@ -362,21 +365,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         if constexpr (k == 2 * NCH - 1) {
           // ---- the unit's partials: lane (li, g) holds row li,
-          // d = 16g + 4v + (db & 3) + 64 (db >> 2) in oacc[db][v]
+          // d = 16g + 4v + (db & 3) + 64 (db >> 2) in oacc[db][v]. The tile
+          // goes through this wave's LDS so that every store instruction
+          // writes 64 lanes x 16 B of contiguous rows (the unit's rows are
+          // consecutive in the partial arrays); stored straight from the
+          // accumulators, each instruction would write 16-B pieces 64 B apart.
           if (row_ok) {
-            const int64_t row = (int64_t)U.e0 * qhead + li;
-            float* dst = A.o + row * kD + 16 * g;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              *reinterpret_cast<floatx4*>(dst + 4 * v) =
+              *reinterpret_cast<floatx4*>(&S.ostage[li][16 * g + 4 * v]) =
                   floatx4{oacc[0][v], oacc[1][v], oacc[2][v], oacc[3][v]};
-              *reinterpret_cast<floatx4*>(dst + 64 + 4 * v) =
+              *reinterpret_cast<floatx4*>(&S.ostage[li][64 + 16 * g + 4 * v]) =
                   floatx4{oacc[4][v], oacc[5][v], oacc[6][v], oacc[7][v]};
             }
             if (g == 0) {
+              const int64_t row = (int64_t)U.e0 * qhead + li;
               A.m[row] = m_row == -INFINITY ? -INFINITY : m_row * kLn2;
               A.l[row] = l_row;
             }
+          }
+          float* dst0 = A.o + (int64_t)U.e0 * qhead * kD;
+          for (int i = lane; i < rows * (kD / 4); i += 64) {
+            const int r = i >> 5, c = i & 31;
+            *reinterpret_cast<floatx4*>(dst0 + r * kD + 4 * c) =
+                *reinterpret_cast<const floatx4*>(&S.ostage[r][4 * c]);
           }
         }
       }
