@@ -650,6 +650,20 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     v_k[k] = i < items ? A.selected[((int64_t)q * hkv + h) * topk + r] : -1;
   }
 
+  // this thread's sequences (b = tid + kFusedThreads k): cu bounds and used
+  // length, also loaded before the LDS setup (clamped, no load behind a branch)
+  constexpr int kSeqPerThread = (kFusedMaxBatch + kFusedThreads - 1) / kFusedThreads;
+  int64_t c0_k[kSeqPerThread], c1_k[kSeqPerThread];
+  int32_t used_k[kSeqPerThread];
+#pragma unroll
+  for (int k = 0; k < kSeqPerThread; ++k) {
+    const int32_t b = tid + kFusedThreads * k;
+    const int32_t bb = b < batch ? b : 0;
+    c0_k[k] = A.cu[bb];
+    c1_k[k] = A.cu[bb + 1];
+    used_k[k] = A.used != nullptr ? A.used[bb] : 0;
+  }
+
   // ---- per-sequence lk and causal delta; batch of each query; cu checks
   for (int32_t x = tid; x < nslots; x += kFusedThreads) s_cnt[x] = 0;
   for (int32_t q = tid; q < tq; q += kFusedThreads) s_qb[q] = -1;
@@ -661,9 +675,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     s_base_um = 0;
   }
   __syncthreads();
-  for (int32_t b = tid; b < batch; b += kFusedThreads) {
-    const int64_t c0 = A.cu[b], c1 = A.cu[b + 1];
-    const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
+#pragma unroll
+  for (int k = 0; k < kSeqPerThread; ++k) {
+    const int32_t b = tid + kFusedThreads * k;
+    if (b >= batch) break;
+    const int64_t c0 = c0_k[k], c1 = c1_k[k];
+    // kv_len_dev: used length clamped at 0, or the whole block-table row
+    const int64_t lk = A.used == nullptr ? (int64_t)A.msb * A.block_size
+                                         : (used_k[k] > 0 ? (int64_t)used_k[k] : 0);
     const int64_t qo_len = c1 - c0;
     s_lkb[b] = (int32_t)lk;
     s_dlb[b] = (int32_t)((lk >= qo_len ? lk - qo_len : 0) - c0);
@@ -698,13 +717,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   // ---- entries: drop padding and blocks past lk, flag bad ids and pages, count
   int32_t slot_k[kFusedItems], arr_k[kFusedItems];
   int64_t col0_k[kFusedItems];                      // first block-table column of the block
-  int32_t touch_k[kFusedItems];                     // pages of the block its valid range touches
+  int32_t len_k[kFusedItems];                       // keys of the block's valid range
 #pragma unroll
   for (int k = 0; k < kFusedItems; ++k) {
     slot_k[k] = -1;
     arr_k[k] = 0;
     col0_k[k] = 0;
-    touch_k[k] = 0;
+    len_k[k] = 0;
     const int32_t i = tid + kFusedThreads * k;
     if (i >= items) continue;
     const int32_t q = i / topk, r = i - q * topk;
@@ -723,7 +742,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     const int64_t block_end = block_start + A.block_size < lk ? block_start + A.block_size : lk;
     slot_k[k] = b * A.msb + v;
     col0_k[k] = (int64_t)b * A.max_pages + (int64_t)v * A.ppb;
-    touch_k[k] = (int32_t)((block_end - block_start + A.page_size - 1) / A.page_size);
+    len_k[k] = (int32_t)(block_end - block_start);
   }
   if (A.num_pages >= 0) {
     // The pages each kept block's valid range touches must exist (the
@@ -741,7 +760,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
 #pragma unroll
         for (int x = 0; x < kPageBatch; ++x) {
           const int32_t pl = p0 + x;
-          const bool touched = pl < touch_k[k];
+          const bool touched = pl < A.ppb && pl * A.page_size < len_k[k];
           page[k][x] = A.block_tables[touched ? col0_k[k] + pl : 0];
         }
 #pragma unroll
@@ -749,7 +768,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
 #pragma unroll
         for (int x = 0; x < kPageBatch; ++x) {
           const int32_t pl = p0 + x;
-          if (pl < touch_k[k] && page[k][x] >= A.num_pages && col0_k[k] + pl < bad_k[k])
+          const bool touched = pl < A.ppb && pl * A.page_size < len_k[k];
+          if (touched && page[k][x] >= A.num_pages && col0_k[k] + pl < bad_k[k])
             bad_k[k] = col0_k[k] + pl;
         }
     }
