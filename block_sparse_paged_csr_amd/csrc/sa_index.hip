@@ -753,7 +753,9 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     int64_t bad_k[kFusedItems];
 #pragma unroll
     for (int k = 0; k < kFusedItems; ++k) bad_k[k] = INT64_MAX;
-    for (int32_t p0 = 0; p0 < A.ppb; p0 += kPageBatch) {
+    // (an empty block table has no element to clamp to, and then no entry is kept)
+    const int32_t ppb_read = (int64_t)batch * A.max_pages > 0 ? A.ppb : 0;
+    for (int32_t p0 = 0; p0 < ppb_read; p0 += kPageBatch) {
       int32_t page[kFusedItems][kPageBatch];
 #pragma unroll
       for (int k = 0; k < kFusedItems; ++k)

@@ -322,6 +322,32 @@ def test_forward_skips_on_device_error():
     assert torch.all(out == 7.0)                  # nothing written
 
 
+# ------------------------------------------------------------------ empty inputs
+
+@pytest.mark.parametrize("head_dim", [128, 32])
+@pytest.mark.parametrize("table", ["full", "empty", "short"])
+def test_nothing_selected(head_dim, table, build_path):
+    """Every rank padded, with the block table as drawn, with no columns at
+    all (max_pages = 0) and with fewer pages than one block (msb = 0): an
+    empty index, O = 0 and lse = -inf, on the one-wave (d = 128) and the
+    wavefront (d = 32) kernels."""
+    w = W.make_random(5100, batch=2, qo_max=3, kv_max=80, hkv=2, qhead=2, head_dim=head_dim,
+                      page_size=16, pages_per_block=2, topk=3)
+    w.selected[...] = -1
+    if table != "full":
+        cols = 0 if table == "empty" else 1
+        w.block_tables = np.ascontiguousarray(w.block_tables[:, :cols])
+    _print_case("nothing_selected", d=head_dim, table=table, build=build_path)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    info, _ = assert_index_equal(idx, ref)
+    assert info["total_edges"] == 0
+    out, lse = run_attention(w, d)
+    assert torch.all(out == 0.0)
+    assert torch.all(lse == -float("inf"))
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def _sample_queries(w, n, seed=0):
