@@ -343,14 +343,8 @@ sa_status forward_common(const sa_index* idx, const float* q, int64_t q_len, con
   const int64_t num_pages = k_len / page_stride;
   if (idx->num_pages < 0 || num_pages < idx->num_pages)
     return fail(SA_ERR_SHAPE, "k_pages / v_pages pages", idx->num_pages, num_pages);
-  if (kv16) {
-    if (kv_format != SA_KV_BF16 && kv_format != SA_KV_F16)
-      return fail(SA_ERR_UNSUPPORTED, "kv_format", SA_KV_BF16, kv_format);
-    if (!sa::small_kernel_fits(head_dim, block_size, page_size, hq / hkv) ||
-        idx->mfma_min_rows != INT32_MAX)
-      return fail(SA_ERR_UNSUPPORTED, "16-bit K/V: head_dim 128, block <= 64, qhead <= 16",
-                  head_dim, block_size);
-  }
+  if (kv16 && kv_format != SA_KV_BF16 && kv_format != SA_KV_F16)
+    return fail(SA_ERR_UNSUPPORTED, "kv_format", SA_KV_BF16, kv_format);
   if (!check_device()) return fail(SA_ERR_GPU_INIT, "no HIP device");
   sa::FwdArgs a{};
   a.q = q;

@@ -47,7 +47,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kMaxUnitEdges = kCapUnitEdges;
 
 // NKB: 32-key blocks per KV block (block_size <= 32 * NKB); WAVES per workgroup.
-template <int NKB, int WAVES>
+template <int NKB, int WAVES, int KVF>
 __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
   constexpr int kWaves = WAVES;
   constexpr int kThreads = WAVES * 64;
@@ -103,8 +103,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
       for (int i = 0; i < kIters; ++i) {
         const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
         const int64_t off = s_off[key];
-        kv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.k + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        vv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.v + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        kv[i] = off >= 0 ? load_kv4<KVF>(A.k, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vv[i] = off >= 0 ? load_kv4<KVF>(A.v, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int i = 0; i < kIters; ++i) {
@@ -258,7 +258,7 @@ __device__ inline floatx4 zero4v() {
   return z;
 }
 
-template <int NKB>
+template <int NKB, int KVF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_mfma16(IndexPtrs P, FwdArgs A) {
   constexpr int kWaves = 4;
   constexpr int kThreads = 256;
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int i = 0; i < kIters; ++i) {
       const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
       const int64_t off = s_off[sl][key];
-      kv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.k + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      vv[i] = off >= 0 ? *reinterpret_cast<const float4*>(A.v + off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      kv[i] = off >= 0 ? load_kv4<KVF>(A.k, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      vv[i] = off >= 0 ? load_kv4<KVF>(A.v, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
 
@@ -478,31 +478,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 }
 
-template <int NKB>
-hipError_t launch_mfma16_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+template <int NKB, int KVF>
+hipError_t launch_mfma16_kv(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
   static thread_local int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma16<NKB>, 256, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma16<NKB, KVF>, 256, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
-  hipLaunchKernelGGL(k_fwd_mfma16<NKB>, dim3((unsigned)per_cu * cus), dim3(256), 0, s, P, a);
+  hipLaunchKernelGGL((k_fwd_mfma16<NKB, KVF>), dim3((unsigned)per_cu * cus), dim3(256), 0, s, P, a);
+  return hipGetLastError();
+}
+
+template <int NKB>
+hipError_t launch_mfma16_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+  switch (a.kv_format) {
+    case SA_KV_BF16: return launch_mfma16_kv<NKB, SA_KV_BF16>(P, a, s, cus);
+    case SA_KV_F16: return launch_mfma16_kv<NKB, SA_KV_F16>(P, a, s, cus);
+    default: return launch_mfma16_kv<NKB, SA_KV_F32>(P, a, s, cus);
+  }
+}
+
+template <int NKB, int WAVES, int KVF>
+hipError_t launch_mfma_kv(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+  static thread_local int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma<NKB, WAVES, KVF>, WAVES * 64, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  hipLaunchKernelGGL((k_fwd_mfma<NKB, WAVES, KVF>), dim3((unsigned)per_cu * cus), dim3(WAVES * 64), 0, s, P, a);
   return hipGetLastError();
 }
 
 template <int NKB, int WAVES>
 hipError_t launch_mfma_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
-  static thread_local int per_cu = 0;
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma<NKB, WAVES>, WAVES * 64, 0) !=
-            hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
+  switch (a.kv_format) {
+    case SA_KV_BF16: return launch_mfma_kv<NKB, WAVES, SA_KV_BF16>(P, a, s, cus);
+    case SA_KV_F16: return launch_mfma_kv<NKB, WAVES, SA_KV_F16>(P, a, s, cus);
+    default: return launch_mfma_kv<NKB, WAVES, SA_KV_F32>(P, a, s, cus);
   }
-  hipLaunchKernelGGL((k_fwd_mfma<NKB, WAVES>), dim3((unsigned)per_cu * cus), dim3(WAVES * 64), 0, s, P, a);
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -82,7 +82,7 @@ struct Stage {
   bool ok;          // the page list fitted in one entry per thread
 };
 
-template <int D4P>
+template <int D4P, int KVF>
 __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
   using C = WaveCfg<D4P>;
   constexpr int NI = C::NI, TPK = C::TPK, KC = C::KC, KS = C::KS;
@@ -208,11 +208,11 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
           const int64_t base = tb < nkeys ? s_pg[pgl - pg0] : -1;
           const bool valid = base >= 0;
           if (qq == 0) s_kvalid[kq] = valid;
-          const float* kp = A.k + base + (int64_t)(tb - pgl * A.page_size) * D;
+          const int64_t krow = base + (int64_t)(tb - pgl * A.page_size) * D;
 #pragma unroll
           for (int j = 0; j < NI; ++j) {
             const int c = qq + TPK * j;
-            kr[j] = (valid && c < D4) ? ld4(kp + c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            kr[j] = (valid && c < D4) ? load_kv4<KVF>(A.k, krow + c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
           }
         }
 #pragma unroll
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
           const int32_t pgl = (int32_t)div_magic((uint32_t)tb, A.ps_magic);
           const int64_t base = tb < nkeys ? s_pg[pgl - pg0] : -1;
           const int64_t off = base + (int64_t)(tb - pgl * A.page_size) * D + c4 * 4;
-          vr[i] = (base >= 0 && col_ok) ? ld4(A.v + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+          vr[i] = (base >= 0 && col_ok) ? load_kv4<KVF>(A.v, off) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         if (cp == 0) {
           for (int x = tid; x < prow * D4P; x += 256) {
@@ -356,21 +356,30 @@ __global__ __launch_bounds__(256) void k_fwd_wave(IndexPtrs P, FwdArgs A) {
   }
 }
 
-template <int D4P>
-hipError_t launch_wave_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned max_grid) {
+template <int D4P, int KVF>
+hipError_t launch_wave_kv(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned max_grid) {
   // Persistent grid: as many workgroups as fit on the device at once.
   static thread_local int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_wave<D4P>, 256, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_wave<D4P, KVF>, 256, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
   unsigned grid = (unsigned)per_cu * cu_count();
   if (grid > max_grid) grid = max_grid;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_fwd_wave<D4P>, dim3(grid), dim3(256), 0, s, P, a);
+  hipLaunchKernelGGL((k_fwd_wave<D4P, KVF>), dim3(grid), dim3(256), 0, s, P, a);
   return hipGetLastError();
+}
+
+template <int D4P>
+hipError_t launch_wave_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned max_grid) {
+  switch (a.kv_format) {
+    case SA_KV_BF16: return launch_wave_kv<D4P, SA_KV_BF16>(P, a, s, max_grid);
+    case SA_KV_F16: return launch_wave_kv<D4P, SA_KV_F16>(P, a, s, max_grid);
+    default: return launch_wave_kv<D4P, SA_KV_F32>(P, a, s, max_grid);
+  }
 }
 
 }  // namespace

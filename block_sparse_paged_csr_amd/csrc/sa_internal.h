@@ -212,6 +212,25 @@ __host__ __device__ inline uint32_t div_magic(uint32_t n, uint64_t magic) {
 inline uint64_t make_div_magic(uint32_t d) { return ((1ull << 40) + d - 1) / d; }
 
 // ---------------------------------------------------------------- device helpers
+// Four consecutive K/V elements at element offset `off` as fp32: a float4 for
+// fp32 pages; for 16-bit pages (KVF = SA_KV_BF16 / SA_KV_F16, `base` then
+// points at uint16 words) 8 bytes, each word converted exactly.
+template <int KVF>
+__device__ inline float kv16_to_f32(uint32_t w) {
+  if constexpr (KVF == SA_KV_BF16) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+}
+template <int KVF>
+__device__ inline float4 load_kv4(const float* base, int64_t off) {
+  if constexpr (KVF == SA_KV_F32) {
+    return *reinterpret_cast<const float4*>(base + off);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+    return make_float4(kv16_to_f32<KVF>(w.x & 0xffffu), kv16_to_f32<KVF>(w.x >> 16),
+                       kv16_to_f32<KVF>(w.y & 0xffffu), kv16_to_f32<KVF>(w.y >> 16));
+  }
+}
+
 // Last b in [0, batch) with cu[b] <= q (types.rs CuSeqlensQ::batch_of).
 __device__ inline int32_t batch_of_dev(const int64_t* __restrict__ cu, int32_t batch, int64_t q) {
   int32_t lo = 0, hi = batch + 1;      // first index with cu[i] > q lies in [lo, hi]

@@ -204,10 +204,9 @@ typedef enum sa_kv_format {
 /* sa_forward_kv16: sa_forward with K/V pages stored as 16-bit words
  * (`kv_format` SA_KV_BF16 or SA_KV_F16; k_len / v_len count elements, as in
  * sa_forward). Every other argument, the partials written and the host
- * checks (in sa_forward's order) are sa_forward's. Then: SA_ERR_UNSUPPORTED
- * "kv_format" for another format, and SA_ERR_UNSUPPORTED for a geometry
- * outside the one-wave kernel (head_dim 128, block_size <= 64, qhead <= 16),
- * the only kernel built for 16-bit pages. */
+ * checks (in sa_forward's order) are sa_forward's. Then SA_ERR_UNSUPPORTED
+ * "kv_format" for another format. Every geometry that sa_forward takes is
+ * supported: each forward kernel converts the words as it loads them. */
 sa_status sa_forward_kv16(const sa_index* idx,
                           const float* q, int64_t q_len,
                           const uint16_t* k_pages, int64_t k_len,

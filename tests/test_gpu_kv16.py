@@ -1,5 +1,5 @@
 """GPU parity of the forward on K/V pages stored as 16-bit words
-(``sa_forward_kv16``, bfloat16 and IEEE fp16).
+(``sa_forward_kv16``, bfloat16 and IEEE fp16), on every forward kernel.
 
 The words come from ``workloads.encode_kv16`` (round to nearest even). The
 oracle decodes them itself (``oracle.decode_kv16``) and runs the fp32-input
@@ -122,12 +122,49 @@ def test_ragged_workload_bf16_sampled():
     _check(w, oracle.decode_kv16(k, "bf16"), oracle.decode_kv16(v, "bf16"), out, lse, queries)
 
 
-def test_kv16_rejects_other_geometry():
-    w = W.make_random(4300, batch=1, qo_max=3, kv_max=80, hkv=1, qhead=2, head_dim=64,
-                      page_size=16, pages_per_block=2, topk=2)
+# Geometries of the other forward kernels: the wavefront kernel (head_dim
+# other than 128), the 16-row MFMA kernel (blocks <= 64 keys, qhead > 16) and
+# the 32-row MFMA kernel (blocks of 96 / 128 keys).
+OTHER = [
+    dict(head_dim=32, qhead=2, page_size=4, pages_per_block=2, qo_max=6, kv_max=120, topk=4),
+    dict(head_dim=64, qhead=4, page_size=8, pages_per_block=4, qo_max=6, kv_max=300, topk=5),
+    dict(head_dim=128, qhead=20, page_size=16, pages_per_block=4, qo_max=200, kv_max=600, topk=6),
+    dict(head_dim=128, qhead=8, page_size=32, pages_per_block=4, qo_max=200, kv_max=1200, topk=6),
+    dict(head_dim=128, qhead=4, page_size=32, pages_per_block=3, qo_max=150, kv_max=900, topk=5),
+]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+@pytest.mark.parametrize("case", range(len(OTHER)))
+def test_other_kernels_kv16(fmt, case):
+    g = OTHER[case]
+    w = W.make_random(4400 + case, batch=2, hkv=2, **g)
+    print(f"[gpu case] kv16 other {fmt} case={case} tq={w.tq} d={w.head_dim} "
+          f"bs={w.block_size} qhead={w.hq // w.hkv}", flush=True)
     d = dev_inputs(w)
-    _, _, kt, vt = _pages16(w, "bf16")
+    k, v, kt, vt = _pages16(w, fmt)
     idx = run_index(w, d)
-    with pytest.raises(sa.SaError) as ei:
-        sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
-    assert ei.value.status == 10
+    o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    kd, vd = oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt)
+    _check(w, kd, vd, out, lse)
+    # and bitwise the fp32 path's partials on the decoded pages
+    o32, m32, l32 = sa.sa_forward(idx, d["q"], torch.from_numpy(kd).cuda(),
+                                  torch.from_numpy(vd).cuda(), *_fwd_args(w, d))
+    rows = sa.sa_index_status(idx)["total_edges"] * (w.hq // w.hkv)
+    assert torch.equal(o[:rows], o32[:rows]) and torch.equal(m[:rows], m32[:rows])
+    assert torch.equal(l[:rows], l32[:rows])
+
+
+def test_prefill_workload_bf16_sampled():
+    w = W.make_config("prefill")
+    print("[gpu case] kv16 prefill bf16", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, "bf16")
+    idx = run_index(w, d)
+    o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    queries = np.sort(rng.choice(w.tq, size=12, replace=False))
+    _check(w, oracle.decode_kv16(k, "bf16"), oracle.decode_kv16(v, "bf16"), out, lse, queries)
