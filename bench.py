@@ -11,8 +11,11 @@ step before.
 Prints ONE JSON line. ``value`` is kept edges per second of whole steps.
 ``roofline`` is for the forward pass (sa_forward), the dominant part of a
 step. Its average duration is measured with HIP events recorded on the
-stream it is launched on, inside the timed region; its algorithmic bytes and
-flops are counted from the built index. ``cpu_baseline`` is the CPU oracle
+stream it is launched on, right after the timed region: one event pair
+around K back-to-back forward launches over the same rotated batches (an
+event marker between kernels costs the GPU a few microseconds, so none sits
+inside the timed region or between the launches timed); its algorithmic
+bytes and flops are counted from the built index. ``cpu_baseline`` is the CPU oracle
 timed on this host.
 
     python bench.py [--steps K] [--warmup W] [--config decode|tiny|prefill|ragged|skewed]
@@ -218,21 +221,23 @@ def main():
             "lse": torch.empty((w.tq, w.hq), dtype=torch.float32, device=dev),
         })
 
-    def step(s, ev=None):
-        w = s["w"]
-        if ev is not None:
-            ev[0].record()
+    def build(s):
         sa.sa_build_index(s["sel"], s["bt"], s["cu"], s["used"], s["idx"])
-        if ev is not None:
-            ev[1].record()
+
+    def forward(s):
+        w = s["w"]
         fwd = sa.sa_forward_kv16 if kv16 else sa.sa_forward
         fwd(s["idx"], s["q"], k, v, s["bt"], s["cu"], s["used"], w.hq, w.hkv, w.head_dim,
             w.block_size, w.page_size, w.softmax_scale, w.causal, s["o"], s["m"], s["l"])
-        if ev is not None:
-            ev[2].record()
+
+    def combine(s):
+        w = s["w"]
         sa.sa_combine(s["idx"], s["o"], s["m"], s["l"], w.hq, w.head_dim, s["out"], s["lse"])
-        if ev is not None:
-            ev[3].record()
+
+    def step(s):
+        build(s)
+        forward(s)
+        combine(s)
 
     # algorithmic work of each batch, counted from the built index
     work = []
@@ -246,26 +251,48 @@ def main():
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # the timed region: K whole steps, nothing else on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % len(sets)], evs[i])
+        step(sets[i % len(sets)])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for s in sets:                                  # device-side status of the last builds
         sa.sa_index_status(s["idx"])
 
-    build_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    fwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    # per-call durations: one pair of HIP events on the launch stream around
+    # K back-to-back launches of each call over the same rotated batches (a
+    # timing marker between two kernels costs the GPU a few microseconds, so
+    # none sits inside the timed region above or between the launches timed).
+    # A spin kernel ahead of the first event keeps the GPU busy while the host
+    # enqueues all K launches, so the pair times the GPU, not the host's launch
+    # rate; the lead is doubled until the first event is still pending when
+    # the last launch has been enqueued.
+    def phase_ms(fn):
+        lead_us = 40.0 * args.steps
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(lead_us * 2500))      # clock64 ticks, >= 1 per ns here
+            e0.record()
+            for i in range(args.steps):
+                fn(sets[i % len(sets)])
+            queued_ahead = not e0.query()
+            e1.record()
+            torch.cuda.synchronize()
+            if queued_ahead:
+                break
+            lead_us *= 2
+        return e0.elapsed_time(e1) / args.steps, queued_ahead
+
+    (build_ms, ok_b), (fwd_ms, ok_f), (comb_ms, ok_c) = map(phase_ms, (build, forward, combine))
     per = [work[i % len(sets)] for i in range(args.steps)]
     edges = sum(p["edges"] for p in per)
     fwd_bytes = np.mean([p["fwd_bytes"] for p in per])
-    fwd_avg_s = float(np.mean(fwd_ms)) / 1e3
+    fwd_avg_s = fwd_ms / 1e3
     step_s = wall / args.steps
     total_bytes = np.mean([p["total_bytes"] for p in per])
     flops = np.mean([p["flops"] for p in per])
-    fc_s = (float(np.mean(fwd_ms)) + float(np.mean(comb_ms))) / 1e3
+    fc_s = (fwd_ms + comb_ms) / 1e3
     roofline = forward_roofline(base, fwd_bytes, flops, fwd_avg_s, args.kv_dtype)
 
     result = {
@@ -293,8 +320,9 @@ def main():
             "hbm_frac": total_bytes / fc_s / 1e9 / HBM_PEAK_GBPS,
             "mfma_frac_fp32": flops / fc_s / 1e12 / FP32_MFMA_PEAK_TFLOPS,
         },
-        "index_build_us": float(np.mean(build_ms)) * 1e3,
-        "combine_us": float(np.mean(comb_ms)) * 1e3,
+        "index_build_us": build_ms * 1e3,
+        "per_call_gpu_bound": bool(ok_b and ok_f and ok_c),
+        "combine_us": comb_ms * 1e3,
     }
     if args.graph:
         result["graph_step_us"] = graph_step_us(sets, step, args.steps)
