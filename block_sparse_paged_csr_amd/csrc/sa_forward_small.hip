@@ -384,11 +384,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
               A.l[row] = l_row;
             }
           }
+          // non-temporal: the partials are read back only by the combine,
+          // so they need not take L2 lines from the blocks that the
+          // neighbouring units read again (ragged 364 -> 355 us)
           float* dst0 = A.o + (int64_t)U.e0 * qhead * kD;
           for (int i = lane; i < rows * (kD / 4); i += 64) {
             const int r = i >> 5, c = i & 31;
-            *reinterpret_cast<floatx4*>(dst0 + r * kD + 4 * c) =
-                *reinterpret_cast<const floatx4*>(&S.ostage[r][4 * c]);
+            __builtin_nontemporal_store(*reinterpret_cast<const floatx4*>(&S.ostage[r][4 * c]),
+                                        reinterpret_cast<floatx4*>(dst0 + r * kD + 4 * c));
           }
         }
       }
