@@ -15,8 +15,11 @@ stream it is launched on, right after the timed region: one event pair
 around K back-to-back forward launches over the same rotated batches (an
 event marker between kernels costs the GPU a few microseconds, so none sits
 inside the timed region or between the launches timed); its algorithmic
-bytes and flops are counted from the built index. ``cpu_baseline`` is the CPU oracle
-timed on this host.
+bytes and flops are counted from the built index. For the MFMA-bound
+workloads ``roofline.mfma_util`` is the matrix pipes' busy fraction that
+rocprofv3 measured for the same kernel (profiles/<workload>_forward_mfma_util.md),
+null once that kernel's sources have changed. ``cpu_baseline`` is the CPU
+oracle timed on this host.
 
     python bench.py [--steps K] [--warmup W] [--config decode|tiny|prefill|ragged|skewed]
     python bench.py --copy-calibration   # plain copy kernel of known size, for PMC scaling
@@ -365,6 +368,7 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32"):
             "frac": achieved / peak,
             "traffic": measured_traffic(w.name if kv_dtype == "f32" else f"{w.name}_{kv_dtype}",
                                         dominant),
+            "mfma_util": measured_mfma_util(w.name) if bound == "mfma" and kv_dtype == "f32" else None,
             "kernel": f"sa_forward ({kernels})", "alg_bytes_per_launch": int(fwd_bytes),
             "alg_flops_per_launch": int(fwd_flops), "avg_launch_us": fwd_s * 1e6}
 
@@ -392,6 +396,31 @@ def measured_traffic(workload, kernel):
     if h.hexdigest() != rec.get("sources_sha256"):
         return None
     return rec["bytes_per_launch"]
+
+
+def measured_mfma_util(workload):
+    """MFMA utilisation of the MFMA forward kernel from
+    profiles/<workload>_forward_mfma_util.md (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES
+    over GRBM_GUI_ACTIVE x SIMDs), or None when there is no such summary or the
+    kernel's sources have changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_forward_mfma_util.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("MFMA_JSON:"):
+                rec = json.loads(line[len("MFMA_JSON:"):])
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for name in rec.get("sources", []):
+        with open(os.path.join(ROOT, "block_sparse_paged_csr_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return rec["mfma_util"]
 
 
 def graph_step_us(sets, step, steps):
