@@ -183,8 +183,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the design for sharding is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs on one GPU and has no "
+              "multi-GPU path (no sharding, no collectives).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
 // Workgroup (h, c) scans chunk c (kScanChunkSlots slots) of head h: its
 // counts, loaded together, give the local sums; the chunk's offset within
 // the head comes from a decoupled look-back over the chunks before it
-// (chunk aggregates and inclusive sums tagged with this build's epoch).
+// (chunk aggregates and inclusive sums tagged with the build call's epoch).
 // Chunks of a head are dispatched in order, so every chunk waited on is
 // already running or done; a spin limit turns a missing chunk into a
 // runtime error instead of a hang. Outputs per nonempty slot: its compact

@@ -183,7 +183,7 @@ struct CombineArgs {
 IndexPtrs index_ptrs(const sa_index* idx);
 ScratchLayout scratch_layout(const sa_index* idx);
 
-// Whether the MFMA forward kernel is part of this build.
+// Whether the MFMA forward kernel is part of the library.
 bool mfma_enabled();
 // Compute units of the current device (cached per host thread).
 unsigned cu_count();

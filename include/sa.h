@@ -38,7 +38,7 @@ extern "C" {
 #endif
 
 /* Status codes: the SparseAttentionError variants of types.rs, plus the
- * limits of this build. */
+ * limits of this library. */
 typedef enum sa_status {
   SA_OK = 0,
   SA_ERR_HEAD_COUNT = 1,     /* HeadCountMismatch: hq, hkv > 0 and hq % hkv == 0 */
@@ -51,7 +51,7 @@ typedef enum sa_status {
   SA_ERR_EMPTY = 7,          /* EmptyInput: tq == 0 || hkv == 0 || topk == 0 */
   SA_ERR_GPU_INIT = 8,       /* GpuInitFailed: no usable gfx950 device */
   SA_ERR_GPU_RUNTIME = 9,    /* GpuRuntimeError: a HIP call failed */
-  SA_ERR_UNSUPPORTED = 10    /* outside this build's limits (see sa_index_plan) */
+  SA_ERR_UNSUPPORTED = 10    /* outside this library's limits (see sa_index_plan) */
 } sa_status;
 
 /* Host-side detail of the last failed call on this host thread. */
