@@ -145,6 +145,54 @@ def test_random_d128_split_units(seed):
     _check_output(w, out, lse)
 
 
+# Head dims away from 128 take the wavefront-reduction kernel, built for
+# head_dim/4 rounded up to a power of two (1 .. 64 float4 columns): dims
+# that are not a power of two mask the padded columns, and head_dim 256 with
+# 16 GQA lanes is the largest qhead * head_dim the library takes (4096).
+WAVE_DIMS = [(4, 3), (12, 5), (100, 2), (132, 3), (256, 16), (256, 1), (40, 7), (252, 4)]
+
+
+@pytest.mark.parametrize("case", range(len(WAVE_DIMS)))
+def test_random_head_dims_wave_kernel(case):
+    d, qhead = WAVE_DIMS[case]
+    w = W.make_random(7100 + case, batch=1 + case % 3, qo_max=5, kv_max=60, hkv=1 + case % 2,
+                      qhead=qhead, head_dim=d, page_size=[2, 4, 8][case % 3],
+                      pages_per_block=2 + case % 3, topk=2 + case % 4)
+    _print_case("random_head_dims", idx=case, head_dim=d, qhead=qhead, tq=w.tq)
+    d_in = dev_inputs(w)
+    idx = run_index(w, d_in)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    assert info["num_units_mfma"] == 0
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+    out, lse = run_attention(w, d_in)
+    _check_output(w, out, lse)
+
+
+# Blocks of 96 and 128 keys on head_dim 128: slots of 32 rows or more take
+# the MFMA kernel that stages the block in LDS (3 or 4 32-key column blocks),
+# the rest the wavefront-reduction kernel; with page holes, ids past the used
+# length, partial last blocks and either causal mode.
+LARGE_BLOCK_GEOM = [(32, 3), (32, 4), (64, 2), (16, 8), (48, 2), (8, 12)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_large_blocks_mfma(seed):
+    ps, ppb = LARGE_BLOCK_GEOM[seed % len(LARGE_BLOCK_GEOM)]
+    w = W.make_random(7300 + seed, batch=1 + seed % 3, qo_max=40, kv_max=700, hkv=1 + seed % 2,
+                      qhead=[4, 8, 16, 8][seed % 4], head_dim=128, page_size=ps,
+                      pages_per_block=ppb, topk=3 + seed % 4, causal=seed % 2 == 1)
+    _print_case("random_large_blocks", seed=seed, tq=w.tq, bs=w.block_size, qhead=w.hq // w.hkv)
+    d_in = dev_inputs(w)
+    idx = run_index(w, d_in)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    assert info["num_units_mfma"] > 0
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+    out, lse = run_attention(w, d_in)
+    _check_output(w, out, lse)
+
+
 # More than 16 query heads per KV head on head_dim 128 and blocks of at most
 # 64 keys: slots of 32 rows or more take the MFMA kernel for such blocks
 # (16-row tiles staged through LDS), the rest the wavefront-reduction kernel.
