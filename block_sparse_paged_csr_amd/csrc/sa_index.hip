@@ -43,6 +43,17 @@ __device__ inline int4 sub4(int4 a, int4 b) {
   return make_int4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
 }
 
+__device__ inline int4 wave_sum4(int4 v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    v.x += __shfl_xor(v.x, off, 64);
+    v.y += __shfl_xor(v.y, off, 64);
+    v.z += __shfl_xor(v.z, off, 64);
+    v.w += __shfl_xor(v.w, off, 64);
+  }
+  return v;
+}
+
 __device__ inline int4 wave_incl_scan4(int4 v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -211,43 +222,57 @@ __global__ __launch_bounds__(kScanThreads) void k_index_scan(IndexPtrs P, BuildA
     if (i < wid) pre = add4(pre, t);
     agg = add4(agg, t);
   }
-  if (tid == 0) {
+  if (wid == 0) {
+    // Wave-parallel look-back: lane i reads chunk ch-1-i (64 predecessors per
+    // round trip). The chunks up to the nearest one whose inclusive sum is
+    // out contribute (their aggregates, that one its inclusive sum); if none
+    // is, the whole window's aggregates count and the next window follows.
     ChunkAgg* my = P.chunk_agg + (int64_t)h * nch + ch;
     int4 excl = make_int4(0, 0, 0, 0);
     if (ch > 0) {
-      my->agg = agg;
-      __hip_atomic_store(&my->flag, A.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      for (int32_t p = ch - 1; p >= 0; --p) {
-        const ChunkAgg* pa = P.chunk_agg + (int64_t)h * nch + p;
+      if (lane == 0) {
+        my->agg = agg;
+        __hip_atomic_store(&my->flag, A.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      for (int32_t top = ch - 1; top >= 0; top -= 64) {
+        const int32_t p = top - lane;
         uint64_t f = 0;
-        int spins = 0;
-        while (true) {
-          f = __hip_atomic_load(&pa->flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-          if (f == A.epoch || f == A.epoch + 1 || spins >= kLookbackSpins) break;
-          __builtin_amdgcn_s_sleep(1);
-          ++spins;
+        int4 val = make_int4(0, 0, 0, 0);
+        if (p >= 0) {
+          const ChunkAgg* pa = P.chunk_agg + (int64_t)h * nch + p;
+          int spins = 0;
+          while (true) {
+            f = __hip_atomic_load(&pa->flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+            if (f == A.epoch || f == A.epoch + 1 || spins >= kLookbackSpins) break;
+            __builtin_amdgcn_s_sleep(1);
+            ++spins;
+          }
+          if (f == A.epoch + 1) val = pa->incl;
+          else if (f == A.epoch) val = pa->agg;
         }
-        if (f != A.epoch && f != A.epoch + 1) {
-          atomicMin(&P.hdr->err_key, err_key(kRankLookback, 0));
+        const bool bad = p >= 0 && f != A.epoch && f != A.epoch + 1;
+        if (__ballot(bad) != 0) {
+          if (lane == 0) atomicMin(&P.hdr->err_key, err_key(kRankLookback, 0));
           break;
         }
-        if (f == A.epoch + 1) {
-          excl = add4(excl, pa->incl);
-          break;
-        }
-        excl = add4(excl, pa->agg);
+        const uint64_t have_incl = __ballot(p >= 0 && f == A.epoch + 1);
+        const int stop = have_incl != 0 ? __builtin_ctzll(have_incl) : 64;
+        excl = add4(excl, wave_sum4(lane <= stop ? val : make_int4(0, 0, 0, 0)));
+        if (have_incl != 0) break;
       }
     }
-    my->incl = add4(excl, agg);
-    __hip_atomic_store(&my->flag, A.epoch + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    s_excl = excl;
-    if (ch == nch - 1) {
-      const int4 tot = add4(excl, agg);
-      P.num_sel[h] = tot.y;
-      P.head_e[h] = tot.x;
-      P.head_uw[h] = tot.z;
-      P.head_um[h] = tot.w;
-      P.sel_offsets[(int64_t)h * (nbs + 1) + tot.y] = tot.x;
+    if (lane == 0) {
+      my->incl = add4(excl, agg);
+      __hip_atomic_store(&my->flag, A.epoch + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      s_excl = excl;
+      if (ch == nch - 1) {
+        const int4 tot = add4(excl, agg);
+        P.num_sel[h] = tot.y;
+        P.head_e[h] = tot.x;
+        P.head_uw[h] = tot.z;
+        P.head_um[h] = tot.w;
+        P.sel_offsets[(int64_t)h * (nbs + 1) + tot.y] = tot.x;
+      }
     }
   }
   __syncthreads();
