@@ -22,6 +22,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRankTile = 16;
 constexpr int kMaxBlock = 1024;      // qhead * D4 <= 1024: one item per thread
 
+// Partial reads: plain, or non-temporal (NT) where the forward wrote the
+// partials with non-temporal stores (the one-wave kernel). Every partial is
+// read once; streamed that way, ragged's combine takes 47 instead of 52 us,
+// while partials written with plain stores (the MFMA kernels) read faster
+// plainly.
+typedef float floatx4nt __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ inline float ld_f(const float* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ inline float4 ld_f4(const float* p) {
+  if constexpr (NT) {
+    const floatx4nt v = __builtin_nontemporal_load(reinterpret_cast<const floatx4nt*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kMaxBlock) void k_combine(IndexPtrs P, CombineArgs A) {
   const int32_t qhead = A.qhead;
   const int64_t q = blockIdx.x / A.hkv;
@@ -52,10 +74,9 @@ __global__ __launch_bounds__(kMaxBlock) void k_combine(IndexPtrs P, CombineArgs 
     for (int t = 0; t < kRankTile; ++t) {
       const bool ok = row[t] >= 0;
       const int64_t rr = ok ? row[t] : 0;
-      mv[t] = ok ? A.m[rr] : -INFINITY;
-      lv[t] = ok ? A.l[rr] : 0.f;
-      ov[t] = ok ? *reinterpret_cast<const float4*>(A.o + rr * A.head_dim + 4 * c)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      mv[t] = ok ? ld_f<NT>(A.m + rr) : -INFINITY;
+      lv[t] = ok ? ld_f<NT>(A.l + rr) : 0.f;
+      ov[t] = ok ? ld_f4<NT>(A.o + rr * A.head_dim + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float mt = -INFINITY;
 #pragma unroll
@@ -98,7 +119,11 @@ hipError_t launch_combine(const sa_index* idx, const CombineArgs& a, hipStream_t
   const int n_items = a.qhead * (a.head_dim / 4);
   int block = (n_items + 63) / 64 * 64;
   if (block > kMaxBlock) return hipErrorInvalidValue;             // plan rejects this
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)grid), dim3(block), 0, s, P, a);
+  // the one-wave forward (where it fits) writes its partials non-temporally
+  if (small_kernel_fits(a.head_dim, idx->block_size, idx->page_size, a.qhead))
+    hipLaunchKernelGGL(k_combine<true>, dim3((unsigned)grid), dim3(block), 0, s, P, a);
+  else
+    hipLaunchKernelGGL(k_combine<false>, dim3((unsigned)grid), dim3(block), 0, s, P, a);
   return hipGetLastError();
 }
 
