@@ -12,14 +12,15 @@
 // fp32 matrix cores (v_mfma_f32_16x16x4f32) and its block is streamed in
 // pieces of 16 keys: first the K pieces (scores of all keys stay in registers),
 // then the exact softmax over the block, then the V pieces. The contraction
-// index d is permuted so that loads cover whole cache lines:
-//   S^T[key, row] = K[key, :] . Q[row, :]   MFMA t, component c, lane group g = lane/16
-//                                           takes d = 16t + 4g + c: the four lanes of a
-//                                           key read 64 contiguous bytes per load
+// index d is permuted so that each lane reads 8 consecutive elements of a
+// row per pair of register groups (one 16-byte load for 16-bit pages, two
+// for fp32):
+//   S^T[key, row] = K[key, :] . Q[row, :]   register group i, component c, lane group
+//                                           g = lane/16 takes d = 32 (i >> 1) + 8g +
+//                                           4 (i & 1) + c (q loaded the same way)
 //   O^T[d, row] += V[key, d] * P[row, key]  output row i of MFMA block db stands for
-//                                           d = 4i + (db & 3) + 64 (db >> 2): the 16
-//                                           lanes of a key read 256 contiguous bytes
-//
+//                                           d = 8i + db
+// Every d is taken once on both sides, so the sums are those of the method.
 // Latency: the next piece (the next unit's first K piece at the end of a unit)
 // is in flight while a piece computes, and the next unit's query rows load
 // during the V pieces. Unit metadata runs further ahead through small per-wave
@@ -74,10 +75,12 @@ enum KvFormat : int { kKvF32 = SA_KV_F32, kKvBf16 = SA_KV_BF16, kKvF16 = SA_KV_F
 typedef const __attribute__((address_space(1))) uint16_t gu16;
 typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(1))) uintx2 guint2;
+typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) uintx4 guint4;
 
 // One piece of a unit in registers: 8 groups of 4 elements a lane.
-//   K piece c: x[t] = K[key 16c + li][16t + 4g .. +3]
-//   V piece c: x[2r + h] = V[key 16c + 4g + r][4li + 64h .. +3]
+//   K piece c: x[i] = K[key 16c + li][32 (i >> 1) + 8g + 4 (i & 1) .. +3]
+//   V piece c: x[2r + h] = V[key 16c + 4g + r][8li + 4h .. +3]
 // fp32 keeps a float4 per group, 16-bit formats the raw 8 bytes (elements
 // 0, 1 in .x, 2, 3 in .y, low half first).
 template <int KVF>
@@ -192,50 +195,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if constexpr (KVF == kKvF32) {
       if constexpr (pk < NCH) {
         const int64_t kb = S.ko[ms][kPiece * pk + li];
-        gfloat* kp = (live && kb >= 0 ? (gfloat*)(A.k + kb) : zero_line()) + 4 * g;
+        gfloat* kp = (live && kb >= 0 ? (gfloat*)(A.k + kb) : zero_line()) + 8 * g;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) pc.x[t] = *(gfloatx4*)(kp + 16 * t);
+        for (int i = 0; i < 8; ++i) pc.x[i] = *(gfloatx4*)(kp + 32 * (i >> 1) + 4 * (i & 1));
       } else {
         constexpr int c = pk - NCH;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t kb = S.ko[ms][kPiece * c + 4 * g + r];
-          gfloat* vp = (live && kb >= 0 ? (gfloat*)(A.v + kb) : zero_line()) + 4 * li;
+          gfloat* vp = (live && kb >= 0 ? (gfloat*)(A.v + kb) : zero_line()) + 8 * li;
           pc.x[2 * r] = *(gfloatx4*)vp;
-          pc.x[2 * r + 1] = *(gfloatx4*)(vp + 64);
+          pc.x[2 * r + 1] = *(gfloatx4*)(vp + 4);
         }
       }
     } else {
-      // 16-bit storage: the same element offsets, half the bytes
+      // 16-bit storage: the same element offsets, half the bytes: one
+      // 16-byte load per pair of register groups
       gu16* kbase = (gu16*)A.k;
       gu16* vbase = (gu16*)A.v;
       gu16* zero = (gu16*)zero_line();
       if constexpr (pk < NCH) {
         const int64_t kb = S.ko[ms][kPiece * pk + li];
-        gu16* kp = (live && kb >= 0 ? kbase + kb : zero) + 4 * g;
+        gu16* kp = (live && kb >= 0 ? kbase + kb : zero) + 8 * g;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) pc.x[t] = *(guint2*)(kp + 16 * t);
+        for (int t = 0; t < 4; ++t) {
+          const uintx4 w = *(guint4*)(kp + 32 * t);
+          pc.x[2 * t] = uintx2{w.x, w.y};
+          pc.x[2 * t + 1] = uintx2{w.z, w.w};
+        }
       } else {
         constexpr int c = pk - NCH;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t kb = S.ko[ms][kPiece * c + 4 * g + r];
-          gu16* vp = (live && kb >= 0 ? vbase + kb : zero) + 4 * li;
-          pc.x[2 * r] = *(guint2*)vp;
-          pc.x[2 * r + 1] = *(guint2*)(vp + 64);
+          gu16* vp = (live && kb >= 0 ? vbase + kb : zero) + 8 * li;
+          const uintx4 w = *(guint4*)vp;
+          pc.x[2 * r] = uintx2{w.x, w.y};
+          pc.x[2 * r + 1] = uintx2{w.z, w.w};
         }
       }
     }
   };
   // The B operand of the unit in record slot rs / meta slot ms: row li,
-  // d = 16t + 4g .. +3 in q[t]; zero past its rows.
+  // d = 32 (i >> 1) + 8g + 4 (i & 1) .. +3 in q[i]; zero past its rows.
   auto load_q = [&](int rs, int ms, bool live, floatx4 (&q)[8]) __attribute__((always_inline)) {
     const Unit U = as_unit(S.rec[rs]);
     const int32_t rows = live ? (U.e1 - U.e0) * qhead : 0;
     const int64_t qrow = (int64_t)S.qi[ms][li] * A.hq + (int64_t)U.h * qhead + li % qhead;
-    gfloat* src = (li < rows ? (gfloat*)(A.q + qrow * kD) : zero_line()) + 4 * g;
+    gfloat* src = (li < rows ? (gfloat*)(A.q + qrow * kD) : zero_line()) + 8 * g;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) q[t] = *(gfloatx4*)(src + 16 * t);
+    for (int i = 0; i < 8; ++i) q[i] = *(gfloatx4*)(src + 32 * (i >> 1) + 4 * (i & 1));
   };
 
   // ---- prologue: records of units 0..2, metadata of units 0 and 1, q and the first piece of unit 0
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             l_row = ls;
           }
         } else {
-          // ---- O^T += V^T . P^T for piece c (row i of block db: d = 4i + (db & 3) + 64 (db >> 2))
+          // ---- O^T += V^T . P^T for piece c (row i of block db: d = 8i + db)
           constexpr int c = k - NCH;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -365,17 +374,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         if constexpr (k == 2 * NCH - 1) {
           // ---- the unit's partials: lane (li, g) holds row li,
-          // d = 16g + 4v + (db & 3) + 64 (db >> 2) in oacc[db][v]. The tile
-          // goes through this wave's LDS so that every store instruction
-          // writes 64 lanes x 16 B of contiguous rows (the unit's rows are
-          // consecutive in the partial arrays); stored straight from the
-          // accumulators, each instruction would write 16-B pieces 64 B apart.
+          // d = 32g + 8v + db in oacc[db][v]. The tile goes through this
+          // wave's LDS so that every store instruction writes 64 lanes x 16 B
+          // of contiguous rows (the unit's rows are consecutive in the
+          // partial arrays); stored straight from the accumulators, each
+          // instruction would write 16-B pieces 32 B apart.
           if (row_ok) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              *reinterpret_cast<floatx4*>(&S.ostage[li][16 * g + 4 * v]) =
+              *reinterpret_cast<floatx4*>(&S.ostage[li][32 * g + 8 * v]) =
                   floatx4{oacc[0][v], oacc[1][v], oacc[2][v], oacc[3][v]};
-              *reinterpret_cast<floatx4*>(&S.ostage[li][64 + 16 * g + 4 * v]) =
+              *reinterpret_cast<floatx4*>(&S.ostage[li][32 * g + 8 * v + 4]) =
                   floatx4{oacc[4][v], oacc[5][v], oacc[6][v], oacc[7][v]};
             }
             if (g == 0) {
