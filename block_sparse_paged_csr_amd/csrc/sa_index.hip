@@ -665,11 +665,20 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   int32_t* s_lkb = s_qb + tq;                   // [batch]
   int32_t* s_dlb = s_lkb + batch;               // [batch]
 
+  // Entry slots k (entries tid + kFusedThreads k) that hold an entry for some
+  // lane of this wave; the loops over entries skip the others as a whole
+  // wave (with tq * topk below the workgroup's capacity, most waves have
+  // one slot or none).
+  const int32_t tid0 = tid - (tid & 63);
+  const int32_t nk_wave = tid0 < items ? (items - tid0 + kFusedThreads - 1) / kFusedThreads : 0;
+
   // this thread's entries of `selected`, loaded first so that their latency
   // overlaps the per-sequence setup
   int32_t v_k[kFusedItems];
 #pragma unroll
   for (int k = 0; k < kFusedItems; ++k) {
+    v_k[k] = -1;
+    if (k >= nk_wave) continue;
     const int32_t i = tid + kFusedThreads * k;
     const int32_t q = i / topk, r = i - q * topk;
     v_k[k] = i < items ? A.selected[((int64_t)q * hkv + h) * topk + r] : -1;
@@ -680,8 +689,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   constexpr int kSeqPerThread = (kFusedMaxBatch + kFusedThreads - 1) / kFusedThreads;
   int64_t c0_k[kSeqPerThread], c1_k[kSeqPerThread];
   int32_t used_k[kSeqPerThread];
+  // (sequence slots with no sequence for any lane of the wave read nothing)
+  const int32_t nb_wave = tid0 < batch ? (batch - tid0 + kFusedThreads - 1) / kFusedThreads : 0;
 #pragma unroll
   for (int k = 0; k < kSeqPerThread; ++k) {
+    c0_k[k] = c1_k[k] = 0;
+    used_k[k] = 0;
+    if (k >= nb_wave) continue;
     const int32_t b = tid + kFusedThreads * k;
     const int32_t bb = b < batch ? b : 0;
     c0_k[k] = A.cu[bb];
@@ -749,6 +763,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     arr_k[k] = 0;
     col0_k[k] = 0;
     len_k[k] = 0;
+    if (k >= nk_wave) continue;
     const int32_t i = tid + kFusedThreads * k;
     if (i >= items) continue;
     const int32_t q = i / topk, r = i - q * topk;
@@ -783,13 +798,19 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     for (int32_t p0 = 0; p0 < ppb_read; p0 += kPageBatch) {
       int32_t page[kFusedItems][kPageBatch];
 #pragma unroll
-      for (int k = 0; k < kFusedItems; ++k)
+      for (int k = 0; k < kFusedItems; ++k) {
+        if (k < nk_wave) {
 #pragma unroll
-        for (int x = 0; x < kPageBatch; ++x) {
-          const int32_t pl = p0 + x;
-          const bool touched = pl < A.ppb && pl * A.page_size < len_k[k];
-          page[k][x] = A.block_tables[touched ? col0_k[k] + pl : 0];
+          for (int x = 0; x < kPageBatch; ++x) {
+            const int32_t pl = p0 + x;
+            const bool touched = pl < A.ppb && pl * A.page_size < len_k[k];
+            page[k][x] = A.block_tables[touched ? col0_k[k] + pl : 0];
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < kPageBatch; ++x) page[k][x] = 0;
         }
+      }
 #pragma unroll
       for (int k = 0; k < kFusedItems; ++k)
 #pragma unroll
@@ -869,7 +890,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   for (int k = 0; k < kFusedItems; ++k) {
     const int32_t i = tid + kFusedThreads * k;
     inv_k[k] = -1;
-    if (i >= items) continue;
+    if (k >= nk_wave || i >= items) continue;
     const int32_t q = i / topk, r = i - q * topk;
     if (slot_k[k] >= 0) {
       const int32_t sl = slot_k[k];
