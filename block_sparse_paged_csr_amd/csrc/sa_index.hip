@@ -643,7 +643,7 @@ __device__ inline uint2 slot_sums(int c, const BuildArgs& A, int thr_e) {
 // [min(nbs, tq*topk)] each; batch of each query [tq]; lk and causal delta per
 // sequence [batch] each.
 __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, BuildArgs A) {
-  extern __shared__ int32_t s_dyn[];
+  extern __shared__ __align__(16) int32_t s_dyn[];
   __shared__ uint2 s_w2[kFusedThreads / 64];
   __shared__ int s_w1[kFusedThreads / 64];
   __shared__ unsigned long long s_err;
@@ -835,7 +835,40 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   const int32_t thr_e = (int32_t)(((int64_t)A.mfma_min_rows + A.qhead - 1) / A.qhead);
   const int32_t per = (nslots + kFusedThreads - 1) / kFusedThreads;   // slots [tid*per, +per)
   int32_t e_h, ns_h, uw_h, um_h;
-  {
+  if (per == 4 && (nslots & 3) == 0) {
+    // four slots a thread (decode: 4096 slots): one 16-byte LDS read and
+    // write each, the slots' sums kept for the second pass
+    const bool have = tid * 4 < nslots;
+    const int4 c4 = have ? *reinterpret_cast<const int4*>(&s_cnt[tid * 4]) : make_int4(0, 0, 0, 0);
+    const int c[4] = {c4.x, c4.y, c4.z, c4.w};
+    uint2 t[4];
+    uint2 mine = make_uint2(0u, 0u);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      t[x] = slot_sums(c[x], A, thr_e);
+      mine.x += t[x].x;
+      mine.y += t[x].y;
+    }
+    uint32_t ta, tb;
+    uint2 run = block_excl_scan2(mine.x, mine.y, s_w2, &ta, &tb);
+    e_h = (int32_t)(ta & 0xffffu);
+    ns_h = (int32_t)(ta >> 16);
+    uw_h = (int32_t)(tb & 0xffffu);
+    um_h = (int32_t)(tb >> 16);
+    int off[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      off[x] = (int32_t)(run.x & 0xffffu);
+      if (c[x] > 0) {
+        const int32_t j = (int32_t)(run.x >> 16);
+        s_list[j] = tid * 4 + x;
+        s_uoff[j] = run.y;
+      }
+      run.x += t[x].x;
+      run.y += t[x].y;
+    }
+    if (have) *reinterpret_cast<int4*>(&s_cnt[tid * 4]) = make_int4(off[0], off[1], off[2], off[3]);
+  } else {
     uint2 mine = make_uint2(0u, 0u);
     for (int32_t x = 0; x < per; ++x) {
       const int32_t sl = tid * per + x;
