@@ -944,8 +944,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   for (int64_t j = ns_h + tid; j <= nbs; j += kFusedThreads)
     P.sel_offsets[(int64_t)h * (nbs + 1) + j] = e_h;
 
-  // ---- look-back: totals of the heads before h (all heads for the last one)
-  for (int32_t hh = tid; hh < h; hh += kFusedThreads) {
+  // ---- look-back: totals of the heads before h (all heads for the last one).
+  // Thread hh polls head hh's flag, then reads its totals. With at most 64
+  // heads before h the pollers are wave 0's lanes and fold the totals with
+  // a wave reduction; beyond that, through LDS atomics.
+  static_assert(offsetof(HeadAgg, ns) == 8 && offsetof(HeadAgg, um) == 16 &&
+                offsetof(HeadAgg, err) == 24, "HeadAgg layout");
+  auto read_head = [&](int32_t hh, unsigned long long* e, unsigned long long* ns, int32_t* uw,
+                       int32_t* um, unsigned long long* err) -> bool {
     const HeadAgg* ag = P.agg + hh;
     int spins = 0;
     while (__hip_atomic_load(&ag->flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != A.epoch &&
@@ -953,23 +959,58 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
       __builtin_amdgcn_s_sleep(1);
       ++spins;
     }
-    if (spins >= kLookbackSpins) {
-      atomicMin(&s_err, err_key(kRankLookback, 0));
-      continue;
-    }
+    if (spins >= kLookbackSpins) return false;
     // bytes 0..31 of the HeadAgg in two 16-byte loads: w0 = (e lo, e hi, ns, uw),
     // w1 = (um, pad, err lo, err hi)
-    static_assert(offsetof(HeadAgg, ns) == 8 && offsetof(HeadAgg, um) == 16 &&
-                  offsetof(HeadAgg, err) == 24, "HeadAgg layout");
     const int4 w0 = *reinterpret_cast<const int4*>(ag);
     const int4 w1 = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ag) + 16);
-    const unsigned long long e = (unsigned long long)(uint32_t)w0.x | ((unsigned long long)(uint32_t)w0.y << 32);
-    const unsigned long long err = (unsigned long long)(uint32_t)w1.z | ((unsigned long long)(uint32_t)w1.w << 32);
-    atomicAdd(&s_base_e, e);
-    atomicAdd(&s_base_ns, (unsigned long long)w0.z);
-    atomicAdd(&s_base_uw, w0.w);
-    atomicAdd(&s_base_um, w1.x);
-    atomicMin(&s_err, err);
+    *e = (unsigned long long)(uint32_t)w0.x | ((unsigned long long)(uint32_t)w0.y << 32);
+    *err = (unsigned long long)(uint32_t)w1.z | ((unsigned long long)(uint32_t)w1.w << 32);
+    *ns = (unsigned long long)w0.z;
+    *uw = w0.w;
+    *um = w1.x;
+    return true;
+  };
+  if (h <= 64) {
+    if (tid < 64) {
+      unsigned long long e = 0, ns = 0, err = ~0ull;
+      int32_t uw = 0, um = 0;
+      if (tid < h && !read_head(tid, &e, &ns, &uw, &um, &err)) {
+        e = ns = 0;
+        uw = um = 0;
+        err = err_key(kRankLookback, 0);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        e += __shfl_xor(e, off, 64);
+        ns += __shfl_xor(ns, off, 64);
+        uw += __shfl_xor(uw, off, 64);
+        um += __shfl_xor(um, off, 64);
+        const unsigned long long o = __shfl_xor(err, off, 64);
+        err = o < err ? o : err;
+      }
+      if (tid == 0) {
+        s_base_e = e;
+        s_base_ns = ns;
+        s_base_uw = uw;
+        s_base_um = um;
+        atomicMin(&s_err, err);
+      }
+    }
+  } else {
+    for (int32_t hh = tid; hh < h; hh += kFusedThreads) {
+      unsigned long long e, ns, err;
+      int32_t uw, um;
+      if (!read_head(hh, &e, &ns, &uw, &um, &err)) {
+        atomicMin(&s_err, err_key(kRankLookback, 0));
+        continue;
+      }
+      atomicAdd(&s_base_e, e);
+      atomicAdd(&s_base_ns, ns);
+      atomicAdd(&s_base_uw, uw);
+      atomicAdd(&s_base_um, um);
+      atomicMin(&s_err, err);
+    }
   }
   __syncthreads();
   const int64_t hb = (int64_t)s_base_e;
