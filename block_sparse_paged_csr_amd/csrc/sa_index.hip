@@ -735,20 +735,26 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
   }
   __syncthreads();
   {
-    // batch of q = last sequence starting at or before q (types.rs batch_of)
-    int v[4], m = -1;
+    // batch of q = last sequence starting at or before q (types.rs batch_of):
+    // a max-scan over the queries, four a thread; up to 256 queries it is
+    // wave 0's alone (no workgroup barriers)
+    if (tq > 256 || tid < 64) {
+      int v[4], m = -1;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int32_t q = 4 * tid + k;
-      v[k] = q < tq ? s_qb[q] : -1;
-      m = v[k] > m ? v[k] : m;
-      v[k] = m;
-    }
-    const int pre = block_excl_max(m, s_w1);
+      for (int k = 0; k < 4; ++k) {
+        const int32_t q = 4 * tid + k;
+        v[k] = q < tq ? s_qb[q] : -1;
+        m = v[k] > m ? v[k] : m;
+        v[k] = m;
+      }
+      const int pre = tq > 256 ? block_excl_max(m, s_w1)
+                               : __builtin_amdgcn_update_dpp(-1, wave_incl_max(m), 0x138, 0xf, 0xf,
+                                                             false);   // wave_shr:1
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int32_t q = 4 * tid + k;
-      if (q < tq) s_qb[q] = v[k] > pre ? v[k] : pre;
+      for (int k = 0; k < 4; ++k) {
+        const int32_t q = 4 * tid + k;
+        if (q < tq) s_qb[q] = v[k] > pre ? v[k] : pre;
+      }
     }
   }
   __syncthreads();
