@@ -245,8 +245,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
 // Blocks of up to 64 keys: 16-row tiles on v_mfma_f32_16x16x4f32, so that
 // units of 17..64 rows (most units of mixed batches) keep 2..4 waves busy.
 // The block's K and V are staged in LDS once per unit as above; each wave then
-// computes whole 16-row tiles against every key, with the same operand
-// layout as the one-wave decode kernel:
+// computes whole 16-row tiles against every key, with this operand layout
+// (its operands come from LDS, so their order does not affect the loads):
 //   S^T[key, row]: MFMA t, component c, lane group g takes d = 16t + 4g + c
 //   O^T[d, row]:   output row i of MFMA block db stands for d = 4i + (db & 3) + 64 (db >> 2)
 // and an exact softmax over the block from register-resident scores.

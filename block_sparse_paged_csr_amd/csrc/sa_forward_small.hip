@@ -74,7 +74,6 @@ enum KvFormat : int { kKvF32 = SA_KV_F32, kKvBf16 = SA_KV_BF16, kKvF16 = SA_KV_F
 
 typedef const __attribute__((address_space(1))) uint16_t gu16;
 typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
-typedef const __attribute__((address_space(1))) uintx2 guint2;
 typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) uintx4 guint4;
 
