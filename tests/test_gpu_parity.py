@@ -10,6 +10,8 @@ ragged, prefill and skewed workloads at full size in the launch configuration
 the benchmark times, with the output compared on sampled queries (all queries
 for decode) and the index compared in full.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -424,3 +426,72 @@ def test_full_size_workload(name, n_sample):
     queries = None if n_sample is None else _sample_queries(w, n_sample)
     err = _check_output(w, out, lse, queries)
     print(f"[gpu case] {name}: O rel err {err:.3e}", flush=True)
+
+
+# The one-kernel build at the edges of its own paths: the batch-of-query
+# scan done by one wave (up to 256 queries) or by the workgroup (more), entry
+# counts that straddle a wave's share of entries (1024 a slot), the slot scan
+# of four slots a thread (4096 slots) against the general one (4095 and
+# 5000), and many heads for the look-back. Built with and without the
+# one-kernel path; index bit-exact, output against the oracle.
+def _fused_case(seed, qo, batch, topk, msb, hkv, ps=4, ppb=2, qhead=2, d=16):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bs = ps * ppb
+    max_pages = msb * ppb
+    qo_b = np.full(batch, qo // batch, dtype=np.int64)
+    qo_b[: qo % batch] += 1
+    cu = np.concatenate([[0], np.cumsum(qo_b)]).astype(np.int64)
+    tq = int(cu[-1])
+    kv = rng.integers(bs, msb * bs + 1, size=batch)
+    pages = [int(math.ceil(k / ps)) for k in kv]
+    num_pages = int(sum(pages)) + 3
+    perm = rng.permutation(num_pages)
+    tbl = np.full((batch, max_pages), -1, dtype=np.int32)
+    o = 0
+    for b in range(batch):
+        tbl[b, : pages[b]] = perm[o:o + pages[b]]
+        o += pages[b]
+    sel = np.full((tq, hkv, topk), -1, dtype=np.int32)
+    for q in range(tq):
+        b = int(np.searchsorted(cu, q, side="right") - 1)
+        hi = max(1, int(math.ceil(kv[b] / bs)))
+        for h in range(hkv):
+            k = min(topk, hi)
+            ids = rng.choice(hi, size=k, replace=False)
+            row = np.full(topk, -1, dtype=np.int64)
+            row[:k] = ids
+            row[rng.random(topk) < 0.2] = -1
+            sel[q, h] = rng.permutation(row)
+    hq = hkv * qhead
+    return W.Workload("fused_edge", rng.standard_normal((tq, hq, d), dtype=np.float32),
+                      rng.standard_normal((num_pages, hkv, ps, d), dtype=np.float32),
+                      rng.standard_normal((num_pages, hkv, ps, d), dtype=np.float32),
+                      sel, tbl, cu, None, hq, hkv, d, bs, ps, topk, 1.0 / math.sqrt(d),
+                      bool(seed % 2))
+
+
+FUSED_EDGE = [
+    # (qo, batch, topk, msb, hkv)
+    (256, 4, 4, 1024, 1),    # 256 queries: one-wave scan; 4096 slots: four a thread
+    (257, 5, 4, 819, 2),     # 257 queries: workgroup scan; 4095 slots
+    (300, 3, 8, 1000, 1),    # 2400 entries; 3000 slots
+    (1025, 7, 1, 600, 3),    # 1025 entries: a wave's share crosses 1024
+    (683, 2, 6, 2500, 1),    # 4098 entries: past the one-kernel build's capacity
+    (512, 8, 8, 625, 1),     # 4096 entries, 5000 slots: five slots a thread
+    (32, 32, 16, 128, 40),   # 40 heads: the look-back folds 39 heads' totals
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_EDGE)))
+def test_fused_build_edges(case, build_path):
+    qo, batch, topk, msb, hkv = FUSED_EDGE[case]
+    w = _fused_case(9000 + case, qo, batch, topk, msb, hkv)
+    _print_case("fused_build_edges", idx=case, tq=w.tq, topk=topk, nbs=batch * msb, hkv=hkv,
+                path=build_path)
+    d_in = dev_inputs(w)
+    idx = run_index(w, d_in)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+    out, lse = run_attention(w, d_in)
+    _check_output(w, out, lse)
