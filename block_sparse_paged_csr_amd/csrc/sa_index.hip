@@ -11,6 +11,9 @@
 //                    compaction of nonempty slots, unit counts per slot
 //   k_index_scatter  one thread per kept (q, h, r): atomic cursor per slot,
 //                    key q*topk + r into the slot's segment (unordered)
+//                    (where one sequence's hkv*msb counters fit LDS, the
+//                    histogram and the scatter run as *_agg variants that
+//                    count a chunk of entries in LDS first)
 //   k_index_rank     persistent over the nonempty slots of all heads: rank
 //                    of each key inside its slot's segment; the plateau of
 //                    sel_slots / sel_offsets past the nonempty slots
@@ -35,6 +38,10 @@ constexpr int kScanThreads = 256;
 constexpr int kScanItems = kScanChunkSlots / kScanThreads;   // slots per thread
 constexpr int kLookbackSpins = 1 << 22;              // then the build reports a runtime error
 constexpr uint64_t kRankLookback = 5;                // error rank: a head's totals never appeared
+constexpr int kAggThreads = 1024;                    // aggregating histogram / scatter
+constexpr int kAggPer = 4;                           // entries per thread
+constexpr int kAggItems = kAggThreads * kAggPer;     // entries per workgroup
+constexpr int32_t kAggMaxSlots = 8192;               // hkv*msb LDS counters (32 KB)
 
 __device__ inline int4 add4(int4 a, int4 b) {
   return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
@@ -138,10 +145,12 @@ __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
 }
 
 // Thread per entry of `selected`, in memory order idx = (q*hkv + h)*topk + r.
-__global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
-  const int64_t total = A.tq * A.hkv * A.topk;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
+// One entry idx = (q*hkv + h)*topk + r of `selected`: sets inv to -1, flags
+// an id outside [-1, msb) and missing page ids of the block's valid range; a
+// kept entry (a valid id whose block starts below the sequence's kv length)
+// returns true with its head h, sequence b and block v.
+__device__ inline bool hist_entry(const IndexPtrs& P, const BuildArgs& A, int64_t idx, int32_t* hp,
+                                  int32_t* bp, int32_t* vp) {
   const int32_t r = (int32_t)(idx % A.topk);
   const int64_t qh = idx / A.topk;
   const int32_t h = (int32_t)(qh % A.hkv);
@@ -149,15 +158,15 @@ __global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
   const int32_t v = A.selected[idx];
   const int2 qi = P.qinfo[q];
   P.inv[((int64_t)h * A.tq + q) * A.topk + r] = -1;
-  if (v == -1) return;
+  if (v == -1) return false;
   if (v < -1 || v >= A.msb) {
     atomicMin(&P.hdr->err_key, err_key(kRankSelected, (uint64_t)idx));
-    return;
+    return false;
   }
   const int32_t b = qi.x;
   const int64_t lk = qi.y;
   const int64_t block_start = (int64_t)v * A.block_size;
-  if (block_start >= lk) return;
+  if (block_start >= lk) return false;
   if (A.num_pages >= 0) {
     // Pages that the kept block's valid range touches must exist (the
     // forward's "block_tables page id" check, moved into the build).
@@ -171,7 +180,54 @@ __global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
     }
     if (bad != INT64_MAX) atomicMin(&P.hdr->err_key, err_key(kRankPage, (uint64_t)bad));
   }
-  atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
+  *hp = h;
+  *bp = b;
+  *vp = v;
+  return true;
+}
+
+__global__ __launch_bounds__(256) void k_index_hist(IndexPtrs P, BuildArgs A) {
+  const int64_t total = A.tq * A.hkv * A.topk;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  int32_t h, b, v;
+  if (hist_entry(P, A, idx, &h, &b, &v)) atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
+}
+
+// Aggregating variants of the histogram and the scatter: a workgroup takes
+// kAggItems consecutive entries, which cover a run of consecutive queries and
+// so mostly one sequence b0 (that of the chunk's first query). Its kept
+// entries of b0 count into LDS counters over (h, v) (hkv*msb of them, dynamic
+// LDS), and the workgroup then adds each nonzero count to the global counter
+// with one atomic. Entries of another sequence take the global atomic
+// directly. Selections concentrate on a few blocks per sequence (sinks, local
+// windows, popular blocks), so this turns most same-address device atomics
+// into LDS ones.
+__global__ __launch_bounds__(kAggThreads) void k_index_hist_agg(IndexPtrs P, BuildArgs A) {
+  extern __shared__ int32_t s_agg[];
+  const int tid = threadIdx.x;
+  const int64_t total = A.tq * A.hkv * A.topk;
+  const int32_t nloc = A.hkv * A.msb;
+  const int64_t c0 = (int64_t)blockIdx.x * kAggItems;
+  for (int32_t j = tid; j < nloc; j += kAggThreads) s_agg[j] = 0;
+  // the grid covers total > 0 entries, but guard the empty launch anyway
+  const int32_t b0 = c0 < total ? P.qinfo[c0 / ((int64_t)A.hkv * A.topk)].x : -1;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kAggPer; ++k) {
+    const int64_t idx = c0 + (int64_t)k * kAggThreads + tid;
+    int32_t h, b, v;
+    if (idx < total && hist_entry(P, A, idx, &h, &b, &v)) {
+      if (b == b0) atomicAdd(&s_agg[h * A.msb + v], 1);
+      else atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b * A.msb + v], 1);
+    }
+  }
+  __syncthreads();
+  for (int32_t j = tid; j < nloc; j += kAggThreads) {
+    const int32_t c = s_agg[j];
+    const int32_t h = j / A.msb;
+    if (c > 0) atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b0 * A.msb + (j - h * A.msb)], c);
+  }
 }
 
 // Workgroup (h, c) scans chunk c (kScanChunkSlots slots) of head h: its
@@ -313,6 +369,54 @@ __global__ __launch_bounds__(256) void k_index_scatter(IndexPtrs P, BuildArgs A)
   if ((int64_t)v * A.block_size >= qi.y) return;
   const int32_t pos = atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)qi.x * A.msb + v], 1);
   P.keys[hb + pos] = (int32_t)(q * A.topk + r);
+}
+
+// The scatter's aggregating variant (see k_index_hist_agg): LDS cursors hand
+// out offsets inside the chunk's share of each (h, v) slot of b0, and one
+// global atomic per nonzero slot reserves that share.
+__global__ __launch_bounds__(kAggThreads) void k_index_scatter_agg(IndexPtrs P, BuildArgs A) {
+  extern __shared__ int32_t s_agg[];
+  const int tid = threadIdx.x;
+  const int64_t total = A.tq * A.hkv * A.topk;
+  const int32_t nloc = A.hkv * A.msb;
+  const int64_t c0 = (int64_t)blockIdx.x * kAggItems;
+  for (int32_t j = tid; j < nloc; j += kAggThreads) s_agg[j] = 0;
+  // the grid covers total > 0 entries, but guard the empty launch anyway
+  const int32_t b0 = c0 < total ? P.qinfo[c0 / ((int64_t)A.hkv * A.topk)].x : -1;
+  __syncthreads();
+  int32_t loc[kAggPer], li[kAggPer], key[kAggPer], hh[kAggPer];
+#pragma unroll
+  for (int k = 0; k < kAggPer; ++k) {
+    loc[k] = -1;
+    const int64_t idx = c0 + (int64_t)k * kAggThreads + tid;
+    if (idx >= total) continue;
+    const int32_t r = (int32_t)(idx % A.topk);
+    const int64_t qh = idx / A.topk;
+    const int32_t h = (int32_t)(qh % A.hkv);
+    const int64_t q = qh / A.hkv;
+    const int32_t v = A.selected[idx];
+    const int2 qi = P.qinfo[q];
+    if (v < 0 || v >= A.msb || (int64_t)v * A.block_size >= qi.y) continue;
+    key[k] = (int32_t)(q * A.topk + r);
+    hh[k] = h;
+    if (qi.x == b0) {
+      loc[k] = h * A.msb + v;
+      li[k] = atomicAdd(&s_agg[loc[k]], 1);
+    } else {
+      const int32_t pos = atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)qi.x * A.msb + v], 1);
+      P.keys[head_edge_base(P, h) + pos] = key[k];
+    }
+  }
+  __syncthreads();
+  for (int32_t j = tid; j < nloc; j += kAggThreads) {
+    const int32_t c = s_agg[j];
+    const int32_t h = j / A.msb;
+    if (c > 0) s_agg[j] = atomicAdd(&P.cnt[(int64_t)h * A.nbs + (int64_t)b0 * A.msb + (j - h * A.msb)], c);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kAggPer; ++k)
+    if (loc[k] >= 0) P.keys[head_edge_base(P, hh[k]) + s_agg[loc[k]] + li[k]] = key[k];
 }
 
 // Status and error details from the smallest error key (~0ull: none).
@@ -1132,10 +1236,29 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
   if (init_grid < 1) init_grid = 1;
   hipLaunchKernelGGL(k_index_init, dim3((unsigned)init_grid), dim3(256), 0, s, P, a);
   const int64_t entries = a.tq * a.hkv * a.topk;
-  hipLaunchKernelGGL(k_index_hist, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
+  // Aggregate per workgroup where one sequence's (h, block) counters fit LDS,
+  // slots repeat (4 entries a slot on average) and the chunks fill half the
+  // CUs; elsewhere (few entries a slot, as in ragged batches) the LDS pass
+  // costs more than the atomics it saves. SA_BUILD_AGG=1 / 0 forces the
+  // choice where the counters fit (tests cover both kernels).
+  const int64_t nloc = (int64_t)a.hkv * a.msb;
+  const bool agg_fits = nloc > 0 && nloc <= kAggMaxSlots;
+  bool agg = agg_fits && entries >= 4 * slots && entries >= (int64_t)cu_count() * kAggItems / 2;
+  const char* force_agg = std::getenv("SA_BUILD_AGG");
+  if (force_agg != nullptr && (force_agg[0] == '0' || force_agg[0] == '1'))
+    agg = agg_fits && force_agg[0] == '1';
+  if (agg)
+    hipLaunchKernelGGL(k_index_hist_agg, dim3(grid_for(entries, kAggItems)), dim3(kAggThreads),
+                       (size_t)nloc * 4, s, P, a);
+  else
+    hipLaunchKernelGGL(k_index_hist, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
   hipLaunchKernelGGL(k_index_scan, dim3((unsigned)(a.hkv * scan_chunks(a.nbs))), dim3(kScanThreads),
                      0, s, P, a);
-  hipLaunchKernelGGL(k_index_scatter, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
+  if (agg)
+    hipLaunchKernelGGL(k_index_scatter_agg, dim3(grid_for(entries, kAggItems)), dim3(kAggThreads),
+                       (size_t)nloc * 4, s, P, a);
+  else
+    hipLaunchKernelGGL(k_index_scatter, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
   // persistent: a few workgroups per CU loop over the nonempty slots; large
   // slots rank through an LDS bitmap over the tq*topk key space when it fits
   BuildArgs ra = a;

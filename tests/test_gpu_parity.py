@@ -495,3 +495,38 @@ def test_fused_build_edges(case, build_path):
     check_units(arrs, info, ref, idx.c.cap_edges, w)
     out, lse = run_attention(w, d_in)
     _check_output(w, out, lse)
+
+
+# The multi-kernel build's histogram and scatter count a chunk of 4096
+# entries in LDS when one sequence's hkv*msb counters fit (8192 at most) and
+# slots repeat, and take one global atomic an entry otherwise; SA_BUILD_AGG
+# forces either kernel pair where the counters fit. Cases at that limit and
+# past it, with hot slots (a few blocks shared by thousands of queries), and
+# with chunks that span hundreds of short sequences (entries outside the
+# chunk's first sequence take the global atomic). Index bit-exact, output
+# against the oracle.
+AGG_EDGE = [
+    # (qo, batch, topk, msb, hkv)
+    (600, 2, 16, 4096, 2),   # 8192 counters: the LDS path; a chunk crosses sequences
+    (600, 2, 16, 4097, 2),   # 8194 counters: one global atomic an entry
+    (2000, 1, 8, 16, 2),     # 16 blocks for 2000 queries: ~1000 edges a slot
+    (3000, 600, 2, 8, 1),    # 5-query sequences: ~400 of them in a chunk
+]
+
+
+@pytest.mark.parametrize("agg", ["1", "0"])
+@pytest.mark.parametrize("case", range(len(AGG_EDGE)))
+def test_multikernel_build_aggregation(case, agg, monkeypatch):
+    monkeypatch.setenv("SA_BUILD_MULTIKERNEL", "1")
+    monkeypatch.setenv("SA_BUILD_AGG", agg)
+    qo, batch, topk, msb, hkv = AGG_EDGE[case]
+    w = _fused_case(9100 + case, qo, batch, topk, msb, hkv)
+    _print_case("multikernel_build_aggregation", idx=case, tq=w.tq, topk=topk, nbs=batch * msb,
+                hkv=hkv, agg=agg)
+    d_in = dev_inputs(w)
+    idx = run_index(w, d_in)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+    out, lse = run_attention(w, d_in)
+    _check_output(w, out, lse)
