@@ -466,9 +466,9 @@ __device__ void finalize_header(const IndexPtrs& P, const BuildArgs& A) {
 
 constexpr int kRankChunk = 2048;   // keys staged in LDS per pass
 constexpr int kRankKeys = 4;       // keys held per thread per pass
-constexpr int kRankBitmapMaxWords = 4096;   // 16 KB (key spaces of up to 131072 keys): a
+constexpr int kRankBitmapMaxWords = 4096;   // 16 KB (a sequence of up to 131072 keys): a
                                             // larger bitmap costs the small slots occupancy
-constexpr int kRankBitmapMinKeys = 384;     // smaller slots: pairwise counting is cheaper
+constexpr int kRankBitmapMinKeys = 128;     // smaller slots: pairwise counting is cheaper
 
 __device__ inline void write_edge(const IndexPtrs& P, const BuildArgs& A, int32_t h,
                                   int64_t head_base, int32_t off0, int32_t key, int32_t rank) {
@@ -480,6 +480,7 @@ __device__ inline void write_edge(const IndexPtrs& P, const BuildArgs& A, int32_
 
 struct SlotInfo {
   int32_t n, h, j, off0, uw, um, b, blk, lk, delta;
+  int32_t kb, nw;   // the sequence's key range [kb, kb + 32*nw) covers the slot's keys
   int64_t base;
 };
 
@@ -548,6 +549,8 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
         const int64_t lk = kv_len_dev(A.used, si.b, A.msb, A.block_size);
         si.lk = (int32_t)lk;
         si.delta = (int32_t)((lk >= qo_len ? lk - qo_len : 0) - q0);
+        si.kb = (int32_t)(q0 * A.topk);
+        si.nw = (int32_t)((qo_len * A.topk + 31) / 32);
         si.h = h;
         si.j = (int32_t)j;
       }
@@ -570,17 +573,18 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
         const int32_t n = s_slot[s].n;
         if (n == 0) continue;
         const int32_t* seg = P.keys + s_slot[s].base + s_slot[s].off0;
-        if (A.rank_bitmap_words > 0 && n >= kRankBitmapMinKeys) {
-          // The slot's keys as bits of a bitmap over the key space; a key's
-          // rank is the number of set bits before it: a prefix count per
-          // thread's run of words, then within the run.
-          const int32_t W = A.rank_bitmap_words;
+        if (s_slot[s].nw <= A.rank_bitmap_words && n >= kRankBitmapMinKeys) {
+          // The slot's keys as bits of a bitmap over its sequence's key
+          // range (the slot's queries are that sequence's); a key's rank is
+          // the number of set bits before it: a prefix count per thread's
+          // run of words, then within the run.
+          const int32_t W = s_slot[s].nw, kb = s_slot[s].kb;
           const int32_t C = (W + 255) / 256;                 // words per thread
           for (int32_t x = tid; x < W; x += 256) s_bits[x] = 0u;
           __syncthreads();
           for (int32_t i = tid; i < n; i += 256) {
-            const int32_t key = seg[i];
-            atomicOr(&s_bits[key >> 5], 1u << (key & 31));
+            const int32_t bit = seg[i] - kb;
+            atomicOr(&s_bits[bit >> 5], 1u << (bit & 31));
           }
           __syncthreads();
           int cntw = 0;
@@ -597,11 +601,11 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
           s_runpre[tid] = pre;
           __syncthreads();
           for (int32_t i = tid; i < n; i += 256) {
-            const int32_t key = seg[i];
-            const int32_t wd = key >> 5, run = wd / C;
+            const int32_t key = seg[i], bit = key - kb;
+            const int32_t wd = bit >> 5, run = wd / C;
             int32_t rank = s_runpre[run];
             for (int32_t x = run * C; x < wd; ++x) rank += __popc(s_bits[x]);
-            rank += __popc(s_bits[wd] & ((1u << (key & 31)) - 1u));
+            rank += __popc(s_bits[wd] & ((1u << (bit & 31)) - 1u));
             write_edge(P, A, s_slot[s].h, s_slot[s].base, s_slot[s].off0, key, rank);
           }
           __syncthreads();                           // the bitmap is reused
@@ -1260,10 +1264,11 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
   else
     hipLaunchKernelGGL(k_index_scatter, dim3(grid_for(entries, 256)), dim3(256), 0, s, P, a);
   // persistent: a few workgroups per CU loop over the nonempty slots; large
-  // slots rank through an LDS bitmap over the tq*topk key space when it fits
+  // slots rank through an LDS bitmap over their sequence's key range when it
+  // fits (the bitmap is sized for the whole tq*topk range, capped)
   BuildArgs ra = a;
-  const int64_t words = (a.tq * a.topk + 31) / 32;
-  ra.rank_bitmap_words = words <= kRankBitmapMaxWords ? (int32_t)words : 0;
+  const int64_t words = (a.tq * a.topk + 31) / 32;   // no sequence has more keys
+  ra.rank_bitmap_words = words <= kRankBitmapMaxWords ? (int32_t)words : kRankBitmapMaxWords;
   unsigned rank_grid = grid_for(slots, 4);
   if (rank_grid > 8 * cu_count()) rank_grid = 8 * cu_count();
   hipLaunchKernelGGL(k_index_rank, dim3(rank_grid), dim3(256), (size_t)ra.rank_bitmap_words * 4, s,

@@ -503,14 +503,17 @@ def test_fused_build_edges(case, build_path):
 # forces either kernel pair where the counters fit. Cases at that limit and
 # past it, with hot slots (a few blocks shared by thousands of queries), and
 # with chunks that span hundreds of short sequences (entries outside the
-# chunk's first sequence take the global atomic). Index bit-exact, output
-# against the oracle.
+# chunk's first sequence take the global atomic). The last two reach the rank
+# kernel's LDS bitmap over one sequence's keys and, past its 131072 keys, the
+# pairwise ranks. Index bit-exact, output against the oracle.
 AGG_EDGE = [
     # (qo, batch, topk, msb, hkv)
     (600, 2, 16, 4096, 2),   # 8192 counters: the LDS path; a chunk crosses sequences
     (600, 2, 16, 4097, 2),   # 8194 counters: one global atomic an entry
     (2000, 1, 8, 16, 2),     # 16 blocks for 2000 queries: ~1000 edges a slot
     (3000, 600, 2, 8, 1),    # 5-query sequences: ~400 of them in a chunk
+    (4000, 4, 8, 16, 2),     # hot slots in 4 sequences: rank bitmaps over each one's keys
+    (2100, 1, 64, 80, 1),    # 134400 keys in one sequence: past the rank bitmap (pairwise)
 ]
 
 
