@@ -147,7 +147,7 @@ struct BuildArgs {
   uint64_t epoch;            // distinct per build call, odd; tags HeadAgg / ChunkAgg flags
   uint64_t cap_magic;        // make_div_magic(cap_edges)
   uint64_t wave_cap_magic;   // make_div_magic(wave_cap_edges)
-  int32_t rank_bitmap_words; // words of the rank kernel's key bitmap (tq*topk bits), 0: none
+  int32_t rank_bitmap_words; // words of the rank kernel's key bitmap (tq*topk bits, capped)
 };
 
 struct FwdArgs {
