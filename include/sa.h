@@ -149,7 +149,12 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch,
  * "block_tables page id").
  * Work units split each slot of n edges into near-equal, consecutive ranges:
  * ceil(n / cap_edges) units for the MFMA kernel if n*(hq/hkv) >= mfma_min_rows,
- * else ceil(n / wave_cap_edges) units for the wavefront kernels. */
+ * else ceil(n / wave_cap_edges) units for the wavefront kernels.
+ * The kernels are chosen from the sizes; two environment variables, read at
+ * each call, override the choice for testing and leave the index unchanged:
+ * SA_BUILD_MULTIKERNEL=1 keeps small problems off the one-kernel build, and
+ * SA_BUILD_AGG=1 / 0 turns the multi-kernel build's per-workgroup (LDS)
+ * counting on / off where hkv*msb <= 8192. */
 sa_status sa_build_index(const int32_t* selected, int64_t selected_len,
                          const int32_t* block_tables, int64_t block_tables_len,
                          const int64_t* cu_seqlens_q, int64_t cu_len,
