@@ -46,8 +46,18 @@ __device__ inline float4 ld_f4(const float* p) {
 template <bool NT>
 __global__ __launch_bounds__(kMaxBlock) void k_combine(IndexPtrs P, CombineArgs A) {
   const int32_t qhead = A.qhead;
-  const int64_t q = blockIdx.x / A.hkv;
-  const int32_t h = blockIdx.x % A.hkv;
+  // Workgroup order: head-major over the one-wave kernel's partials (decode
+  // combine 5.2 -> 5.1 us), query-major over the MFMA kernels' (prefill's
+  // combine read them 2% slower head-major).
+  int64_t q;
+  int32_t h;
+  if constexpr (NT) {
+    h = (int32_t)(blockIdx.x / A.tq);
+    q = blockIdx.x - (int64_t)h * A.tq;
+  } else {
+    q = blockIdx.x / A.hkv;
+    h = blockIdx.x % A.hkv;
+  }
   const int32_t D4 = A.head_dim >> 2;
   const int x = threadIdx.x;
   const int qh = x / D4, c = x - qh * D4;
