@@ -52,8 +52,9 @@ __global__ __launch_bounds__(kMaxBlock) void k_combine(IndexPtrs P, CombineArgs 
   int64_t q;
   int32_t h;
   if constexpr (NT) {
-    h = (int32_t)(blockIdx.x / A.tq);
-    q = blockIdx.x - (int64_t)h * A.tq;
+    const uint32_t tq32 = (uint32_t)A.tq;   // tq * hkv workgroups: fits 32 bits
+    h = (int32_t)(blockIdx.x / tq32);
+    q = (int64_t)(blockIdx.x - (uint32_t)h * tq32);
   } else {
     q = blockIdx.x / A.hkv;
     h = blockIdx.x % A.hkv;
@@ -64,18 +65,29 @@ __global__ __launch_bounds__(kMaxBlock) void k_combine(IndexPtrs P, CombineArgs 
   const bool item = qh < qhead;
   const int32_t* inv = P.inv + ((int64_t)h * A.tq + q) * A.topk;
 
-  // independent reads first
+  // Independent reads first, in one round trip: status, head base and the
+  // first tile's inv entries, one rank per lane (lane & 15) in a single vector
+  // load, broadcast below with readlane. The rank index is clamped to
+  // topk - 1, so every load is in bounds; inv is read before the status test
+  // (a failed build leaves it allocated, and its values go unused then). The
+  // empty asm makes the status branch wait for the inv and head-base loads
+  // too, so that the compiler cannot sink them below the branch into round
+  // trips of their own.
+  const int32_t tl = (int32_t)(threadIdx.x & (kRankTile - 1));
   const int32_t status = P.hdr->status;
   const int64_t head_base = P.edge_head_base[h];
+  int32_t mine = inv[tl < A.topk ? tl : A.topk - 1];
+  asm volatile("" ::"v"(mine), "s"(head_base));
   if (status != SA_OK) return;
 
   float big = -INFINITY, total = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int32_t r0 = 0; r0 < A.topk; r0 += kRankTile) {
+    if (r0 > 0) mine = inv[r0 + tl < A.topk ? r0 + tl : A.topk - 1];
     int64_t row[kRankTile];
 #pragma unroll
     for (int t = 0; t < kRankTile; ++t) {
-      const int32_t p = r0 + t < A.topk ? inv[r0 + t] : -1;
+      const int32_t p = r0 + t < A.topk ? __builtin_amdgcn_readlane(mine, t) : -1;
       row[t] = (p >= 0 && item) ? (head_base + p) * qhead + qh : -1;
     }
     float mv[kRankTile], lv[kRankTile];
