@@ -810,6 +810,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     c1_k[k] = A.cu[bb + 1];
     used_k[k] = A.used != nullptr ? A.used[bb] : 0;
   }
+  // cu[0] and cu[batch] for head 0's checks, loaded here with the rest (cu
+  // has batch + 1 entries): behind the check's branches they were two
+  // serial round trips that the workgroup barrier below waited for
+  const int64_t cu_first = A.cu[0], cu_last = A.cu[batch];
 
   // ---- per-sequence lk and causal delta; batch of each query; cu checks
   for (int32_t x = tid; x < nslots; x += kFusedThreads) s_cnt[x] = 0;
@@ -838,8 +842,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
     if (c0 < c1 && c0 >= 0 && c0 < tq) s_qb[c0] = b;   // first query of a nonempty sequence
   }
   if (h == 0 && tid == 0) {
-    if (A.cu[0] != 0) atomicMin(&s_err, err_key(kRankCuContent, 0));
-    if (A.cu[batch] != A.tq) atomicMin(&s_err, err_key(kRankCuTotal, 0));
+    if (cu_first != 0) atomicMin(&s_err, err_key(kRankCuContent, 0));
+    if (cu_last != A.tq) atomicMin(&s_err, err_key(kRankCuTotal, 0));
   }
   __syncthreads();
   {
