@@ -514,6 +514,7 @@ AGG_EDGE = [
     (3000, 600, 2, 8, 1),    # 5-query sequences: ~400 of them in a chunk
     (4000, 4, 8, 16, 2),     # hot slots in 4 sequences: rank bitmaps over each one's keys
     (2100, 1, 64, 80, 1),    # 134400 keys in one sequence: past the rank bitmap (pairwise)
+    (200, 2, 2, 8, 70),      # 70 heads: the multi-kernel build's per-head totals and look-backs
 ]
 
 
