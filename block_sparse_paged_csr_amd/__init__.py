@@ -318,15 +318,18 @@ class Workspace:
 def sa_attention(q, k_pages, v_pages, selected, block_tables, cu_seqlens_q, used_kv_lens,
                  block_size, softmax_scale, causal, *, tq=None,
                  workspace: Workspace | None = None,
-                 out=None, lse=None, with_lse=True, return_index=False):
+                 out=None, lse=None, with_lse=True, return_index=False, check=True):
     """build -> forward -> combine on the current stream.
 
     Shapes: q [tq, hq, d]; k_pages/v_pages [num_pages, hkv, page_size, d];
     selected [tq, hkv, topk]; block_tables [batch, max_pages];
     cu_seqlens_q [batch+1] (int64); used_kv_lens [batch] (int32) or None.
-    ``tq`` defaults to q.shape[0]. Device-side errors (cu_seqlens content,
-    selected ids, page ids) leave ``out`` unwritten and are read with
-    ``sa_index_status`` on the returned index.
+    ``tq`` defaults to q.shape[0]. Errors the build finds on the device
+    (cu_seqlens content, selected ids, page ids) fill ``out`` and ``lse`` with
+    NaN; with ``check`` (the default) this call then waits for the stream,
+    reads the build's status and raises ``SaError``. ``check=False`` leaves the
+    call asynchronous; ``sa_index_status`` on the returned index reads the
+    status later.
     """
     _check_head_dims(q, k_pages, v_pages)
     if tq is None:
@@ -361,6 +364,8 @@ def sa_attention(q, k_pages, v_pages, selected, block_tables, cu_seqlens_q, used
         _stream(dev))
     _check(st)
     index = Index(c, workspace.raw)
+    if check:
+        sa_index_status(index, check=True, device=dev)
     if return_index:
         return out, lse, index
     return out, lse

@@ -78,7 +78,16 @@ __global__ __launch_bounds__(kMaxBlock) void k_combine(IndexPtrs P, CombineArgs 
   const int64_t head_base = P.edge_head_base[h];
   int32_t mine = inv[tl < A.topk ? tl : A.topk - 1];
   asm volatile("" ::"v"(mine), "s"(head_base));
-  if (status != SA_OK) return;
+  if (status != SA_OK) {
+    // The build failed (the pages return an error here): the forward wrote
+    // nothing, so the output gets a defined value instead of stale memory.
+    if (item) {
+      const int64_t o_off = (q * A.hq + (int64_t)h * qhead + qh) * A.head_dim + c * 4;
+      *reinterpret_cast<float4*>(A.out + o_off) = make_float4(NAN, NAN, NAN, NAN);
+      if (A.lse != nullptr && c == 0) A.lse[q * A.hq + (int64_t)h * qhead + qh] = NAN;
+    }
+    return;
+  }
 
   float big = -INFINITY, total = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

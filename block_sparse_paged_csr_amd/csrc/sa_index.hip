@@ -492,6 +492,12 @@ struct SlotInfo {
 __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
   if (blockIdx.x == 0 && threadIdx.x == 0) finalize_header(P, A);
   if (A.nbs == 0) return;                          // no slots at all (msb == 0)
+  // Every device error is final once the histogram has run. A failed build
+  // leaves edges, inv and the units unused, so the ranking is skipped; with
+  // bad cu_seqlens a slot's keys need not lie in its sequence's key range,
+  // which the bitmap below relies on.
+  if (__hip_atomic_load(&P.hdr->err_key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ~0ull)
+    return;
   extern __shared__ uint32_t s_bits[];              // [rank_bitmap_words] (dynamic)
   __shared__ SlotInfo s_slot[4];
   __shared__ __align__(16) int32_t s_keys[kRankChunk];
@@ -582,9 +588,10 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
           const int32_t C = (W + 255) / 256;                 // words per thread
           for (int32_t x = tid; x < W; x += 256) s_bits[x] = 0u;
           __syncthreads();
+          const uint32_t nbits = 32u * (uint32_t)W;
           for (int32_t i = tid; i < n; i += 256) {
             const int32_t bit = seg[i] - kb;
-            atomicOr(&s_bits[bit >> 5], 1u << (bit & 31));
+            if ((uint32_t)bit < nbits) atomicOr(&s_bits[bit >> 5], 1u << (bit & 31));
           }
           __syncthreads();
           int cntw = 0;
@@ -602,11 +609,13 @@ __global__ __launch_bounds__(256) void k_index_rank(IndexPtrs P, BuildArgs A) {
           __syncthreads();
           for (int32_t i = tid; i < n; i += 256) {
             const int32_t key = seg[i], bit = key - kb;
+            if ((uint32_t)bit >= nbits) continue;      // not reached with valid cu_seqlens
             const int32_t wd = bit >> 5, run = wd / C;
             int32_t rank = s_runpre[run];
             for (int32_t x = run * C; x < wd; ++x) rank += __popc(s_bits[x]);
             rank += __popc(s_bits[wd] & ((1u << (bit & 31)) - 1u));
-            write_edge(P, A, s_slot[s].h, s_slot[s].base, s_slot[s].off0, key, rank);
+            write_edge(P, A, s_slot[s].h, s_slot[s].base, s_slot[s].off0, key,
+                       rank < n ? rank : n - 1);
           }
           __syncthreads();                           // the bitmap is reused
           continue;

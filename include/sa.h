@@ -20,9 +20,12 @@
  *    The detail is then available from sa_last_error() on the same host thread.
  *  - Checks that need device data (cu_seqlens_q content, selected ids,
  *    block-table page ids) run inside the build kernels. They record the
- *    first failure in the index's device header. sa_forward and sa_combine
- *    on an index whose header holds an error write nothing. Call
- *    sa_index_status() to read the result.
+ *    first failure in the index's device header. On an index whose header
+ *    holds an error, sa_forward writes nothing and sa_combine writes NaN to
+ *    every element of `out` (and `lse`), so that a caller who does not wait
+ *    for the status never reads stale memory as a result. The pages' forward
+ *    returns the error instead; reporting it here would need a host wait.
+ *    Call sa_index_status() to read the error.
  *  - Layouts are row-major and element types are as stated: float32 for
  *    q/K/V/partials/outputs, int32 for ids, int64 for cu_seqlens_q.
  */
@@ -231,7 +234,8 @@ sa_status sa_forward_kv16(const sa_index* idx,
  * p = (edge_head_base[h] + inv)*qhead + qh:
  *   M = max m_p;  L = sum l_p exp(m_p - M);  O = sum o_p exp(m_p - M) / L
  *   out float32 [tq, hq, head_dim];  lse float32 [tq, hq] = M + log L, or NULL
- * No rank with finite m gives O = 0, lse = -inf. */
+ * No rank with finite m gives O = 0, lse = -inf. If the index's build found
+ * an input error (sa_index_status), every element of out and lse is NaN. */
 sa_status sa_combine(const sa_index* idx,
                      const float* o_partial, const float* m_partial, const float* l_partial,
                      int32_t hq, int32_t head_dim,
@@ -250,7 +254,8 @@ sa_status sa_attention_workspace_bytes(int64_t tq, int32_t hkv, int32_t topk, in
  * three calls above. Host checks run before anything is enqueued, in the
  * forward's order and then the build's. `idx_out` (host, may be NULL)
  * receives the index handle, so that sa_index_status() can read the
- * device-side outcome. */
+ * device-side outcome; when the build found an input error, out and lse
+ * hold NaN (see sa_combine). */
 sa_status sa_attention(const float* q, int64_t q_len,
                        const float* k_pages, int64_t k_len,
                        const float* v_pages, int64_t v_len,

@@ -17,9 +17,11 @@ What it computes, and the passages it follows (alice-llm 2.0.0,
   blocks, in float64. What a token contributes follows
   ``process_work_unit`` (forward.rs).
 * ``kvouter_ref.forward_partials_ref`` / ``combine_ref``: the KV-outer partials
-  ``(o, m, l)`` per edge and GQA lane (forward.rs, ``ForwardPartials`` and
-  ``process_work_unit``), and their log-sum-exp merge. Only the combine's name
-  and its "standard FlashAttention log-sum-exp update" are on the pages.
+  ``(o, m, l)`` per edge and GQA lane (forward.rs, the ``ForwardPartials``
+  field docs), each one block's share of the query-outer softmax, and their
+  log-sum-exp merge. The pages name the combine pass (forward.rs, module doc)
+  and say it is the log-sum-exp merge of FlashAttention, without its
+  formula.
 * ``dense_ref.dense_masked_ref``: brute-force masked dense attention over
   every logical position. It has no union gather and serves as a pin.
 * ``kv16_ref.decode_kv16``: the float32 value of a K/V page word stored as

@@ -15,12 +15,12 @@ index fields it must fill:
    (forward.rs, ``process_work_unit``, the KV-length resolution).
 3. Every ``(q, h, r)`` with ``v = selected[q, h, r]``: ``v == -1`` is padding;
    ``v < -1`` or ``v >= msb`` is ``SelectedOutOfRange``; ``v * block_size >= lk_b``
-   is dropped (the ``inv`` doc: "masked or out-of-range"); anything else is an
+   is dropped (the ``inv`` field doc: such ranks get ``-1``); anything else is an
    edge ``(q, r)`` of raw slot ``b * msb + v`` under head ``h``.
 4. Per head: the nonempty raw slots in ascending order form the compact list
    ``sel_slots[h, :num_sel[h]]`` (the rest of the row is ``-1``).
    ``sel_offsets[h]`` holds the head-local CSR offsets and stays at ``E_h``
-   after ``num_sel[h]`` (the "plateaued" doc). Inside a slot, edges are in
+   after ``num_sel[h]`` (the field doc keeps the offsets flat there). Inside a slot, edges are in
    ascending ``(q, r)``.
 5. ``edge_head_base`` is the exclusive prefix sum of ``E_h``.
    ``inv[h, q, r]`` is the head-local position of edge ``(q, r)``, or ``-1``.

@@ -1,125 +1,114 @@
 """KV-outer partials and their log-sum-exp combine, in float64 (test
-infrastructure; only tests, the smoke check and the benchmark's CPU-baseline
-leg may import it).
+infrastructure: only the tests, the package smoke check and the benchmark's
+CPU-baseline leg may import it; the GPU library never does).
 
-``forward_partials_ref`` restates ``process_work_unit`` (alice-llm 2.0.0,
-``forward.rs``) unit by unit, in its order, with one unit per compact slot:
+The partial of one edge comes from what it stands for (alice-llm 2.0.0,
+forward.rs: the ``ForwardPartials`` field docs, and what ``process_work_unit``
+lets one key of a block contribute). It is written out per edge, with no
+walk over slots, units or pages:
 
-1. decode the slot: ``raw = sel_slots[h, j]``, ``b = raw // msb``, ``blk = raw % msb``;
-2. clamp the block to ``[blk*bs, min((blk+1)*bs, lk_b))``; an empty range
-   leaves the slot's partials at their initial ``(o=0, m=-inf, l=0)``;
-3. gather the block's rows page by page through ``block_tables[b, blk*ppb + pl]``,
-   skipping negative pages; a page id ``>= num_pages`` is the
-   ``ShapeMismatch("block_tables page id")`` error;
-4. per edge ``(q, r)`` of the slot, and per GQA lane ``qh``: the score of each
-   gathered row is ``dot(q, k) * scale`` if the row is causally alive, else
-   ``-inf``; ``m`` is the max; all dead gives ``(0, -inf, 0)``; otherwise
-   ``p = exp(s - m)``, ``l = sum p`` and ``o = sum p * v``.
+* edge ``(q, r)`` under KV head ``h`` names block ``v = selected[q, h, r]`` of
+  the sequence ``b`` that holds query ``q``;
+* the block's keys ``T`` are the logical positions ``t`` with
+  ``v*bs <= t < min((v+1)*bs, lk_b)`` whose page ``block_tables[b, t // ps]``
+  is not negative (``k_t = k_pages[page, h, t % ps]``, ``v_t`` likewise);
+* with ``causal`` a key is alive only if ``t <= limit(q)``, the right-aligned
+  limit the query-outer oracle uses;
+* for GQA lane ``qh`` (query head ``h*qhead + qh``) the scores over the alive
+  keys are ``s_t = dot(q, k_t) * scale``; then ``m = max s_t``,
+  ``l = sum exp(s_t - m)`` and ``o = sum exp(s_t - m) v_t`` (not normalised).
+  No alive key gives ``(o, m, l) = (0, -inf, 0)``.
 
-Partial ``(e, qh)`` sits at row ``e * qhead + qh`` (``ForwardPartials::partial_index``).
+Hence ``o / l`` is softmax attention over that block alone and ``m + log l``
+its log-sum-exp. Row ``e * qhead + qh`` holds edge ``e``, lane ``qh``
+(``ForwardPartials``: edges in CSR order, GQA lanes inner).
 
-``combine_ref`` is this module's reading of the combine pass, which the
-pages name but do not show ("standard FlashAttention log-sum-exp update",
-``forward.rs`` module doc). For ``(q, h, qh)`` it takes every rank with
-``inv[h, q, r] >= 0``, at partial row ``(edge_head_base[h] + inv) * qhead + qh``,
-and computes ``M = max m``, ``L = sum l * exp(m - M)`` and
-``O = sum o * exp(m - M) / L``. With no finite ``m`` the result is ``O = 0``
-and ``lse = -inf``; otherwise ``lse = M + log L``.
+``combine_ref`` is this package's reading of the combine pass, which the
+forward.rs module doc names but does not show: the log-sum-exp merge that
+FlashAttention uses to join the softmax of separate key blocks. For
+``(q, h, qh)`` it takes every rank with ``inv[h, q, r] >= 0``, at partial row
+``(edge_head_base[h] + inv) * qhead + qh``, and computes ``M = max m``,
+``L = sum l * exp(m - M)`` and ``O = sum o * exp(m - M) / L``. With no finite
+``m`` the result is ``O = 0`` and ``lse = -inf``; otherwise ``lse = M + log L``.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .errors import SparseAttentionError
-from .index_ref import batch_of
+from .attention_ref import causal_limit
+from .index_ref import batch_of, resolve_kv_lens
 
 
-def forward_partials_ref(q, k_pages, v_pages, index, block_tables, cu_seqlens_q,
+def block_keys(tbl_row, v, lk_b, block_size, page_size):
+    """Positions of block ``v`` below ``lk_b`` that sit on a page, with their
+    pages: ``(t [n], page [n])``."""
+    lo = v * block_size
+    hi = min(lo + block_size, lk_b)
+    t = np.arange(lo, hi) if hi > lo else np.zeros(0, dtype=np.int64)
+    pages = tbl_row[t // page_size] if t.size else np.zeros(0, dtype=np.int64)
+    keep = pages >= 0
+    return t[keep], pages[keep]
+
+
+def partial_over_keys(lanes, k, v, alive, scale):
+    """``(o [qhead, d], m [qhead], l [qhead])`` over the keys where ``alive``:
+    ``m`` the largest score, ``l`` and ``o`` the sums of ``exp(s - m)`` and of
+    ``exp(s - m) v``."""
+    qhead, d = lanes.shape
+    if not alive.any():
+        return np.zeros((qhead, d)), np.full(qhead, -np.inf), np.zeros(qhead)
+    s = (lanes @ k[alive].T) * scale                     # [qhead, n_alive]
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    return p @ v[alive], m, p.sum(axis=1)
+
+
+def forward_partials_ref(q, k_pages, v_pages, selected, index, block_tables, cu_seqlens_q,
                          used_kv_lens, hq, hkv, head_dim, block_size, page_size,
                          softmax_scale, causal, only_edges=None):
-    """Return ``(o [E*qhead, d], m [E*qhead], l [E*qhead])`` in float64.
+    """Partials of the index's edges, in float64.
 
-    ``only_edges`` (a set of edge positions) restricts the work to those
-    edges; the other rows keep their initial ``(0, -inf, 0)``."""
+    Returns ``(o [E*qhead, d], m [E*qhead], l [E*qhead])`` with row
+    ``e*qhead + qh``. With ``only_edges`` (a sequence of edge positions) the
+    rows are those edges' only, in the order given: ``[len*qhead, ...]``."""
     qhead = hq // hkv
-    ppb = block_size // page_size
-    msb = index["msb"]
     cu = np.asarray(cu_seqlens_q, dtype=np.int64).ravel()
     batch = cu.shape[0] - 1
     tbl = np.asarray(block_tables, dtype=np.int64).reshape(batch, -1)
+    msb = tbl.shape[1] // (block_size // page_size)
     tq = int(cu[-1])
+    topk = np.asarray(selected).size // max(tq * hkv, 1)
+    sel = np.asarray(selected, dtype=np.int64).reshape(tq, hkv, topk)
     num_pages = np.asarray(k_pages).size // (hkv * page_size * head_dim)
     qv = np.asarray(q, dtype=np.float32).reshape(tq, hq, head_dim)
     kp = np.asarray(k_pages, dtype=np.float32).reshape(num_pages, hkv, page_size, head_dim)
     vp = np.asarray(v_pages, dtype=np.float32).reshape(num_pages, hkv, page_size, head_dim)
     scale = float(np.float32(softmax_scale))
-    edges = index["edges"]
+    lk = resolve_kv_lens(used_kv_lens, batch, msb, block_size)
+    edges = np.asarray(index["edges"])
+    base = np.asarray(index["edge_head_base"], dtype=np.int64)
     n_edges = edges.shape[0]
-    o = np.zeros((n_edges * qhead, head_dim), dtype=np.float64)
-    m = np.full(n_edges * qhead, -np.inf, dtype=np.float64)
-    l = np.zeros(n_edges * qhead, dtype=np.float64)
+    wanted = np.arange(n_edges) if only_edges is None else np.asarray(only_edges, dtype=np.int64)
 
-    for h in range(hkv):
-        head_base = int(index["edge_head_base"][h])
-        for j in range(int(index["num_sel"][h])):
-            if only_edges is not None:
-                lo = head_base + int(index["sel_offsets"][h, j])
-                hi = head_base + int(index["sel_offsets"][h, j + 1])
-                if not any(lo <= e < hi for e in only_edges):
-                    continue
-            raw = int(index["sel_slots"][h, j])
-            b, blk = raw // msb, raw % msb
-            lk = (msb * block_size if used_kv_lens is None
-                  else max(int(np.asarray(used_kv_lens).ravel()[b]), 0))
-            block_start = blk * block_size
-            block_end = min((blk + 1) * block_size, lk)
-            if block_end <= block_start:
-                continue
+    o = np.zeros((wanted.shape[0] * qhead, head_dim), dtype=np.float64)
+    m = np.full(wanted.shape[0] * qhead, -np.inf, dtype=np.float64)
+    l = np.zeros(wanted.shape[0] * qhead, dtype=np.float64)
+    for n, e in enumerate(wanted.tolist()):
+        h = int(np.searchsorted(base, e, side="right") - 1)     # head whose range holds e
+        qi, r = int(edges[e, 0]), int(edges[e, 1])
+        v = int(sel[qi, h, r])
+        b = int(batch_of(cu, qi))
+        t, pages = block_keys(tbl[b], v, int(lk[b]), block_size, page_size)
+        alive = np.ones(t.shape[0], dtype=bool)
+        if causal:
             qo_len = int(cu[b + 1] - cu[b])
-            k_rows, v_rows, positions = [], [], []
-            for pl in range(ppb):
-                page_seq_start = blk * block_size + pl * page_size
-                lo = max(block_start, page_seq_start)
-                hi = min(block_end, page_seq_start + page_size)
-                if hi <= lo:
-                    continue
-                page = int(tbl[b, blk * ppb + pl])
-                if page < 0:
-                    continue
-                if page >= num_pages:
-                    raise SparseAttentionError("ShapeMismatch", "block_tables page id",
-                                               num_pages, page)
-                for pos in range(lo - page_seq_start, hi - page_seq_start):
-                    k_rows.append(kp[page, h, pos])
-                    v_rows.append(vp[page, h, pos])
-                    positions.append(page_seq_start + pos)
-            if not positions:
-                continue
-            kb = np.asarray(k_rows, dtype=np.float64)
-            vb = np.asarray(v_rows, dtype=np.float64)
-            pos_arr = np.asarray(positions)
-            e0 = head_base + int(index["sel_offsets"][h, j])
-            e1 = head_base + int(index["sel_offsets"][h, j + 1])
-            for e in range(e0, e1):
-                if only_edges is not None and e not in only_edges:
-                    continue
-                qi = int(edges[e, 0])
-                alive = np.ones(pos_arr.shape[0], dtype=bool)
-                if causal:
-                    q_local = qi - int(cu[int(batch_of(cu, qi))])
-                    limit = lk - qo_len + q_local if lk >= qo_len else q_local
-                    alive = pos_arr <= limit
-                for qh in range(qhead):
-                    row = e * qhead + qh
-                    qvec = qv[qi, h * qhead + qh].astype(np.float64)
-                    s = np.where(alive, (kb @ qvec) * scale, -np.inf)
-                    mx = s.max()
-                    if not np.isfinite(mx):
-                        continue                      # (o=0, m=-inf, l=0)
-                    p = np.where(alive, np.exp(s - mx), 0.0)
-                    m[row] = mx
-                    l[row] = p.sum()
-                    o[row] = p @ vb
+            alive = t <= causal_limit(int(lk[b]), qo_len, qi - int(cu[b]))
+        k_rows = kp[pages, h, t % page_size, :].astype(np.float64)
+        v_rows = vp[pages, h, t % page_size, :].astype(np.float64)
+        lanes = qv[qi, h * qhead:(h + 1) * qhead, :].astype(np.float64)
+        oe, me, le = partial_over_keys(lanes, k_rows, v_rows, alive, scale)
+        rows = slice(n * qhead, (n + 1) * qhead)
+        o[rows], m[rows], l[rows] = oe, me, le
     return o, m, l
 
 
@@ -127,7 +116,6 @@ def combine_ref(index, o_partial, m_partial, l_partial, hq, head_dim):
     """Log-sum-exp merge of the partials into ``(O [tq, hq, d], lse [tq, hq])``."""
     hkv = index["hkv"]
     tq = index["tq"]
-    topk = index["topk"]
     qhead = hq // hkv
     inv = index["inv"]
     base = index["edge_head_base"]

@@ -19,15 +19,13 @@ import torch
 import block_sparse_paged_csr_amd as sa
 import oracle
 import workloads as W
-from _gpu import (assert_index_equal, check_units, dev_inputs, max_rel_err, oracle_index,
-                  run_attention, run_index)
+from _gpu import (assert_index_equal, check_partials, check_units, dev_inputs, max_rel_err,
+                  oracle_index, qo_sampled, run_attention, run_index, sample_edges)
 
 pytestmark = pytest.mark.gpu
 
 TOL_O = 1e-4          # max|O_gpu - O_ref| / max|O_ref|
 TOL_LSE = 1e-4        # absolute, natural-log units
-TOL_M = 1e-5          # partial max, absolute (scores are O(1))
-TOL_OL = 1e-5         # partial o and l, relative to the largest magnitude
 
 
 def _qo(w, queries=None):
@@ -41,8 +39,12 @@ def _print_case(case, **kw):
     print(f"[gpu case] {case} {kw}", flush=True)
 
 
-def _check_output(w, out, lse, queries=None):
-    ref_o, ref_lse = _qo(w, queries)
+def _check_output(w, out, lse, queries=None, parallel=False):
+    if parallel:
+        qs = np.arange(w.tq) if queries is None else queries
+        ref_o, ref_lse = qo_sampled(w, qs, workers=8)
+    else:
+        ref_o, ref_lse = _qo(w, queries)
     got_o = out.cpu().numpy().astype(np.float64)
     got_lse = lse.cpu().numpy().astype(np.float64)
     if queries is not None:
@@ -218,33 +220,47 @@ def test_random_d128_wide_gqa_mfma_units(seed):
     _check_output(w, out, lse)
 
 
-@pytest.mark.parametrize("seed", range(8))
-def test_random_partials_match_kvouter_ref(seed):
-    w = W.make_random(700 + seed, batch=2, qo_max=4, kv_max=48, hkv=2, qhead=1 + seed % 3,
-                      head_dim=32, page_size=2, pages_per_block=2 + seed % 2, topk=3)
-    _print_case("random_partials", seed=seed)
+# Partial-level parity on every forward kernel: (o, m, l) per edge and lane
+# against the oracle, so that the reference point m (which the combine cannot
+# see) is checked on each of them.
+#   wave:   head_dim 32, the wavefront-reduction kernel
+#   small:  head_dim 128, blocks <= 64 keys, qhead <= 16: the one-wave kernel
+#   mfma16: head_dim 128, blocks <= 64 keys, qhead > 16: 16-row MFMA tiles
+#   mfma:   head_dim 128, blocks of 96 / 128 keys: 32-row MFMA tiles (slots
+#           under 32 rows take the wavefront kernel)
+PARTIAL_KERNELS = {
+    "wave": dict(head_dim=32, page_size=2, pages_per_block=(2, 3), qhead=(1, 2, 3),
+                 qo_max=4, kv_max=48, topk=3),
+    "small": dict(head_dim=128, page_size=16, pages_per_block=(1, 2, 4), qhead=(1, 4, 8, 16),
+                  qo_max=12, kv_max=300, topk=4),
+    "mfma16": dict(head_dim=128, page_size=16, pages_per_block=(2, 4), qhead=(20, 32),
+                   qo_max=40, kv_max=260, topk=3),
+    "mfma": dict(head_dim=128, page_size=32, pages_per_block=(3, 4), qhead=(4, 8, 16),
+                 qo_max=60, kv_max=600, topk=3),
+}
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kernel", list(PARTIAL_KERNELS))
+def test_random_partials_match_kvouter_ref(kernel, seed):
+    g = PARTIAL_KERNELS[kernel]
+    w = W.make_random(700 + 37 * seed + 1000 * list(PARTIAL_KERNELS).index(kernel),
+                      batch=1 + seed % 3, qo_max=g["qo_max"], kv_max=g["kv_max"],
+                      hkv=1 + seed % 2, qhead=g["qhead"][seed % len(g["qhead"])],
+                      head_dim=g["head_dim"], page_size=g["page_size"],
+                      pages_per_block=g["pages_per_block"][seed % len(g["pages_per_block"])],
+                      topk=g["topk"], causal=bool(seed % 2))
+    _print_case("random_partials", kernel=kernel, seed=seed, tq=w.tq, bs=w.block_size,
+                qhead=w.hq // w.hkv)
     d = dev_inputs(w)
     idx = run_index(w, d)
     ref = oracle_index(w)
-    assert_index_equal(idx, ref)
-    o, m, l = sa.sa_forward(idx, d["q"], d["k"], d["v"], d["bt"], d["cu"], d["used"], w.hq,
-                            w.hkv, w.head_dim, w.block_size, w.page_size, w.softmax_scale,
-                            w.causal)
-    ro, rm, rl = oracle.forward_partials_ref(w.q, w.k_pages, w.v_pages, ref, w.block_tables,
-                                             w.cu_seqlens_q, w.used_kv_lens, w.hq, w.hkv,
-                                             w.head_dim, w.block_size, w.page_size,
-                                             w.softmax_scale, w.causal)
-    rows = rm.shape[0]
-    gm = m[:rows].cpu().numpy().astype(np.float64)
-    gl = l[:rows].cpu().numpy().astype(np.float64)
-    go = o[:rows].cpu().numpy().astype(np.float64)
-    fin = np.isfinite(rm)
-    assert np.array_equal(fin, np.isfinite(gm))
-    if fin.any():
-        assert np.abs(gm[fin] - rm[fin]).max() <= TOL_M
-        assert max_rel_err(gl, rl)[0] <= TOL_OL
-        assert max_rel_err(go, ro)[0] <= TOL_OL
-    assert np.all(gl[~fin] == 0) and np.all(go[~fin] == 0)
+    info, _ = assert_index_equal(idx, ref)
+    if kernel in ("mfma16", "mfma"):
+        assert info["num_units_mfma"] > 0, "no unit reached the MFMA kernel"
+    else:
+        assert info["num_units_mfma"] == 0
+    check_partials(w, d, idx, ref)
 
 
 def test_tiny_workload():
@@ -357,19 +373,65 @@ def test_device_error_page_id(golden_dir, build_path):
                                                    case["got"])
 
 
-def test_forward_skips_on_device_error():
-    w = W.make_random(33, batch=2, hkv=1, topk=2)
+@pytest.mark.parametrize("head_dim", [32, 128])
+def test_forward_skips_on_device_error(head_dim, build_path):
+    """A build that finds an input error: sa_forward writes no partial,
+    sa_combine fills out and lse with NaN, and sa_attention raises (or, with
+    check=False, returns and leaves the status to sa_index_status)."""
+    w = W.make_random(33, batch=2, hkv=1, topk=2, head_dim=head_dim)
+    _print_case("device_error_outputs", d=head_dim, build=build_path)
     d = dev_inputs(w)
     sel = w.selected.copy()
     sel.reshape(-1)[0] = 10 ** 6
     d["sel"] = torch.from_numpy(sel).cuda()
     out = torch.full((w.tq, w.hq, w.head_dim), 7.0, device="cuda")
-    o, lse, idx = sa.sa_attention(d["q"], d["k"], d["v"], d["sel"], d["bt"], d["cu"], d["used"],
-                                  w.block_size, w.softmax_scale, w.causal, out=out,
-                                  return_index=True)
-    with pytest.raises(sa.SaError):
+    lse = torch.full((w.tq, w.hq), 7.0, device="cuda")
+    o, l_, idx = sa.sa_attention(d["q"], d["k"], d["v"], d["sel"], d["bt"], d["cu"], d["used"],
+                                 w.block_size, w.softmax_scale, w.causal, out=out, lse=lse,
+                                 return_index=True, check=False)
+    with pytest.raises(sa.SaError) as ei:
         sa.sa_index_status(idx)
-    assert torch.all(out == 7.0)                  # nothing written
+    assert ei.value.kind == "SelectedOutOfRange"
+    assert torch.all(torch.isnan(out)) and torch.all(torch.isnan(lse))
+    rows = idx.c.max_edges * (w.hq // w.hkv)
+    o_p = torch.full((rows, w.head_dim), 5.0, device="cuda")
+    m_p = torch.full((rows,), 5.0, device="cuda")
+    l_p = torch.full((rows,), 5.0, device="cuda")
+    sa.sa_forward(idx, d["q"], d["k"], d["v"], d["bt"], d["cu"], d["used"], w.hq, w.hkv,
+                  w.head_dim, w.block_size, w.page_size, w.softmax_scale, w.causal, o_p, m_p, l_p)
+    torch.cuda.synchronize()
+    assert torch.all(o_p == 5.0) and torch.all(m_p == 5.0) and torch.all(l_p == 5.0)
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_attention(d["q"], d["k"], d["v"], d["sel"], d["bt"], d["cu"], d["used"],
+                        w.block_size, w.softmax_scale, w.causal)
+    assert ei.value.kind == "SelectedOutOfRange"
+
+
+def test_rank_skipped_on_bad_cu_total(monkeypatch):
+    """cu_seqlens_q whose total is below tq, on the multi-kernel build with a
+    slot of 900 keys (the rank kernel's bitmap path): the status is the
+    ShapeMismatch "cu_seqlens_q total", and the build writes inside its buffer
+    only (a guard region after the index buffer stays untouched)."""
+    monkeypatch.setenv("SA_BUILD_MULTIKERNEL", "1")
+    batch, tq, topk, hkv, d = 2, 1000, 16, 1, 16
+    ps, bs, max_pages = 16, 16, 64
+    _print_case("rank_bad_cu_total", tq=tq, topk=topk)
+    sel = torch.full((tq, hkv, topk), -1, dtype=torch.int32, device="cuda")
+    sel[:, :, 0] = 0                                  # every query picks block 0
+    bt = torch.arange(batch * max_pages, dtype=torch.int32, device="cuda").reshape(batch, max_pages)
+    cu = torch.tensor([0, 100, 200], dtype=torch.int64, device="cuda")
+    idx = sa.sa_index_plan(tq, hkv, topk, batch, max_pages, bs, ps, hkv, d, batch * max_pages)
+    raw = torch.full((idx.c.index_bytes + 256 + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
+    off = (-raw.data_ptr()) % 256
+    idx.buffer = raw[off:off + idx.c.index_bytes]
+    idx.c.buffer = idx.buffer.data_ptr()
+    sa.sa_build_index(sel, bt, cu, None, idx)
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_index_status(idx)
+    e = ei.value
+    assert (e.kind, e.what, e.expected, e.got) == ("ShapeMismatch", "cu_seqlens_q total", tq, 200)
+    guard = raw[off + idx.c.index_bytes:]
+    assert torch.all(guard == 0xAB)
 
 
 # ------------------------------------------------------------------ empty inputs
@@ -411,9 +473,15 @@ def _sample_queries(w, n, seed=0):
     return np.asarray(sorted(picks))
 
 
-@pytest.mark.parametrize("name,n_sample", [("decode", None), ("ragged", 48),
-                                           ("prefill", 24), ("skewed", 16)])
+@pytest.mark.parametrize("name,n_sample", [("decode", None), ("ragged", 128),
+                                           ("prefill", 128), ("skewed", 128)])
 def test_full_size_workload(name, n_sample):
+    """A full-size workload in the launch configuration the benchmark times:
+    the index in full; the partials of sampled edges (the hottest and the
+    smallest slot of each head, unit boundaries, random edges) against the
+    oracle; the output on every query (decode) or on n_sample random queries
+    plus the first and last query of each sequence, the oracle's rows computed
+    in parallel worker processes."""
     _print_case("full_size", name=name)
     w = W.make_config(name)
     d = dev_inputs(w)
@@ -421,11 +489,15 @@ def test_full_size_workload(name, n_sample):
     ref = oracle_index(w)
     info, arrs = assert_index_equal(idx, ref)
     check_units(arrs, info, ref, idx.c.cap_edges, w)
+    edges = sample_edges(ref, arrs, info)
+    perr = check_partials(w, d, idx, ref, only_edges=edges)
+    print(f"[gpu case] {name}: partials of {len(edges)} edges: {perr}", flush=True)
     out, lse = run_attention(w, d)
     torch.cuda.synchronize()
     queries = None if n_sample is None else _sample_queries(w, n_sample)
-    err = _check_output(w, out, lse, queries)
-    print(f"[gpu case] {name}: O rel err {err:.3e}", flush=True)
+    err = _check_output(w, out, lse, queries, parallel=True)
+    print(f"[gpu case] {name}: O rel err {err:.3e} over "
+          f"{w.tq if queries is None else len(queries)} queries", flush=True)
 
 
 # The one-kernel build at the edges of its own paths: the batch-of-query

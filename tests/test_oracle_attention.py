@@ -44,7 +44,7 @@ def ko(w):
     idx = build_index_ref(w.selected, w.tq, w.hkv, w.topk, w.block_tables, w.batch,
                           w.max_pages, w.cu_seqlens_q, w.used_kv_lens, w.block_size,
                           w.page_size, w.num_pages)
-    o, m, l = forward_partials_ref(w.q, w.k_pages, w.v_pages, idx, w.block_tables,
+    o, m, l = forward_partials_ref(w.q, w.k_pages, w.v_pages, w.selected, idx, w.block_tables,
                                    w.cu_seqlens_q, w.used_kv_lens, w.hq, w.hkv,
                                    w.head_dim, w.block_size, w.page_size,
                                    w.softmax_scale, w.causal)
