@@ -100,6 +100,9 @@ def _declare(lib):
         "sa_attention": [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64,
                          i64, i32, i32, i32, i32, i32, i32, i32, i32, c_float, i32,
                          vp, sz, vp, vp, idxp, vp],
+        "sa_attention_noalloc": [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                                 i64, i32, i32, i32, i32, i32, i32, i32, i32, c_float, i32,
+                                 vp, vp, idxp, vp],
         "sa_last_error": [POINTER(SaErrorDetail)],
         "sa_status_string": [c_int32],
     }
@@ -371,6 +374,45 @@ def sa_attention(q, k_pages, v_pages, selected, block_tables, cu_seqlens_q, used
     return out, lse
 
 
+SA_NOALLOC_SCRATCH_BYTES = 32 << 20     # include/sa.h
+
+
+def sa_attention_noalloc(q, k_pages, v_pages, selected, block_tables, cu_seqlens_q,
+                         used_kv_lens, block_size, softmax_scale, causal, out, lse=None, *,
+                         tq=None, check=False, return_index=False):
+    """sa_attention with the library's own per-GPU workspace: the C call
+    allocates nothing, and neither does this wrapper (``out`` is required and
+    ``lse`` optional, both caller tensors). Calls on one GPU share the
+    workspace and must not overlap. ``check`` reads the build's status
+    (a host wait) and raises ``SaError`` on a device-side input error."""
+    _check_head_dims(q, k_pages, v_pages)
+    if tq is None:
+        tq = q.shape[0]
+    hq = q.shape[1] if q.dim() == 3 else 0
+    hkv, page_size, head_dim = k_pages.shape[1], k_pages.shape[2], k_pages.shape[3]
+    topk = selected.shape[-1]
+    batch, max_pages = block_tables.shape
+    c = SaIndex()
+    st = lib().sa_attention_noalloc(
+        _ptr(q, torch.float32, "q"), q.numel(),
+        _ptr(k_pages, torch.float32, "k_pages"), k_pages.numel(),
+        _ptr(v_pages, torch.float32, "v_pages"), v_pages.numel(),
+        _ptr(selected, torch.int32, "selected"), selected.numel(),
+        _ptr(block_tables, torch.int32, "block_tables"), block_tables.numel(),
+        _ptr(cu_seqlens_q, torch.int64, "cu_seqlens_q"), cu_seqlens_q.numel(),
+        _ptr(used_kv_lens, torch.int32, "used_kv_lens"),
+        0 if used_kv_lens is None else used_kv_lens.numel(),
+        tq, hq, hkv, head_dim, topk, batch, max_pages, block_size, page_size,
+        float(softmax_scale), int(bool(causal)),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), ctypes.byref(c),
+        _stream(q.device))
+    _check(st)
+    index = Index(c, None)
+    if check:
+        sa_index_status(index, check=True, device=q.device)
+    return (out, lse, index) if return_index else (out, lse)
+
+
 def index_arrays(index: Index, info: dict | None = None) -> dict:
     """Views of the index arrays inside its device buffer (for tests and
     external consumers). ``edges`` and ``units`` are trimmed to the device
@@ -409,5 +451,6 @@ __all__ = [
     "SaError", "SaIndex", "Index", "Workspace", "lib", "sa_index_plan", "sa_build_index",
     "sa_index_status", "sa_forward", "sa_forward_kv16", "sa_combine", "sa_attention",
     "SA_KV_F32", "SA_KV_BF16", "SA_KV_F16",
-    "sa_attention_workspace_bytes", "index_arrays", "STATUS_NAMES",
+    "sa_attention_workspace_bytes", "sa_attention_noalloc", "SA_NOALLOC_SCRATCH_BYTES",
+    "index_arrays", "STATUS_NAMES",
 ]

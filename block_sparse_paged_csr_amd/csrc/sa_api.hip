@@ -7,6 +7,7 @@
 #include <climits>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sa_internal.h"
 
@@ -377,6 +378,15 @@ sa_status forward_common(const sa_index* idx, const float* q, int64_t q_len, con
   return ok();
 }
 
+// sa_attention's host checks, in its order (the forward's, then the
+// build's, then the plan's): fills the plan and the workspace size.
+sa_status attention_host_checks(int64_t q_len, int64_t k_len, int64_t v_len,
+                                int64_t selected_len, int64_t block_tables_len, int64_t cu_len,
+                                const int32_t* used_kv_lens, int64_t used_len, int64_t tq,
+                                int32_t hq, int32_t hkv, int32_t head_dim, int32_t topk,
+                                int32_t batch, int32_t max_pages, int32_t block_size,
+                                int32_t page_size, sa_index* idx, size_t* need);
+
 }  // namespace
 
 extern "C" {
@@ -445,16 +455,16 @@ sa_status sa_attention_workspace_bytes(int64_t tq, int32_t hkv, int32_t topk, in
   return ok();
 }
 
-sa_status sa_attention(const float* q, int64_t q_len, const float* k_pages, int64_t k_len,
-                       const float* v_pages, int64_t v_len, const int32_t* selected,
-                       int64_t selected_len,
-                       const int32_t* block_tables, int64_t block_tables_len,
-                       const int64_t* cu_seqlens_q, int64_t cu_len, const int32_t* used_kv_lens,
-                       int64_t used_len, int64_t tq, int32_t hq, int32_t hkv, int32_t head_dim,
-                       int32_t topk, int32_t batch, int32_t max_pages, int32_t block_size,
-                       int32_t page_size, float softmax_scale, int32_t causal, void* workspace,
-                       size_t workspace_bytes, float* out, float* lse, sa_index* idx_out,
-                       hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+sa_status attention_host_checks(int64_t q_len, int64_t k_len, int64_t v_len,
+                                int64_t selected_len, int64_t block_tables_len, int64_t cu_len,
+                                const int32_t* used_kv_lens, int64_t used_len, int64_t tq,
+                                int32_t hq, int32_t hkv, int32_t head_dim, int32_t topk,
+                                int32_t batch, int32_t max_pages, int32_t block_size,
+                                int32_t page_size, sa_index* idx, size_t* need) {
   sa_status st = check_heads_blocks(hq, hkv, head_dim, block_size, page_size);
   if (st != SA_OK) return st;
   st = check_build_lengths(selected_len, block_tables_len, cu_len, used_kv_lens, used_len, tq,
@@ -466,13 +476,34 @@ sa_status sa_attention(const float* q, int64_t q_len, const float* k_pages, int6
   if (k_len % page_stride != 0 || v_len != k_len)
     return fail(SA_ERR_SHAPE, "k_pages / v_pages page stride", page_stride, k_len);
   const int64_t num_pages = k_len / page_stride;
-  sa_index idx;
   st = sa_index_plan(tq, hkv, topk, batch, max_pages, block_size, page_size, hq, head_dim,
-                     num_pages, &idx);
+                     num_pages, idx);
   if (st != SA_OK) return st;
+  return sa_attention_workspace_bytes(tq, hkv, topk, batch, max_pages, block_size, page_size,
+                                      hq, head_dim, need);
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_attention(const float* q, int64_t q_len, const float* k_pages, int64_t k_len,
+                       const float* v_pages, int64_t v_len, const int32_t* selected,
+                       int64_t selected_len,
+                       const int32_t* block_tables, int64_t block_tables_len,
+                       const int64_t* cu_seqlens_q, int64_t cu_len, const int32_t* used_kv_lens,
+                       int64_t used_len, int64_t tq, int32_t hq, int32_t hkv, int32_t head_dim,
+                       int32_t topk, int32_t batch, int32_t max_pages, int32_t block_size,
+                       int32_t page_size, float softmax_scale, int32_t causal, void* workspace,
+                       size_t workspace_bytes, float* out, float* lse, sa_index* idx_out,
+                       hipStream_t stream) {
+  sa_index idx;
   size_t need = 0;
-  sa_attention_workspace_bytes(tq, hkv, topk, batch, max_pages, block_size, page_size, hq,
-                               head_dim, &need);
+  sa_status st = attention_host_checks(q_len, k_len, v_len, selected_len, block_tables_len,
+                                       cu_len, used_kv_lens, used_len, tq, hq, hkv, head_dim,
+                                       topk, batch, max_pages, block_size, page_size, &idx,
+                                       &need);
+  if (st != SA_OK) return st;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0 ||
       workspace_bytes < need)
     return fail(SA_ERR_SHAPE, "workspace", (int64_t)need, (int64_t)workspace_bytes);
@@ -496,6 +527,82 @@ sa_status sa_attention(const float* q, int64_t q_len, const float* k_pages, int6
   if (st != SA_OK) return st;
   if (idx_out) *idx_out = idx;
   return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free entry
+// Workspace of sa_attention_noalloc: a file-scope device array that the code
+// object's loader places on every GPU the library runs on (each GPU has its
+// own copy at its own address). In host code `scratch` names a host-side
+// stand-in, never the device memory: every host use goes through the device
+// address that hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (first call on a device:
+// looked up with that device current), or null with the failure recorded.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    fail(SA_ERR_GPU_INIT, "no HIP device");
+    return nullptr;
+  }
+  if (dev >= kMaxDevices) {
+    fail(SA_ERR_UNSUPPORTED, "device ordinal", kMaxDevices, dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      runtime_error(e, "scratch symbol address");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_attention_noalloc(const float* q, int64_t q_len, const float* k_pages,
+                               int64_t k_len, const float* v_pages, int64_t v_len,
+                               const int32_t* selected, int64_t selected_len,
+                               const int32_t* block_tables, int64_t block_tables_len,
+                               const int64_t* cu_seqlens_q, int64_t cu_len,
+                               const int32_t* used_kv_lens, int64_t used_len, int64_t tq,
+                               int32_t hq, int32_t hkv, int32_t head_dim, int32_t topk,
+                               int32_t batch, int32_t max_pages, int32_t block_size,
+                               int32_t page_size, float softmax_scale, int32_t causal,
+                               float* out, float* lse, sa_index* idx_out,
+                               hipStream_t stream) {
+  // the host checks of sa_attention come first, in its order
+  sa_index plan;
+  size_t need = 0;
+  sa_status st = attention_host_checks(q_len, k_len, v_len, selected_len, block_tables_len,
+                                       cu_len, used_kv_lens, used_len, tq, hq, hkv, head_dim,
+                                       topk, batch, max_pages, block_size, page_size, &plan,
+                                       &need);
+  if (st != SA_OK) return st;
+  if (need > (size_t)SA_NOALLOC_SCRATCH_BYTES)
+    return fail(SA_ERR_UNSUPPORTED, "workspace exceeds the no-alloc scratch",
+                (int64_t)SA_NOALLOC_SCRATCH_BYTES, (int64_t)need);
+  void* ws = scratch_for_current_device();
+  if (ws == nullptr) return (sa_status)g_last.status;
+  return sa_attention(q, q_len, k_pages, k_len, v_pages, v_len, selected, selected_len,
+                      block_tables, block_tables_len, cu_seqlens_q, cu_len, used_kv_lens,
+                      used_len, tq, hq, hkv, head_dim, topk, batch, max_pages, block_size,
+                      page_size, softmax_scale, causal, ws, (size_t)SA_NOALLOC_SCRATCH_BYTES,
+                      out, lse, idx_out, stream);
 }
 
 }  // extern "C"

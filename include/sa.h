@@ -271,6 +271,39 @@ sa_status sa_attention(const float* q, int64_t q_len,
                        float* out, float* lse,
                        sa_index* idx_out, hipStream_t stream);
 
+/* Size of the library's own workspace for sa_attention_noalloc (bytes, per
+ * GPU). */
+#define SA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* sa_attention_noalloc: sa_attention without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc). The index and the
+ * partials live in a device array of SA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends. The first
+ * call on a GPU looks the array up there (the runtime then loads it with the
+ * library's device code for that GPU); no call allocates anything. Arguments, outputs, host checks (in
+ * sa_attention's order) and the device-side error behaviour are
+ * sa_attention's. Then SA_ERR_UNSUPPORTED "workspace exceeds the no-alloc
+ * scratch" (expected = the limit, got = sa_attention_workspace_bytes) when
+ * the problem needs more than the array holds. Every call on one GPU uses
+ * the same array and leaves its contents there; calls that overlap on one
+ * GPU (several streams or host threads) race, so serialise them. `idx_out`
+ * (host, may be NULL) receives the index handle, whose buffer is that array,
+ * valid until the next call on the same GPU. */
+sa_status sa_attention_noalloc(const float* q, int64_t q_len,
+                               const float* k_pages, int64_t k_len,
+                               const float* v_pages, int64_t v_len,
+                               const int32_t* selected, int64_t selected_len,
+                               const int32_t* block_tables, int64_t block_tables_len,
+                               const int64_t* cu_seqlens_q, int64_t cu_len,
+                               const int32_t* used_kv_lens, int64_t used_len,
+                               int64_t tq, int32_t hq, int32_t hkv, int32_t head_dim,
+                               int32_t topk, int32_t batch, int32_t max_pages,
+                               int32_t block_size, int32_t page_size,
+                               float softmax_scale, int32_t causal,
+                               float* out, float* lse,
+                               sa_index* idx_out, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* sa_status_string(sa_status status);
 

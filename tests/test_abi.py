@@ -79,16 +79,23 @@ def test_plan_errors():
 
 
 def _abi_attention_error(q_len, k_len, v_len, sel_len, tbl_len, cu_len, used_len, tq, hq, hkv,
-                         d, topk, batch, max_pages, bs, ps):
-    """Call sa_attention with null device pointers; only host checks can run."""
+                         d, topk, batch, max_pages, bs, ps, noalloc=False):
+    """Call sa_attention (or sa_attention_noalloc) with null device pointers;
+    only host checks can run."""
     lib = sa.lib()
     dummy = ctypes.c_void_p(0x1000)                 # never dereferenced by host checks
     used_ptr = None if used_len is None else dummy
     c = sa.SaIndex()
-    st = lib.sa_attention(dummy, q_len, dummy, k_len, dummy, v_len, dummy, sel_len, dummy,
-                          tbl_len, dummy, cu_len, used_ptr, used_len or 0, tq, hq, hkv, d, topk,
-                          batch, max_pages, bs, ps, 0.5, 1, None, 0, dummy, None,
-                          ctypes.byref(c), None)
+    if noalloc:
+        st = lib.sa_attention_noalloc(dummy, q_len, dummy, k_len, dummy, v_len, dummy, sel_len,
+                                      dummy, tbl_len, dummy, cu_len, used_ptr, used_len or 0, tq,
+                                      hq, hkv, d, topk, batch, max_pages, bs, ps, 0.5, 1, dummy,
+                                      None, ctypes.byref(c), None)
+    else:
+        st = lib.sa_attention(dummy, q_len, dummy, k_len, dummy, v_len, dummy, sel_len, dummy,
+                              tbl_len, dummy, cu_len, used_ptr, used_len or 0, tq, hq, hkv, d,
+                              topk, batch, max_pages, bs, ps, 0.5, 1, None, 0, dummy, None,
+                              ctypes.byref(c), None)
     assert st != 0
     det = sa.SaErrorDetail()
     lib.sa_last_error(ctypes.byref(det))
@@ -120,8 +127,9 @@ def _cases():
     return w, base, cases
 
 
+@pytest.mark.parametrize("noalloc", [False, True])
 @pytest.mark.parametrize("case", list(_cases()[2].keys()))
-def test_host_error_order_matches_oracle(case):
+def test_host_error_order_matches_oracle(case, noalloc):
     w, base, cases = _cases()
     a = dict(base, **cases[case])
     tq = int(np.asarray(a["cu"])[-1]) if np.asarray(a["cu"]).size else 0
@@ -137,12 +145,33 @@ def test_host_error_order_matches_oracle(case):
                                np.asarray(a["cu"]).size,
                                None if a["used"] is None else np.asarray(a["used"]).size,
                                tq, a["hq"], a["hkv"], a["d"], topk, batch, max_pages, a["bs"],
-                               a["ps"])
+                               a["ps"], noalloc=noalloc)
     assert got[0] == ref.kind, (got, ref)
     if ref.kind == "ShapeMismatch":
         assert got[1:] == (ref.what, ref.expected, ref.got)
     if ref.kind in ("HeadCountMismatch", "BlockPageMismatch"):
         assert got[2:] == (ref.expected, ref.got)
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    # decode-sized problems fit; prefill-sized ones need more than the
+    # library's 32 MiB array and fail on the host, before any device call
+    for name, fits in (("decode", True), ("prefill", False)):
+        w = W.make_config(name, with_kv=False)
+        need = sa.sa_attention_workspace_bytes(w.tq, w.hkv, w.topk, w.batch, w.max_pages,
+                                               w.block_size, w.page_size, w.hq, w.head_dim)
+        assert (need <= sa.SA_NOALLOC_SCRATCH_BYTES) == fits
+    w = W.make_config("prefill", with_kv=False)
+    page = w.hkv * w.page_size * w.head_dim
+    got = _abi_attention_error(w.tq * w.hq * w.head_dim, page * 4, page * 4, w.selected.size,
+                               w.block_tables.size, w.batch + 1, w.batch, w.tq, w.hq, w.hkv,
+                               w.head_dim, w.topk, w.batch, w.max_pages, w.block_size,
+                               w.page_size, noalloc=True)
+    assert got[:3] == ("Unsupported", "workspace exceeds the no-alloc scratch",
+                       sa.SA_NOALLOC_SCRATCH_BYTES)
+    assert got[3] == need
+    with open(os.path.join(ROOT, "include", "sa.h")) as f:
+        assert "#define SA_NOALLOC_SCRATCH_BYTES (32u << 20)" in f.read()
 
 
 def test_missing_gpu_tensors_fail_loudly():
