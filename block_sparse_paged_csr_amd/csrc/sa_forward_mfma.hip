@@ -47,15 +47,26 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kMaxUnitEdges = kCapUnitEdges;
 
 // NKB: 32-key blocks per KV block (block_size <= 32 * NKB); WAVES per workgroup.
+//
+// Each wave runs its tiles as a software pipeline so that the matrix pipe is
+// not left waiting on memory: the unit's query ids sit in LDS, and the next
+// tile's q rows (scaled by softmax_scale * log2 e as they load) are fetched
+// right after the current tile's QK products have read theirs, so their
+// round trip overlaps the softmax and the PV products. The LDS operands of
+// each group of matrix instructions are read one group ahead.
 template <int NKB, int WAVES, int KVF>
 __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
   constexpr int kWaves = WAVES;
   constexpr int kThreads = WAVES * 64;
   constexpr int kKeys = NKB * 32;
+  constexpr int kIters = kKeys * (kD / 4) / kThreads;   // gather float4 per thread (K and V each)
+  static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
+  static_assert(kThreads % (kD / 4) == 0, "a thread gathers one column of its keys");
   __shared__ __align__(16) float s_k[kKeys * kKPitch];
   __shared__ __align__(16) float s_v[kKeys * kVPitch];
   __shared__ int64_t s_off[kKeys];
-  __shared__ int s_valid[kKeys];
+  __shared__ int32_t s_qid[kMaxUnitEdges];
+  __shared__ uint32_t s_valid[NKB];       // bit k of word kb: key kb*32 + k has a row
   __shared__ int s_unit;
 
   DevHeader* hdr = P.hdr;
@@ -69,6 +80,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
   const int lr = lane & 31, half = lane >> 5;
   const int32_t qhead = A.qhead;
   const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
+  const float c2 = A.scale_log2;
+
+  // q row of tile row `row` (lanes 0-31 take d 0..63, lanes 32-63 d 64..127).
+  // A row past the unit reads the unit's last row instead: each row's scores,
+  // probabilities and output stay in that row's own lanes and such rows are
+  // never stored, so the loads need no branch and no select, and the compiler
+  // waits for them only where the QK products use them. The float4 groups
+  // [i0, i0 + 8) of the row are loaded.
+  auto q_row = [&](const Unit& U, int32_t rows, int32_t tile, int32_t* qi_out) -> const float* {
+    int32_t row = tile * 32 + lr;
+    row = row < rows ? row : rows - 1;
+    const int32_t qi = s_qid[row / qhead];
+    *qi_out = qi;
+    return A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + row % qhead) * kD + half * 64;
+  };
+  auto load_q8 = [&](const float* qp, int i0, float4 (&qr)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+  };
 
   for (int32_t u = blockIdx.x;;) {
     if (u >= num_units) break;
@@ -80,8 +110,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
     const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
     const int64_t bt_row = (int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb;
     const int64_t head_off = (int64_t)U.h * A.page_size * kD;
+    const int32_t n_e = U.e1 - U.e0;
+    const int32_t rows = n_e * qhead;
+    const int64_t row0 = (int64_t)U.e0 * qhead;
+    const int32_t ntiles = (rows + 31) / 32;
 
-    // ---- row offset of each key (-1: past the valid range or no page)
+    // ---- row offset of each key (-1: past the valid range or no page), the
+    // validity bits, and the query id of each edge of the unit
     for (int key = tid; key < kKeys; key += kThreads) {
       int64_t off = -1;
       if (key < nkeys) {
@@ -91,24 +126,38 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
           off = (int64_t)page * page_stride + head_off + (int64_t)(key - pgl * A.page_size) * kD;
       }
       s_off[key] = off;
-      s_valid[key] = off >= 0;
+      const uint64_t bits = __ballot(off >= 0);
+      if ((lane & 31) == 0) s_valid[key >> 5] = (uint32_t)(bits >> (lane & 32));
     }
+    for (int e = tid; e < n_e; e += kThreads) s_qid[e] = P.edges[2 * (int64_t)(U.e0 + e)];
     __syncthreads();
+
+    // ---- this wave's first tile: q requested now, so that it arrives while
+    // the block is gathered
+    int32_t tile = wv;
+    float4 qr[16];
+    int32_t qi = 0;
+    const float* qp = tile < ntiles ? q_row(U, rows, tile, &qi) : nullptr;
+    if (tile < ntiles) {
+      load_q8(qp, 0, qr);
+      load_q8(qp, 8, qr);
+    }
+
     // ---- gather K and V of the block into LDS (zero rows past the valid range)
     {
-      constexpr int kIters = kKeys * (kD / 4) / kThreads;
-      static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
+      const int c4 = tid % (kD / 4);
+      int64_t offs[kIters];
+#pragma unroll
+      for (int i = 0; i < kIters; ++i) offs[i] = s_off[(tid + i * kThreads) / (kD / 4)];
       float4 kv[kIters], vv[kIters];
 #pragma unroll
       for (int i = 0; i < kIters; ++i) {
-        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
-        const int64_t off = s_off[key];
-        kv[i] = off >= 0 ? load_kv4<KVF>(A.k, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        vv[i] = off >= 0 ? load_kv4<KVF>(A.v, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        kv[i] = offs[i] >= 0 ? load_kv4<KVF>(A.k, offs[i] + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vv[i] = offs[i] >= 0 ? load_kv4<KVF>(A.v, offs[i] + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int i = 0; i < kIters; ++i) {
-        const int x = tid + i * kThreads, key = x / (kD / 4), c4 = x % (kD / 4);
+        const int key = (tid + i * kThreads) / (kD / 4);
         *reinterpret_cast<float4*>(&s_k[key * kKPitch + c4 * 4]) = kv[i];
         *reinterpret_cast<float4*>(&s_v[key * kVPitch + c4 * 4]) = vv[i];
       }
@@ -116,99 +165,170 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
     __syncthreads();
 
     // Keys held by this lane in the S^T accumulators: kb*32 + 8*(r/4) + 4*half + r%4.
-    // Bit r of vm[kb] says whether that key has a page (holes are rare).
+    // Bit r of vm[kb] says whether that key has a row.
     uint32_t vm[NKB];
+    bool all_rows = true;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      vm[kb] = 0;
+      const uint32_t wbits = s_valid[kb];
+      all_rows = all_rows && wbits == 0xffffffffu;
+      uint32_t m = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        vm[kb] |= (s_valid[kb * 32 + 8 * (r / 4) + 4 * half + (r % 4)] ? 1u : 0u) << r;
+      for (int r = 0; r < 16; ++r) m |= ((wbits >> (8 * (r / 4) + 4 * half + (r % 4))) & 1u) << r;
+      vm[kb] = m;
     }
 
-    const int32_t rows = (U.e1 - U.e0) * qhead;
-    const int64_t row0 = (int64_t)U.e0 * qhead;
-    const int32_t ntiles = (rows + 31) / 32;
-    for (int32_t tile = wv; tile < ntiles; tile += kWaves) {
+    while (tile < ntiles) {
       const int32_t row = tile * 32 + lr;
       const bool row_ok = row < rows;
-      int32_t qi = 0;
-      if (row_ok) qi = P.edges[2 * (int64_t)(U.e0 + row / qhead)];
-      const float* qp = A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + (row_ok ? row % qhead : 0)) * kD + half * 64;
-      float4 qr[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        qr[i] = row_ok ? *reinterpret_cast<const float4*>(qp + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      // Key k is alive iff k < nkeys, its page exists and (causal) block_start + k
-      // <= q + delta. kmax folds the two bounds; comparisons stay 32-bit.
+      // Key k is alive iff it has a row and (causal) block_start + k <= q + delta;
+      // kmaxh folds the causal bound for this lane's keys (32-bit compares).
       int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
       klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
       const int32_t kmaxh = (int32_t)(klim < -1 ? -1 : klim) - 4 * half;
+      // every key of the tile alive for every row: the masks can be skipped
+      const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
 
-      // ---- S^T = K . Q^T over d (lanes 0-31: d 0..63, lanes 32-63: d 64..127)
+      // ---- S^T = K . Q^T over d; the K operands of each step are read one step ahead
       floatx16 sacc[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
+      float4 kc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        kc[kb] = *reinterpret_cast<const float4*>(&s_k[(kb * 32 + lr) * kKPitch + half * 64]);
+      __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
 #pragma unroll
       for (int m4 = 0; m4 < 16; ++m4) {
-        float4 kv[NKB];
+        float4 kn[NKB];
+        if (m4 < 15) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          kv[kb] = *reinterpret_cast<const float4*>(
-              &s_k[(kb * 32 + lr) * kKPitch + half * 64 + m4 * 4]);
+          for (int kb = 0; kb < NKB; ++kb)
+            kn[kb] = *reinterpret_cast<const float4*>(
+                &s_k[(kb * 32 + lr) * kKPitch + half * 64 + (m4 + 1) * 4]);
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[kb].x, qr[m4].x, sacc[kb], 0, 0, 0);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[kb].y, qr[m4].y, sacc[kb], 0, 0, 0);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[kb].z, qr[m4].z, sacc[kb], 0, 0, 0);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[kb].w, qr[m4].w, sacc[kb], 0, 0, 0);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].x, qr[m4].x, sacc[kb], 0, 0, 0);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].y, qr[m4].y, sacc[kb], 0, 0, 0);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].z, qr[m4].z, sacc[kb], 0, 0, 0);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].w, qr[m4].w, sacc[kb], 0, 0, 0);
         }
-        // bound how far LDS reads run ahead of the MFMAs that use them
-        __builtin_amdgcn_sched_barrier(0);
+        // the next step's LDS reads go out before this step's products
+        if (m4 < 15) __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0008, 4 * NKB, 0);
+        if (m4 < 15) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
+        }
       }
 
-      // ---- mask, row max and sum (base 2; the scale carries log2 e)
-      float mx = -INFINITY;
+      // ---- the first half of the next tile's q, into the registers the
+      // products above have read (the second half follows the PV products)
+      const int32_t next = tile + kWaves;
+      if (next < ntiles) {
+        qp = q_row(U, rows, next, &qi);
+        load_q8(qp, 0, qr);
+      }
+
+      // ---- mask, row max and sum. The scores are raw dot products; the
+      // largest scaled score c2*s is c2 times the largest raw score (c2 >= 0)
+      // or the smallest (c2 < 0), and p = exp2(c2*s - that), base 2 with
+      // log2 e in c2.
+      const bool up = c2 >= 0.f;
+      float ext = up ? -INFINITY : INFINITY;
+      if (full) {
+        if (up) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool alive = ((vm[kb] >> r) & 1u) && (kb * 32 + 8 * (r / 4) + (r % 4)) <= kmaxh;
-          const float s = alive ? sacc[kb][r] * A.scale_log2 : -INFINITY;
-          sacc[kb][r] = s;
-          mx = fmaxf(mx, s);
+            for (int r = 0; r < 16; ++r) ext = fmaxf(ext, sacc[kb][r]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ext = fminf(ext, sacc[kb][r]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float sum = 0.f;
+      } else {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s = sacc[kb][r];
-          const float p = (s == -INFINITY) ? 0.f : exp2f(s - mx);
-          sacc[kb][r] = p;
-          sum += p;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const bool alive = ((vm[kb] >> r) & 1u) && (kb * 32 + 8 * (r / 4) + (r % 4)) <= kmaxh;
+            ext = alive ? (up ? fmaxf(ext, sacc[kb][r]) : fminf(ext, sacc[kb][r])) : ext;
+          }
+      }
+      {
+        const float other = __shfl_xor(ext, 32, 64);
+        ext = up ? fmaxf(ext, other) : fminf(ext, other);
+      }
+      const bool none = up ? ext == -INFINITY : ext == INFINITY;
+      const float mb2 = none ? -INFINITY : ext * c2;     // max scaled score, base-2 units
+      const float nref = none ? 0.f : -mb2;
+      float sum4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, nref));
+            sacc[kb][r] = p;
+            sum4[r & 3] += p;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool alive = ((vm[kb] >> r) & 1u) && (kb * 32 + 8 * (r / 4) + (r % 4)) <= kmaxh;
+            const float p = alive ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, nref)) : 0.f;
+            sacc[kb][r] = p;
+            sum4[r & 3] += p;
+          }
+      }
+      float sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
       sum += __shfl_xor(sum, 32, 64);
 
-      // ---- O^T = V^T . P^T; the k pair of MFMA (kb, r) is keys kappa and kappa + 4
+      // ---- O^T = V^T . P^T; the k pair of MFMA (kb, r) is keys kappa and kappa + 4.
+      // The V operands of each pair of r are read one pair ahead.
       floatx16 oacc[kD / 32];
 #pragma unroll
       for (int db = 0; db < kD / 32; ++db) oacc[db] = zero16();
+      float vc[2][kD / 32];
+      auto read_v = [&](int r0, float (&dst)[2][kD / 32]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int j = 0; j < 2; ++j) {
+          const int r = r0 + j, kb = r / 16, rr = r % 16;
+          const float* vrow = &s_v[(kb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4)) * kVPitch + lr];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          const float* vrow = &s_v[key * kVPitch + lr];
-          float va[kD / 32];
+          for (int db = 0; db < kD / 32; ++db) dst[j][db] = vrow[db * 32];
+        }
+      };
+      read_v(0, vc);
+      __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
 #pragma unroll
-          for (int db = 0; db < kD / 32; ++db) va[db] = vrow[db * 32];
+      for (int r0 = 0; r0 < 16 * NKB; r0 += 2) {
+        float vn[2][kD / 32];
+        if (r0 + 2 < 16 * NKB) read_v(r0 + 2, vn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int db = 0; db < kD / 32; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[db], sacc[kb][r], oacc[db], 0, 0, 0);
-          if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vc[j][db], sacc[(r0 + j) / 16][(r0 + j) % 16],
+                                                            oacc[db], 0, 0, 0);
+        if (r0 + 2 < 16 * NKB) __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2 * (kD / 32), 0);
+        if (r0 + 2 < 16 * NKB) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db) vc[j][db] = vn[j][db];
         }
+      }
+
+      // ---- the second half of the next tile's q. Issued before this tile's
+      // stores: a wait for a load also waits for every store issued before it
+      if (next < ntiles) load_q8(qp, 8, qr);
 
       // ---- store the tile's partial rows (o unnormalised, m in natural-log units)
       if (row_ok) {
@@ -220,10 +340,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
             *reinterpret_cast<float4*>(op + db * 32 + 8 * g) =
                 make_float4(oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]);
         if (half == 0) {
-          A.m[row0 + row] = mx == -INFINITY ? -INFINITY : mx * kLn2;
+          A.m[row0 + row] = mb2 * kLn2;
           A.l[row0 + row] = sum;
         }
       }
+      tile = next;
     }
     __syncthreads();                       // LDS of this unit no longer read
     if (tid == 0) s_unit = (int)gridDim.x + (int)atomicAdd(&hdr->queue_mfma, 1u);
