@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="also time the step replayed from a captured HIP graph")
+    p.add_argument("--two-pass", action="store_true",
+                   help="decode-shaped batches: sa_forward + sa_combine instead of the fused "
+                        "sa_forward_combine that sa_attention takes")
     return p.parse_args()
 
 
@@ -134,9 +137,13 @@ def algorithmic_work(w, arrs, info, kv_elem_bytes=4):
     part_bytes = rows * (d + 2) * 4
     meta_fwd = info["num_units_wave"] * 16 + info["num_units_mfma"] * 16 + E * 8
     fwd_bytes = kv_bytes + q_bytes + part_bytes + meta_fwd
-    comb_bytes = part_bytes + w.tq * w.hkv * w.topk * 4 + w.tq * w.hq * (d + 1) * 4
+    out_bytes = w.tq * w.hq * (d + 1) * 4
+    comb_bytes = part_bytes + w.tq * w.hkv * w.topk * 4 + out_bytes
+    # the fused forward + combine: K/V once, q once, inv and selected once, O and lse
+    fused_bytes = kv_bytes + q_bytes + 2 * w.tq * w.hkv * w.topk * 4 + out_bytes
     return {"kv_bytes": kv_bytes, "fwd_bytes": fwd_bytes, "comb_bytes": comb_bytes,
-            "total_bytes": fwd_bytes + comb_bytes, "flops": flops, "edges": E, "rows": rows}
+            "total_bytes": fwd_bytes + comb_bytes, "fused_bytes": fused_bytes, "flops": flops,
+            "edges": E, "rows": rows}
 
 
 def cpu_workers():
@@ -276,10 +283,25 @@ def main():
         w = s["w"]
         sa.sa_combine(s["idx"], s["o"], s["m"], s["l"], w.hq, w.head_dim, s["out"], s["lse"])
 
+    fused = (not args.two_pass and not kv16 and base.tq == base.batch and
+             sa.fused_fits(base.hq, base.hkv, base.head_dim, base.block_size, base.page_size,
+                           base.topk))
+
+    def forward_combine(s):
+        w = s["w"]
+        sa.sa_forward_combine(s["idx"], s["sel"], s["q"], k, v, s["bt"], s["cu"], s["used"], w.hq,
+                              w.hkv, w.head_dim, w.block_size, w.page_size, w.softmax_scale,
+                              w.causal, s["out"], s["lse"])
+
     def step(s):
+        # what sa_attention runs: the build, then the fused forward + combine for
+        # decode-shaped batches, else the forward and the combine
         build(s)
-        forward(s)
-        combine(s)
+        if fused:
+            forward_combine(s)
+        else:
+            forward(s)
+            combine(s)
 
     # algorithmic work of each batch, counted from the built index
     work = []
@@ -326,16 +348,22 @@ def main():
             lead_us *= 2
         return e0.elapsed_time(e1) / args.steps, queued_ahead
 
-    (build_ms, ok_b), (fwd_ms, ok_f), (comb_ms, ok_c) = map(phase_ms, (build, forward, combine))
+    if fused:
+        (build_ms, ok_b), (fwd_ms, ok_f) = map(phase_ms, (build, forward_combine))
+        comb_ms, ok_c = 0.0, True
+    else:
+        (build_ms, ok_b), (fwd_ms, ok_f), (comb_ms, ok_c) = map(phase_ms, (build, forward, combine))
     per = [work[i % len(sets)] for i in range(args.steps)]
     edges = sum(p["edges"] for p in per)
     fwd_bytes = np.mean([p["fwd_bytes"] for p in per])
     fwd_avg_s = fwd_ms / 1e3
     step_s = wall / args.steps
-    total_bytes = np.mean([p["total_bytes"] for p in per])
+    total_bytes = np.mean([p["fused_bytes" if fused else "total_bytes"] for p in per])
     flops = np.mean([p["flops"] for p in per])
     fc_s = (fwd_ms + comb_ms) / 1e3
-    roofline = forward_roofline(base, fwd_bytes, flops, fwd_avg_s, args.kv_dtype)
+    if fused:
+        fwd_bytes = total_bytes
+    roofline = forward_roofline(base, fwd_bytes, flops, fwd_avg_s, args.kv_dtype, fused)
 
     result = {
         "metric": METRIC,
@@ -365,6 +393,7 @@ def main():
         "index_build_us": build_ms * 1e3,
         "per_call_gpu_bound": bool(ok_b and ok_f and ok_c),
         "combine_us": comb_ms * 1e3,
+        "fused_forward_combine": bool(fused),
     }
     if args.graph:
         result["graph_step_us"] = graph_step_us(sets, step, args.steps)
@@ -373,17 +402,21 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def forward_kernels(w):
+def forward_kernels(w, fused=False):
     """The kernels one sa_forward launches for this geometry: the one-wave
     kernel alone where it fits (head_dim 128, blocks <= 64 keys, qhead <= 16),
-    else the wavefront-reduction kernel and the MFMA kernel."""
+    else the wavefront-reduction kernel and the MFMA kernel; with `fused`, the
+    one kernel of sa_forward_combine."""
     qhead = w.hq // w.hkv
+    nch = (w.block_size + 15) // 16
+    if fused:
+        return f"k_fwd_fused<{nch}>", None
     if w.head_dim == 128 and w.block_size <= 64 and qhead <= 16:
-        return f"k_fwd_small<{(w.block_size + 15) // 16}>", None
+        return f"k_fwd_small<{nch}>", None
     return "k_fwd_wave", "k_fwd_mfma"
 
 
-def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32"):
+def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32", fused=False):
     """Roofline of the forward pass (sa_forward: the one-wave kernel where
     it fits, else the wavefront kernel for units under 32 rows, then the MFMA
     kernel, which exits at once when the build made no such unit). Bound by HBM when the algorithmic intensity is
@@ -391,7 +424,7 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32"):
     fp32 MFMA. `traffic` comes from the committed FETCH_SIZE + WRITE_SIZE
     summary for this workload, and only while the kernel's source is the one
     the counters were taken on."""
-    small, mfma = forward_kernels(w)
+    small, mfma = forward_kernels(w, fused)
     if kv_dtype != "f32":
         small = small.replace(">", f", {kv_dtype}>")
     ridge = FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
@@ -408,7 +441,8 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32"):
             "traffic": measured_traffic(w.name if kv_dtype == "f32" else f"{w.name}_{kv_dtype}",
                                         dominant),
             "mfma_util": measured_mfma_util(w.name) if bound == "mfma" and kv_dtype == "f32" else None,
-            "kernel": f"sa_forward ({kernels})", "alg_bytes_per_launch": int(fwd_bytes),
+            "kernel": f"{'sa_forward_combine' if fused else 'sa_forward'} ({kernels})",
+            "alg_bytes_per_launch": int(fwd_bytes),
             "alg_flops_per_launch": int(fwd_flops), "avg_launch_us": fwd_s * 1e6}
 
 

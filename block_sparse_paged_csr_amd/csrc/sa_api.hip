@@ -322,13 +322,13 @@ namespace {
 // sa_forward's checks (in the page's order) and launch, for K/V pages stored
 // as fp32 or, with `kv16`, as 16-bit words of `kv_format` (`k`, `v` then
 // hold uint16 elements; formats and geometry are checked after the others).
-sa_status forward_common(const sa_index* idx, const float* q, int64_t q_len, const void* k_pages,
+sa_status forward_checks(const sa_index* idx, const float* q, int64_t q_len, const void* k_pages,
                          int64_t k_len, const void* v_pages, int64_t v_len,
                          const int32_t* block_tables, const int64_t* cu_seqlens_q,
                          const int32_t* used_kv_lens, int32_t hq, int32_t hkv, int32_t head_dim,
                          int32_t block_size, int32_t page_size, float softmax_scale,
                          int32_t causal, bool kv16, int32_t kv_format, float* o_partial,
-                         float* m_partial, float* l_partial, hipStream_t stream) {
+                         float* m_partial, float* l_partial, sa::FwdArgs* args) {
   sa_status st = check_heads_blocks(hq, hkv, head_dim, block_size, page_size);
   if (st != SA_OK) return st;
   if (idx == nullptr || idx->buffer == nullptr) return fail(SA_ERR_SHAPE, "idx (null)", 1, 0);
@@ -373,6 +373,23 @@ sa_status forward_common(const sa_index* idx, const float* q, int64_t q_len, con
   a.causal = causal != 0;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.ps_magic = sa::make_div_magic((uint32_t)page_size);
+  *args = a;
+  return SA_OK;
+}
+
+sa_status forward_common(const sa_index* idx, const float* q, int64_t q_len, const void* k_pages,
+                         int64_t k_len, const void* v_pages, int64_t v_len,
+                         const int32_t* block_tables, const int64_t* cu_seqlens_q,
+                         const int32_t* used_kv_lens, int32_t hq, int32_t hkv, int32_t head_dim,
+                         int32_t block_size, int32_t page_size, float softmax_scale,
+                         int32_t causal, bool kv16, int32_t kv_format, float* o_partial,
+                         float* m_partial, float* l_partial, hipStream_t stream) {
+  sa::FwdArgs a{};
+  sa_status st = forward_checks(idx, q, q_len, k_pages, k_len, v_pages, v_len, block_tables,
+                                cu_seqlens_q, used_kv_lens, hq, hkv, head_dim, block_size,
+                                page_size, softmax_scale, causal, kv16, kv_format, o_partial,
+                                m_partial, l_partial, &a);
+  if (st != SA_OK) return st;
   hipError_t e = sa::launch_forward(idx, a, stream);
   if (e != hipSuccess) return runtime_error(e, "forward launch");
   return ok();
@@ -436,6 +453,30 @@ sa_status sa_combine(const sa_index* idx, const float* o_partial, const float* m
   a.topk = idx->topk;
   hipError_t e = sa::launch_combine(idx, a, stream);
   if (e != hipSuccess) return runtime_error(e, "combine launch");
+  return ok();
+}
+
+sa_status sa_forward_combine(const sa_index* idx, const int32_t* selected, int64_t selected_len,
+                             const float* q, int64_t q_len, const float* k_pages, int64_t k_len,
+                             const float* v_pages, int64_t v_len, const int32_t* block_tables,
+                             const int64_t* cu_seqlens_q, const int32_t* used_kv_lens,
+                             int32_t hq, int32_t hkv, int32_t head_dim, int32_t block_size,
+                             int32_t page_size, float softmax_scale, int32_t causal, float* out,
+                             float* lse, hipStream_t stream) {
+  sa::FwdArgs a{};
+  sa_status st = forward_checks(idx, q, q_len, k_pages, k_len, v_pages, v_len, block_tables,
+                                cu_seqlens_q, used_kv_lens, hq, hkv, head_dim, block_size,
+                                page_size, softmax_scale, causal, false, SA_KV_F32, nullptr,
+                                nullptr, nullptr, &a);
+  if (st != SA_OK) return st;
+  const int64_t want_sel = idx->tq * (int64_t)idx->hkv * idx->topk;
+  if (selected_len != want_sel) return fail(SA_ERR_SHAPE, "selected", want_sel, selected_len);
+  if (!sa::fused_kernel_fits(head_dim, block_size, page_size, hq / hkv, idx->topk))
+    return fail(SA_ERR_UNSUPPORTED,
+                "fused forward: head_dim 128, blocks of at most 64 keys, hq/hkv <= 16, topk <= 512",
+                128, head_dim);
+  hipError_t e = sa::launch_forward_fused(idx, a, selected, out, lse, stream);
+  if (e != hipSuccess) return runtime_error(e, "fused forward launch");
   return ok();
 }
 
@@ -519,12 +560,21 @@ sa_status sa_attention(const float* q, int64_t q_len, const float* k_pages, int6
   st = sa_build_index(selected, selected_len, block_tables, block_tables_len, cu_seqlens_q,
                       cu_len, used_kv_lens, used_len, &idx, stream);
   if (st != SA_OK) return st;
-  st = sa_forward(&idx, q, q_len, k_pages, k_len, v_pages, v_len, block_tables, cu_seqlens_q,
-                  used_kv_lens, hq, hkv, head_dim, block_size, page_size, softmax_scale, causal,
-                  o_part, m_part, l_part, stream);
-  if (st != SA_OK) return st;
-  st = sa_combine(&idx, o_part, m_part, l_part, hq, head_dim, out, lse, stream);
-  if (st != SA_OK) return st;
+  if (tq == batch && sa::fused_kernel_fits(head_dim, block_size, page_size, hq / hkv, topk)) {
+    // one query per sequence on average (decode): forward and combine in one
+    // launch, no partials in memory
+    st = sa_forward_combine(&idx, selected, selected_len, q, q_len, k_pages, k_len, v_pages,
+                            v_len, block_tables, cu_seqlens_q, used_kv_lens, hq, hkv, head_dim,
+                            block_size, page_size, softmax_scale, causal, out, lse, stream);
+    if (st != SA_OK) return st;
+  } else {
+    st = sa_forward(&idx, q, q_len, k_pages, k_len, v_pages, v_len, block_tables, cu_seqlens_q,
+                    used_kv_lens, hq, hkv, head_dim, block_size, page_size, softmax_scale, causal,
+                    o_part, m_part, l_part, stream);
+    if (st != SA_OK) return st;
+    st = sa_combine(&idx, o_part, m_part, l_part, hq, head_dim, out, lse, stream);
+    if (st != SA_OK) return st;
+  }
   if (idx_out) *idx_out = idx;
   return ok();
 }

@@ -428,6 +428,306 @@ hipError_t launch_nch(const sa_index* idx, const FwdArgs& a, hipStream_t s, unsi
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------ fused forward + combine
+// One workgroup per (query q, KV head h) computes the final rows O[q, h*qhead
+// .. h*qhead + qhead) and their lse in one launch, with no partials in
+// memory: the forward's block partials and their log-sum-exp combine, for
+// batches where each block serves one query (decode). Query q's kept ranks
+// (inv[h, q, r] >= 0, block selected[q, h, r]) are dealt to the eight waves;
+// each wave streams its blocks through the same 16-key pieces as k_fwd_small
+// (the next piece in flight, the next block's key offsets fetched a block
+// ahead) and keeps a running (M, L, O) per row, rescaled when a block raises
+// the maximum: the merge the combine applies. The waves' (M, L, O) meet in
+// LDS and one merge writes the output. Every kept block is read once, as in
+// the KV-outer path when each slot holds one edge.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedRanksPerWave = 64;           // topk <= 8 * 64
+
+struct FusedWaveLds {
+  int32_t blk[kFusedRanksPerWave];               // block ids of the wave's kept ranks
+  int64_t ko[2][kMaxKeys];                       // key offsets of the current / next block, or -1
+  uint64_t vm[2];                                // bit t: key t has a row
+};
+
+template <int NCH, int KVF>
+__global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_fused(
+    IndexPtrs P, FwdArgs A, const int32_t* __restrict__ selected, float* __restrict__ out,
+    float* __restrict__ lse, int32_t tq, int32_t topk) {
+  using Piece = PieceT<KVF>;
+  __shared__ FusedWaveLds s_wave[kFusedWaves];
+  __shared__ float s_m[kFusedWaves][kRows], s_l[kFusedWaves][kRows];
+  __shared__ __align__(16) float s_o[kFusedWaves][kRows][kD];
+
+  const int32_t qhead = A.qhead;
+  // head-major workgroups: neighbours read the same head of neighbouring sequences
+  const int32_t h = (int32_t)(blockIdx.x / (uint32_t)tq);
+  const int32_t q = (int32_t)(blockIdx.x - (uint32_t)h * (uint32_t)tq);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int64_t orow0 = (int64_t)q * A.hq + (int64_t)h * qhead;    // first output row
+
+  if (P.hdr->status != SA_OK) {
+    // a failed build: the output gets a defined value, as sa_combine gives it
+    for (int x = threadIdx.x; x < qhead * kD; x += kFusedWaves * 64) out[orow0 * kD + x] = NAN;
+    if (lse != nullptr && (int)threadIdx.x < qhead) lse[orow0 + threadIdx.x] = NAN;
+    return;
+  }
+  FusedWaveLds& S = s_wave[w];
+  const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
+  const int64_t head_off = (int64_t)h * A.page_size * kD;
+
+  // ---- the query's sequence: b = q when cu[q] <= q < cu[q + 1] (a decode
+  // batch), else the search of batch_of; its kv length and causal offset
+  int32_t b;
+  {
+    const int32_t qq = q < A.batch ? q : A.batch - 1;
+    const int64_t c0 = A.cu[qq], c1 = A.cu[qq + 1];
+    b = (c0 <= q && q < c1) ? qq : batch_of_dev(A.cu, A.batch, q);
+  }
+  const int64_t cb0 = A.cu[b];
+  const int64_t qo_len = A.cu[b + 1] - cb0;
+  const int64_t lk = kv_len_dev(A.used, b, A.msb, A.block_size);
+  const int64_t delta = (lk >= qo_len ? lk - qo_len : 0) - cb0;
+  const int64_t bt_row = (int64_t)b * A.max_pages;
+
+  // ---- this wave's kept ranks r = w + 8 i (lane i): their block ids, in rank order
+  int32_t n_blk;
+  {
+    const int32_t r = w + kFusedWaves * lane;
+    const bool in = r < topk;
+    const int64_t at = ((int64_t)q * A.hkv + h) * topk + (in ? r : 0);
+    const int32_t e = P.inv[((int64_t)h * tq + q) * topk + (in ? r : 0)];
+    const int32_t v = selected[at];
+    const bool kept = in && e >= 0;
+    const uint64_t bal = __ballot(kept);
+    const int32_t pos = (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (kept) S.blk[pos] = v;
+    n_blk = (int32_t)__popcll(bal);
+  }
+  // key offsets of the wave's k-th block into slot ks (lane = key)
+  auto block_meta = [&](int32_t k, int ks) {
+    int64_t ko = -1;
+    if (k < n_blk) {
+      const int32_t v = S.blk[k];
+      const int64_t start = (int64_t)v * A.block_size;
+      int64_t end = start + A.block_size;
+      end = end < lk ? end : lk;
+      if (start + lane < end) {
+        const int32_t pl = (int32_t)div_magic((uint32_t)lane, A.ps_magic);
+        const int32_t page = A.block_tables[bt_row + (int64_t)v * A.ppb + pl];
+        if (page >= 0 && page < A.num_pages)
+          ko = (int64_t)page * page_stride + head_off + (int64_t)(lane - pl * A.page_size) * kD;
+      }
+    }
+    S.ko[ks][lane] = ko;
+    const uint64_t vm = __ballot(ko >= 0);
+    if (lane == 0) S.vm[ks] = vm;
+  };
+  auto load_piece = [&](auto pkc, int ks, bool live, Piece& pc) __attribute__((always_inline)) {
+    constexpr int pk = decltype(pkc)::value;
+    if constexpr (KVF == kKvF32) {
+      if constexpr (pk < NCH) {
+        const int64_t kb = S.ko[ks][kPiece * pk + li];
+        gfloat* kp = (live && kb >= 0 ? (gfloat*)(A.k + kb) : zero_line()) + 8 * g;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pc.x[i] = *(gfloatx4*)(kp + 32 * (i >> 1) + 4 * (i & 1));
+      } else {
+        constexpr int c = pk - NCH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t kb = S.ko[ks][kPiece * c + 4 * g + r];
+          gfloat* vp = (live && kb >= 0 ? (gfloat*)(A.v + kb) : zero_line()) + 8 * li;
+          pc.x[2 * r] = *(gfloatx4*)vp;
+          pc.x[2 * r + 1] = *(gfloatx4*)(vp + 4);
+        }
+      }
+    } else {
+      gu16* kbase = (gu16*)A.k;
+      gu16* vbase = (gu16*)A.v;
+      gu16* zero = (gu16*)zero_line();
+      if constexpr (pk < NCH) {
+        const int64_t kb = S.ko[ks][kPiece * pk + li];
+        gu16* kp = (live && kb >= 0 ? kbase + kb : zero) + 8 * g;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uintx4 x = *(guint4*)(kp + 32 * t);
+          pc.x[2 * t] = uintx2{x.x, x.y};
+          pc.x[2 * t + 1] = uintx2{x.z, x.w};
+        }
+      } else {
+        constexpr int c = pk - NCH;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t kb = S.ko[ks][kPiece * c + 4 * g + r];
+          gu16* vp = (live && kb >= 0 ? vbase + kb : zero) + 8 * li;
+          const uintx4 x = *(guint4*)vp;
+          pc.x[2 * r] = uintx2{x.x, x.y};
+          pc.x[2 * r + 1] = uintx2{x.z, x.w};
+        }
+      }
+    }
+  };
+
+  // the query's rows as the B operand: row li (lane group g takes
+  // d = 32 (i >> 1) + 8g + 4 (i & 1) .. +3 in qreg[i]); zero past qhead
+  floatx4 qreg[8];
+  {
+    gfloat* src = (li < qhead ? (gfloat*)(A.q + (orow0 + li) * kD) : zero_line()) + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qreg[i] = *(gfloatx4*)(src + 32 * (i >> 1) + 4 * (i & 1));
+  }
+  block_meta(0, 0);
+  Piece bufA, bufB;
+  load_piece(IC<0>{}, 0, n_blk > 0, bufA);
+
+  // running merge of this wave's blocks for row li (base-2 units)
+  float M = -INFINITY, L = 0.f;
+  floatx4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = zero4();
+  const bool row_ok = li < qhead;
+
+  for (int32_t k = 0; k < n_blk; ++k) {
+    const int ks = k & 1, ks1 = ks ^ 1;
+    const bool more = k + 1 < n_blk;
+    const int32_t v = S.blk[k];
+    const int64_t block_start = (int64_t)v * A.block_size;
+    int64_t block_end = block_start + A.block_size;
+    block_end = block_end < lk ? block_end : lk;
+    const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
+    const uint64_t vm = S.vm[ks];
+    int64_t klim = A.causal ? (int64_t)q + delta - block_start : (int64_t)nkeys - 1;
+    klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
+    const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
+    float sreg[NCH][4];
+    float resc = 1.f;
+
+    auto step = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int j = decltype(kc)::value;
+      if constexpr (j < 2 * NCH) {
+        Piece& cur = (j & 1) ? bufB : bufA;
+        Piece& nxt = (j & 1) ? bufA : bufB;
+        if constexpr (j == 0) block_meta(k + 1, ks1);     // the next block's key offsets
+        if constexpr (j + 1 < 2 * NCH) load_piece(IC<j + 1>{}, ks, true, nxt);
+        else load_piece(IC<0>{}, ks1, more, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j < NCH) {
+          floatx4 sa0 = zero4(), sa1 = zero4();
+#pragma unroll
+          for (int t = 0; t < 8; t += 2) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t, c), qreg[t][c], sa0, 0, 0, 0);
+              sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t + 1, c), qreg[t + 1][c], sa1,
+                                                         0, 0, 0);
+            }
+          }
+          const floatx4 s = sa0 + sa1;    // lane (li, g), reg r: key 16j + 4g + r, row li
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kPiece * j + 4 * g + r;
+            const bool alive = row_ok && ((vm >> key) & 1ull) && key <= kmax;
+            sreg[j][r] = alive ? s[r] * A.scale_log2 : -INFINITY;
+          }
+          if constexpr (j == NCH - 1) {
+            // ---- the block's maximum joins the running one; rescale O and L
+            float mx = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sreg[c][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(M, mx);
+            resc = (M == -INFINITY) ? 0.f : exp2f(M - m_new);
+            float ls = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float p = sreg[c][r] == -INFINITY ? 0.f : exp2f(sreg[c][r] - m_new);
+                sreg[c][r] = p;
+                ls += p;
+              }
+            ls += __shfl_xor(ls, 16, 64);
+            ls += __shfl_xor(ls, 32, 64);
+            if (m_new != -INFINITY) {
+              L = L * resc + ls;
+              M = m_new;
+            }
+#pragma unroll
+            for (int db = 0; db < 8; ++db) oacc[db] *= resc == 0.f ? 0.f : resc;
+          }
+        } else {
+          constexpr int c = j - NCH;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+              oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, 2 * r + (db >> 2), db & 3),
+                                                              sreg[c][r], oacc[db], 0, 0, 0);
+          }
+        }
+      }
+    };
+    step(IC<0>{}); step(IC<1>{}); step(IC<2>{}); step(IC<3>{});
+    step(IC<4>{}); step(IC<5>{}); step(IC<6>{}); step(IC<7>{});
+  }
+
+  // ---- the waves' (M, L, O) into LDS: lane (li, g) holds row li,
+  // d = 32g + 8v + db in oacc[db][v]
+  if (row_ok) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      *reinterpret_cast<floatx4*>(&s_o[w][li][32 * g + 8 * v]) =
+          floatx4{oacc[0][v], oacc[1][v], oacc[2][v], oacc[3][v]};
+      *reinterpret_cast<floatx4*>(&s_o[w][li][32 * g + 8 * v + 4]) =
+          floatx4{oacc[4][v], oacc[5][v], oacc[6][v], oacc[7][v]};
+    }
+    if (g == 0) {
+      s_m[w][li] = M;
+      s_l[w][li] = L;
+    }
+  }
+  __syncthreads();
+  // ---- final merge: item x covers row x / 32 and float4 column x % 32
+  for (int x = threadIdx.x; x < qhead * (kD / 4); x += kFusedWaves * 64) {
+    const int row = x >> 5, c4 = x & 31;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kFusedWaves; ++ww) mt = fmaxf(mt, s_m[ww][row]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lt = 0.f;
+    if (mt != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < kFusedWaves; ++ww) {
+        const float mw = s_m[ww][row];
+        const float f = mw == -INFINITY ? 0.f : exp2f(mw - mt);
+        const float4 o4 = *reinterpret_cast<const float4*>(&s_o[ww][row][4 * c4]);
+        acc = make_float4(fmaf(o4.x, f, acc.x), fmaf(o4.y, f, acc.y), fmaf(o4.z, f, acc.z),
+                          fmaf(o4.w, f, acc.w));
+        lt = fmaf(s_l[ww][row], f, lt);
+      }
+      const float il = 1.f / lt;
+      acc = make_float4(acc.x * il, acc.y * il, acc.z * il, acc.w * il);
+    }
+    *reinterpret_cast<float4*>(out + (orow0 + row) * kD + 4 * c4) = acc;
+    if (lse != nullptr && c4 == 0)
+      lse[orow0 + row] = mt == -INFINITY ? -INFINITY : mt * kLn2 + logf(lt);
+  }
+}
+
+template <int NCH, int KVF>
+hipError_t launch_fused_nch(const sa_index* idx, const FwdArgs& a, const int32_t* selected,
+                            float* out, float* lse, hipStream_t s) {
+  const int64_t grid = idx->tq * (int64_t)idx->hkv;
+  hipLaunchKernelGGL((k_fwd_fused<NCH, KVF>), dim3((unsigned)grid), dim3(kFusedWaves * 64), 0, s,
+                     index_ptrs(idx), a, selected, out, lse, (int32_t)idx->tq, idx->topk);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool small_kernel_fits(int head_dim, int block_size, int page_size, int qhead) {
@@ -436,6 +736,39 @@ bool small_kernel_fits(int head_dim, int block_size, int page_size, int qhead) {
 }
 
 int small_kernel_rows() { return kRows; }
+
+bool fused_kernel_fits(int head_dim, int block_size, int page_size, int qhead, int topk) {
+  return small_kernel_fits(head_dim, block_size, page_size, qhead) &&
+         topk <= kFusedWaves * kFusedRanksPerWave;
+}
+
+hipError_t launch_forward_fused(const sa_index* idx, const FwdArgs& a, const int32_t* selected,
+                                float* out, float* lse, hipStream_t s) {
+  const int nch = (a.block_size + kPiece - 1) / kPiece;
+  switch (a.kv_format) {
+    case kKvBf16:
+      switch (nch) {
+        case 1: return launch_fused_nch<1, kKvBf16>(idx, a, selected, out, lse, s);
+        case 2: return launch_fused_nch<2, kKvBf16>(idx, a, selected, out, lse, s);
+        case 3: return launch_fused_nch<3, kKvBf16>(idx, a, selected, out, lse, s);
+        default: return launch_fused_nch<4, kKvBf16>(idx, a, selected, out, lse, s);
+      }
+    case kKvF16:
+      switch (nch) {
+        case 1: return launch_fused_nch<1, kKvF16>(idx, a, selected, out, lse, s);
+        case 2: return launch_fused_nch<2, kKvF16>(idx, a, selected, out, lse, s);
+        case 3: return launch_fused_nch<3, kKvF16>(idx, a, selected, out, lse, s);
+        default: return launch_fused_nch<4, kKvF16>(idx, a, selected, out, lse, s);
+      }
+    default:
+      switch (nch) {
+        case 1: return launch_fused_nch<1, kKvF32>(idx, a, selected, out, lse, s);
+        case 2: return launch_fused_nch<2, kKvF32>(idx, a, selected, out, lse, s);
+        case 3: return launch_fused_nch<3, kKvF32>(idx, a, selected, out, lse, s);
+        default: return launch_fused_nch<4, kKvF32>(idx, a, selected, out, lse, s);
+      }
+  }
+}
 
 hipError_t launch_forward_small(const sa_index* idx, const FwdArgs& a, hipStream_t s,
                                 unsigned max_units) {

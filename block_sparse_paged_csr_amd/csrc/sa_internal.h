@@ -204,6 +204,11 @@ hipError_t launch_forward_small(const sa_index* idx, const FwdArgs& a, hipStream
 // its units hold at most small_kernel_rows() rows.
 bool small_kernel_fits(int head_dim, int block_size, int page_size, int qhead);
 int small_kernel_rows();
+// The fused forward + combine (one workgroup per (query, KV head)): the
+// one-wave kernel's geometry and at most 512 ranks a row.
+bool fused_kernel_fits(int head_dim, int block_size, int page_size, int qhead, int topk);
+hipError_t launch_forward_fused(const sa_index* idx, const FwdArgs& a, const int32_t* selected,
+                                float* out, float* lse, hipStream_t s);
 
 // Exact n / d for n * d < 2^40 with magic = ceil(2^40 / d).
 __host__ __device__ inline uint32_t div_magic(uint32_t n, uint64_t magic) {

@@ -241,6 +241,31 @@ sa_status sa_combine(const sa_index* idx,
                      int32_t hq, int32_t head_dim,
                      float* out, float* lse, hipStream_t stream);
 
+/* sa_forward_combine: sa_forward followed by sa_combine in one launch, with
+ * no partials in memory (forward.rs module doc: the forward's persistent
+ * outer loop and the log-sum-exp combine of its partials). One workgroup per
+ * (query, KV head) reads the query's kept blocks (inv >= 0; block ids from
+ * `selected`, int32 [tq, hkv, topk], the array the index was built from),
+ * merges the blocks' softmax pieces as they come, and writes `out` and `lse`
+ * exactly as sa_combine defines them. Meant for batches where each block
+ * serves one query (decode: one query per sequence); with shared blocks it is
+ * still exact but reads a shared block once per query. Host checks: those of
+ * sa_forward, then SHAPE "selected" (selected_len != tq*hkv*topk), then
+ * UNSUPPORTED outside head_dim 128, blocks of at most 64 keys, hq/hkv <= 16
+ * and topk <= 512. On an index whose build failed, out and lse are NaN.
+ * sa_attention takes this path itself when tq == batch and the geometry fits. */
+sa_status sa_forward_combine(const sa_index* idx,
+                             const int32_t* selected, int64_t selected_len,
+                             const float* q, int64_t q_len,
+                             const float* k_pages, int64_t k_len,
+                             const float* v_pages, int64_t v_len,
+                             const int32_t* block_tables, const int64_t* cu_seqlens_q,
+                             const int32_t* used_kv_lens,
+                             int32_t hq, int32_t hkv, int32_t head_dim,
+                             int32_t block_size, int32_t page_size,
+                             float softmax_scale, int32_t causal,
+                             float* out, float* lse, hipStream_t stream);
+
 /* sa_attention_workspace_bytes: bytes of the workspace that sa_attention
  * needs: the index buffer plus the worst-case partials, 256-B aligned. */
 sa_status sa_attention_workspace_bytes(int64_t tq, int32_t hkv, int32_t topk, int32_t batch,
@@ -251,7 +276,8 @@ sa_status sa_attention_workspace_bytes(int64_t tq, int32_t hkv, int32_t topk, in
 /* sa_attention: sa_build_index -> sa_forward -> sa_combine on one stream,
  * with the index and partials inside `workspace`. num_pages is
  * k_len / (hkv*page_size*head_dim). Arguments mean what they mean in the
- * three calls above. Host checks run before anything is enqueued, in the
+ * three calls above (build -> sa_forward_combine when tq == batch and its
+ * geometry fits). Host checks run before anything is enqueued, in the
  * forward's order and then the build's. `idx_out` (host, may be NULL)
  * receives the index handle, so that sa_index_status() can read the
  * device-side outcome; when the build found an input error, out and lse

@@ -263,6 +263,63 @@ def test_random_partials_match_kvouter_ref(kernel, seed):
     check_partials(w, d, idx, ref)
 
 
+# The fused forward + combine (sa_forward_combine; sa_attention takes it when
+# tq == batch): one workgroup per (query, KV head) merges the query's kept
+# blocks as it reads them. Exact for any batch, so it is checked on decode-like
+# batches with empty sequences and sequences of two queries too (shared
+# blocks, and the batch_of search instead of b = q), against the oracle and
+# against the two-pass path (sa_forward + sa_combine).
+FUSED_GEOM = [(16, 4), (16, 1), (8, 2), (4, 4), (16, 3), (32, 2), (2, 8)]
+
+
+@pytest.mark.parametrize("seed", range(14))
+def test_fused_forward_combine(seed):
+    ps, ppb = FUSED_GEOM[seed % len(FUSED_GEOM)]
+    w = W.make_random(8800 + seed, batch=1 + seed % 7, qo_max=[1, 2][seed % 2], kv_max=400,
+                      hkv=1 + seed % 3, qhead=[1, 2, 4, 8, 16][seed % 5], head_dim=128,
+                      page_size=ps, pages_per_block=ppb, topk=1 + seed % 9,
+                      causal=bool(seed % 3))
+    _print_case("fused_forward_combine", seed=seed, tq=w.tq, batch=w.batch, bs=w.block_size,
+                qhead=w.hq // w.hkv, topk=w.topk)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    ref = oracle_index(w)
+    assert_index_equal(idx, ref)
+    out, lse = sa.sa_forward_combine(idx, d["sel"], d["q"], d["k"], d["v"], d["bt"], d["cu"],
+                                     d["used"], w.hq, w.hkv, w.head_dim, w.block_size,
+                                     w.page_size, w.softmax_scale, w.causal)
+    _check_output(w, out, lse)
+    o, m, l = sa.sa_forward(idx, d["q"], d["k"], d["v"], d["bt"], d["cu"], d["used"], w.hq,
+                            w.hkv, w.head_dim, w.block_size, w.page_size, w.softmax_scale,
+                            w.causal)
+    out2, lse2 = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    assert max_rel_err(out.cpu().numpy(), out2.cpu().numpy())[0] <= 1e-5
+    fin = torch.isfinite(lse2)
+    assert torch.equal(fin, torch.isfinite(lse))
+    if fin.any():
+        assert (lse[fin] - lse2[fin]).abs().max().item() <= 1e-5
+    if w.tq == w.batch:
+        out3, lse3 = run_attention(w, d)              # sa_attention's own choice: fused
+        assert torch.equal(out3, out) and torch.equal(lse3, lse)
+
+
+def test_fused_rejects_geometry_outside_it():
+    w = W.make_random(8850, batch=2, qo_max=1, kv_max=200, hkv=1, qhead=2, head_dim=64,
+                      page_size=16, pages_per_block=2, topk=3)
+    d = dev_inputs(w)
+    idx = run_index(w, d)
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_forward_combine(idx, d["sel"], d["q"], d["k"], d["v"], d["bt"], d["cu"], d["used"],
+                              w.hq, w.hkv, w.head_dim, w.block_size, w.page_size,
+                              w.softmax_scale, w.causal)
+    assert ei.value.kind == "Unsupported"
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_forward_combine(idx, d["sel"][:-1], d["q"], d["k"], d["v"], d["bt"], d["cu"],
+                              d["used"], w.hq, w.hkv, w.head_dim, w.block_size, w.page_size,
+                              w.softmax_scale, w.causal)
+    assert (ei.value.kind, ei.value.what) == ("ShapeMismatch", "selected")
+
+
 def test_tiny_workload():
     w = W.make_config("tiny")
     _print_case("tiny")
@@ -494,6 +551,13 @@ def test_full_size_workload(name, n_sample):
     print(f"[gpu case] {name}: partials of {len(edges)} edges: {perr}", flush=True)
     out, lse = run_attention(w, d)
     torch.cuda.synchronize()
+    if w.tq == w.batch:
+        # sa_attention took the fused forward + combine: the two-pass path agrees
+        o, m, l = sa.sa_forward(idx, d["q"], d["k"], d["v"], d["bt"], d["cu"], d["used"], w.hq,
+                                w.hkv, w.head_dim, w.block_size, w.page_size, w.softmax_scale,
+                                w.causal)
+        out2, _ = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+        assert max_rel_err(out.cpu().numpy(), out2.cpu().numpy())[0] <= 1e-5
     queries = None if n_sample is None else _sample_queries(w, n_sample)
     err = _check_output(w, out, lse, queries, parallel=True)
     print(f"[gpu case] {name}: O rel err {err:.3e} over "
