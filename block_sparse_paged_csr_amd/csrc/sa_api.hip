@@ -136,6 +136,8 @@ ScratchLayout scratch_layout(const sa_index* idx) {
   L.agg = o;     o = align256(o + sizeof(HeadAgg) * (size_t)idx->hkv);
   L.chunk_agg = o;
   o = align256(o + sizeof(ChunkAgg) * (size_t)idx->hkv * (size_t)scan_chunks(idx->nbs));
+  L.units_sorted = o;
+  o = align256(o + sizeof(Unit) * (size_t)idx->max_units);
   L.end = o;
   return L;
 }
@@ -163,6 +165,7 @@ IndexPtrs index_ptrs(const sa_index* idx) {
   P.qinfo = reinterpret_cast<int2*>(b + L.qinfo);
   P.agg = reinterpret_cast<HeadAgg*>(b + L.agg);
   P.chunk_agg = reinterpret_cast<ChunkAgg*>(b + L.chunk_agg);
+  P.units_sorted = reinterpret_cast<Unit*>(b + L.units_sorted);
   return P;
 }
 

@@ -46,6 +46,199 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // Most edges in one MFMA unit (cap_edges <= kMaxUnitEdges, see the plan).
 constexpr int kMaxUnitEdges = kCapUnitEdges;
 
+// ---- pieces of one 32-row tile, shared by the two 32-row kernels below
+// (K and V rows in LDS with pitches kKPitch and kVPitch floats).
+
+// Bit r of the result for 32-key block kb: key kb*32 + 8*(r/4) + 4*half + r%4
+// (the key of accumulator r of this lane) has a row, from the block's
+// validity words; `all_rows` is set when every key of the block has one.
+template <int NKB>
+__device__ __forceinline__ void lane_key_bits(const uint32_t* valid, int half, uint32_t (&vm)[NKB],
+                                              bool& all_rows) {
+  all_rows = true;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const uint32_t wbits = valid[kb];
+    all_rows = all_rows && wbits == 0xffffffffu;
+    uint32_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m |= ((wbits >> (8 * (r / 4) + 4 * half + (r % 4))) & 1u) << r;
+    vm[kb] = m;
+  }
+}
+
+// S^T = K . Q^T over d for the lane's row (lane % 32); the K operands of
+// each step are read one step ahead.
+template <int NKB>
+__device__ __forceinline__ void tile_scores(const float* sk, const float4 (&qr)[16], int lr, int half,
+                                            floatx16 (&sacc)[NKB]) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
+  float4 kc[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+    kc[kb] = *reinterpret_cast<const float4*>(&sk[(kb * 32 + lr) * kKPitch + half * 64]);
+  __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
+#pragma unroll
+  for (int m4 = 0; m4 < 16; ++m4) {
+    float4 kn[NKB];
+    if (m4 < 15) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        kn[kb] = *reinterpret_cast<const float4*>(&sk[(kb * 32 + lr) * kKPitch + half * 64 + (m4 + 1) * 4]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].x, qr[m4].x, sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].y, qr[m4].y, sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].z, qr[m4].z, sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].w, qr[m4].w, sacc[kb], 0, 0, 0);
+    }
+    // the next step's LDS reads go out before this step's products
+    if (m4 < 15) __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 4 * NKB, 0);
+    if (m4 < 15) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
+    }
+  }
+}
+
+// Mask, block max and sum. The scores are raw dot products; the largest
+// scaled score c2*s is c2 times the largest raw score (c2 >= 0) or the
+// smallest (c2 < 0), and p = exp2(c2*s - that), base 2 with log2 e in c2.
+// Replaces the scores by p (0 for dead keys) and returns the max scaled
+// score in base-2 units (-inf: no alive key) and the row sum. `full`: every
+// key alive for every row of the tile, so the masks are skipped; otherwise
+// key k of the lane is alive iff its bit in vm is set and its index in the
+// block, less 4*half, is at most kmaxh.
+//
+// Bits r (0..15) of a 32-key block whose key 8*(r/4) + r%4 is at most x.
+__device__ __forceinline__ uint32_t keys_upto(int32_t x) {
+  if (x < 0) return 0u;
+  x = x < 31 ? x : 31;
+  const uint32_t grp = (uint32_t)x >> 3, w = ((uint32_t)x & 7u) + 1u;
+  const uint32_t lo = (1u << (4 * grp)) - 1u;
+  return lo | (((1u << (w < 4u ? w : 4u)) - 1u) << (4 * grp));
+}
+template <int NKB>
+__device__ __forceinline__ void tile_softmax(floatx16 (&sacc)[NKB], bool full, const uint32_t (&vm)[NKB],
+                                             int32_t kmaxh, float c2, float& mb2, float& sum) {
+  const bool up = c2 >= 0.f;
+  if (!full) {
+    // dead keys' scores become the identity of the max (min); the alive
+    // bits are formed here for each tile, as plain per-lane words
+    const float dead = up ? -INFINITY : INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      uint32_t w = vm[kb];
+      asm volatile("" : "+v"(w));
+      const uint32_t aw = w & keys_upto(kmaxh - kb * 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = ((aw >> r) & 1u) ? sacc[kb][r] : dead;
+    }
+  }
+  float ext = up ? -INFINITY : INFINITY;
+  if (up) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ext = fmaxf(ext, sacc[kb][r]);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ext = fminf(ext, sacc[kb][r]);
+  }
+  {
+    const float other = __shfl_xor(ext, 32, 64);
+    ext = up ? fmaxf(ext, other) : fminf(ext, other);
+  }
+  const bool none = up ? ext == -INFINITY : ext == INFINITY;
+  mb2 = none ? -INFINITY : ext * c2;
+  const float nref = none ? 0.f : -mb2;
+  // p = exp2(c2*s - mb2); a dead key's infinite score gives exp2(-inf) = 0,
+  // or NaN when c2 == 0, which the max with 0 turns into 0 (masked tiles only)
+  float sum4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (full) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, nref));
+        sacc[kb][r] = p;
+        sum4[r & 3] += p;
+      }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fmaxf(__builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, nref)), 0.f);
+        sacc[kb][r] = p;
+        sum4[r & 3] += p;
+      }
+  }
+  sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
+  sum += __shfl_xor(sum, 32, 64);
+}
+
+// O^T = V^T . P^T; the k pair of MFMA (kb, r) is keys kappa and kappa + 4.
+// The V operands of each pair of r are read one pair ahead.
+template <int NKB>
+__device__ __forceinline__ void tile_pv(const float* sv, const floatx16 (&sacc)[NKB], int lr, int half,
+                                        floatx16 (&oacc)[kD / 32]) {
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db) oacc[db] = zero16();
+  float vc[2][kD / 32];
+  auto read_v = [&](int r0, float (&dst)[2][kD / 32]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = r0 + j, kb = r / 16, rr = r % 16;
+      const float* vrow = &sv[(kb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4)) * kVPitch + lr];
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db) dst[j][db] = vrow[db * 32];
+    }
+  };
+  read_v(0, vc);
+  __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
+#pragma unroll
+  for (int r0 = 0; r0 < 16 * NKB; r0 += 2) {
+    float vn[2][kD / 32];
+    if (r0 + 2 < 16 * NKB) read_v(r0 + 2, vn);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < kD / 32; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vc[j][db], sacc[(r0 + j) / 16][(r0 + j) % 16],
+                                                        oacc[db], 0, 0, 0);
+    if (r0 + 2 < 16 * NKB) __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * (kD / 32), 0);
+    if (r0 + 2 < 16 * NKB) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int db = 0; db < kD / 32; ++db) vc[j][db] = vn[j][db];
+    }
+  }
+}
+
+// The tile's partial row `row` of the unit (o unnormalised, m in natural-log units).
+__device__ __forceinline__ void tile_store(const FwdArgs& A, int64_t row0, int32_t row, int half,
+                                           const floatx16 (&oacc)[kD / 32], float mb2, float sum) {
+  float* op = A.o + (row0 + row) * kD + 4 * half;
+#pragma unroll
+  for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(op + db * 32 + 8 * g) =
+          make_float4(oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]);
+  if (half == 0) {
+    A.m[row0 + row] = mb2 * kLn2;
+    A.l[row0 + row] = sum;
+  }
+}
+
 // NKB: 32-key blocks per KV block (block_size <= 32 * NKB); WAVES per workgroup.
 //
 // Each wave runs its tiles as a software pipeline so that the matrix pipe is
@@ -167,16 +360,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
     // Keys held by this lane in the S^T accumulators: kb*32 + 8*(r/4) + 4*half + r%4.
     // Bit r of vm[kb] says whether that key has a row.
     uint32_t vm[NKB];
-    bool all_rows = true;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const uint32_t wbits = s_valid[kb];
-      all_rows = all_rows && wbits == 0xffffffffu;
-      uint32_t m = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) m |= ((wbits >> (8 * (r / 4) + 4 * half + (r % 4))) & 1u) << r;
-      vm[kb] = m;
-    }
+    bool all_rows;
+    lane_key_bits<NKB>(s_valid, half, vm, all_rows);
 
     while (tile < ntiles) {
       const int32_t row = tile * 32 + lr;
@@ -189,39 +374,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
       // every key of the tile alive for every row: the masks can be skipped
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
 
-      // ---- S^T = K . Q^T over d; the K operands of each step are read one step ahead
       floatx16 sacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
-      float4 kc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        kc[kb] = *reinterpret_cast<const float4*>(&s_k[(kb * 32 + lr) * kKPitch + half * 64]);
-      __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
-#pragma unroll
-      for (int m4 = 0; m4 < 16; ++m4) {
-        float4 kn[NKB];
-        if (m4 < 15) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-            kn[kb] = *reinterpret_cast<const float4*>(
-                &s_k[(kb * 32 + lr) * kKPitch + half * 64 + (m4 + 1) * 4]);
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].x, qr[m4].x, sacc[kb], 0, 0, 0);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].y, qr[m4].y, sacc[kb], 0, 0, 0);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].z, qr[m4].z, sacc[kb], 0, 0, 0);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].w, qr[m4].w, sacc[kb], 0, 0, 0);
-        }
-        // the next step's LDS reads go out before this step's products
-        if (m4 < 15) __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x0008, 4 * NKB, 0);
-        if (m4 < 15) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
-        }
-      }
+      tile_scores<NKB>(s_k, qr, lr, half, sacc);
 
       // ---- the first half of the next tile's q, into the registers the
       // products above have read (the second half follows the PV products)
@@ -231,119 +385,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
         load_q8(qp, 0, qr);
       }
 
-      // ---- mask, row max and sum. The scores are raw dot products; the
-      // largest scaled score c2*s is c2 times the largest raw score (c2 >= 0)
-      // or the smallest (c2 < 0), and p = exp2(c2*s - that), base 2 with
-      // log2 e in c2.
-      const bool up = c2 >= 0.f;
-      float ext = up ? -INFINITY : INFINITY;
-      if (full) {
-        if (up) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ext = fmaxf(ext, sacc[kb][r]);
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ext = fminf(ext, sacc[kb][r]);
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool alive = ((vm[kb] >> r) & 1u) && (kb * 32 + 8 * (r / 4) + (r % 4)) <= kmaxh;
-            ext = alive ? (up ? fmaxf(ext, sacc[kb][r]) : fminf(ext, sacc[kb][r])) : ext;
-          }
-      }
-      {
-        const float other = __shfl_xor(ext, 32, 64);
-        ext = up ? fmaxf(ext, other) : fminf(ext, other);
-      }
-      const bool none = up ? ext == -INFINITY : ext == INFINITY;
-      const float mb2 = none ? -INFINITY : ext * c2;     // max scaled score, base-2 units
-      const float nref = none ? 0.f : -mb2;
-      float sum4[4] = {0.f, 0.f, 0.f, 0.f};
-      if (full) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, nref));
-            sacc[kb][r] = p;
-            sum4[r & 3] += p;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool alive = ((vm[kb] >> r) & 1u) && (kb * 32 + 8 * (r / 4) + (r % 4)) <= kmaxh;
-            const float p = alive ? __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, nref)) : 0.f;
-            sacc[kb][r] = p;
-            sum4[r & 3] += p;
-          }
-      }
-      float sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
-      sum += __shfl_xor(sum, 32, 64);
-
-      // ---- O^T = V^T . P^T; the k pair of MFMA (kb, r) is keys kappa and kappa + 4.
-      // The V operands of each pair of r are read one pair ahead.
+      float mb2, sum;
+      tile_softmax<NKB>(sacc, full, vm, kmaxh, c2, mb2, sum);
       floatx16 oacc[kD / 32];
-#pragma unroll
-      for (int db = 0; db < kD / 32; ++db) oacc[db] = zero16();
-      float vc[2][kD / 32];
-      auto read_v = [&](int r0, float (&dst)[2][kD / 32]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = r0 + j, kb = r / 16, rr = r % 16;
-          const float* vrow = &s_v[(kb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4)) * kVPitch + lr];
-#pragma unroll
-          for (int db = 0; db < kD / 32; ++db) dst[j][db] = vrow[db * 32];
-        }
-      };
-      read_v(0, vc);
-      __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
-#pragma unroll
-      for (int r0 = 0; r0 < 16 * NKB; r0 += 2) {
-        float vn[2][kD / 32];
-        if (r0 + 2 < 16 * NKB) read_v(r0 + 2, vn);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int db = 0; db < kD / 32; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vc[j][db], sacc[(r0 + j) / 16][(r0 + j) % 16],
-                                                            oacc[db], 0, 0, 0);
-        if (r0 + 2 < 16 * NKB) __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
-        __builtin_amdgcn_sched_group_barrier(0x0008, 2 * (kD / 32), 0);
-        if (r0 + 2 < 16 * NKB) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int db = 0; db < kD / 32; ++db) vc[j][db] = vn[j][db];
-        }
-      }
+      tile_pv<NKB>(s_v, sacc, lr, half, oacc);
 
       // ---- the second half of the next tile's q. Issued before this tile's
       // stores: a wait for a load also waits for every store issued before it
       if (next < ntiles) load_q8(qp, 8, qr);
 
-      // ---- store the tile's partial rows (o unnormalised, m in natural-log units)
-      if (row_ok) {
-        float* op = A.o + (row0 + row) * kD + 4 * half;
-#pragma unroll
-        for (int db = 0; db < kD / 32; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4*>(op + db * 32 + 8 * g) =
-                make_float4(oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]);
-        if (half == 0) {
-          A.m[row0 + row] = mb2 * kLn2;
-          A.l[row0 + row] = sum;
-        }
-      }
+      if (row_ok) tile_store(A, row0, row, half, oacc, mb2, sum);
       tile = next;
     }
     __syncthreads();                       // LDS of this unit no longer read
@@ -361,6 +412,305 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
       atomicExch(&hdr->done_mfma, 0u);
     }
   }
+}
+
+// fp32 pages, blocks of 65..128 keys: the same tiles, with everything a unit
+// reads from memory besides q brought into LDS by direct-to-LDS loads
+// (global_load_lds: each lane moves 4 or 16 bytes from its own global address
+// into LDS; no registers hold the data):
+//   - the block-table entries and query ids of the unit two ahead go out
+//     when a unit starts, its record at the end of the unit before; the key
+//     offsets of the next unit are formed from them when a unit starts;
+//   - the next unit's K and V rows go out as soon as every wave has left
+//     this unit's tiles, all in flight at once (about 17 wave instructions
+//     of 1 KB), and one wait and one barrier publish them;
+//   - each wave's first q rows of the next unit load after its last QK
+//     products of this unit.
+// Within a unit the waves run their tiles without further barriers, so the
+// two waves of a SIMD drift apart and one's softmax overlaps the other's
+// matrix products. The units, sorted largest first by the index build, are
+// dealt statically (workgroup g takes unit k*G + g for even k and k*G + G-1-g
+// for odd k, G workgroups): near-equal shares without a queue, and every
+// lookahead is known.
+//
+// The padded K and V regions are filled as a whole: 16-byte chunk i of a
+// region (row i / pitch, column chunk i % pitch) comes from the key's row, or
+// from a zero line for padding, missing keys and the tail of the last
+// instruction. A wave waits for its own direct-to-LDS loads with vmcnt (they
+// complete in order with its other vector memory operations) and a
+// workgroup barrier then publishes them.
+constexpr int kSlots = 3;
+__device__ const float g_zero_row[kD] = {};
+
+typedef const __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// s_waitcnt with vmcnt(N), no wait on the other counters (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier once this wave's LDS operations have completed (its
+// vector memory operations may still be in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// A lane index the compiler cannot see through, so that address arithmetic
+// built on it is formed where it is used rather than kept live.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
+template <int NKB>
+__global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
+  constexpr int kWaves = 8;
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kKeys = NKB * 32;
+  constexpr int kKInstr = (kKeys * (kKPitch / 4) + 63) / 64;   // wave instructions filling the K region
+  constexpr int kVInstr = (kKeys * (kVPitch / 4) + 63) / 64;
+  constexpr int kVMin = kVInstr / kWaves;                     // V instructions of every wave, at least
+  static_assert(kKeys <= kThreads && kMaxUnitEdges <= kThreads, "one key and one edge per thread");
+  static_assert(kMaxUnitEdges % 64 == 0, "query ids move in whole waves");
+  __shared__ __align__(16) float s_k[kKInstr * 256];
+  __shared__ __align__(16) float s_v[kVInstr * 256];
+  __shared__ int64_t s_off[kKeys];                   // key row offsets of the next unit (-1: none)
+  __shared__ uint32_t s_valid[2][NKB];               // validity bits, by unit parity
+  __shared__ int32_t s_rec[kSlots][8];               // records, slot j % 3 for unit j
+  __shared__ int32_t s_page[kSlots][kKeys];          // block-table entry of each key
+  __shared__ int32_t s_qid[kSlots][kMaxUnitEdges];   // query id of each edge
+
+  const DevHeader* hdr = P.hdr;
+  if (hdr->status != SA_OK) return;
+  const int32_t num_units = hdr->num_units_mfma;
+  const int32_t G = gridDim.x, g = blockIdx.x;
+  if (g >= num_units) return;
+  auto unit_at = [&](int32_t k) -> int32_t { return k * G + ((k & 1) ? G - 1 - g : g); };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
+  const int32_t qhead = A.qhead;
+  const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
+  const float c2 = A.scale_log2;
+  const int32_t* units = reinterpret_cast<const int32_t*>(P.units_sorted);   // largest first
+  // Per-lane constants (row lane lr, half of the lanes) are formed again from
+  // an opaque lane index where they are used, instead of being kept live
+  // across the unit loop: the tile code needs nearly every register.
+  int lr = lane & 31, half = lane >> 5;
+
+  // a record from LDS, in scalar registers (the fields are uniform)
+  auto unit_of = [&](int sl) {
+    const int32_t* r = s_rec[sl];
+    return Unit{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3]),
+                __builtin_amdgcn_readfirstlane(r[4]), __builtin_amdgcn_readfirstlane(r[5]),
+                __builtin_amdgcn_readfirstlane(r[6]), __builtin_amdgcn_readfirstlane(r[7])};
+  };
+  auto keys_of = [&](int32_t blk, int32_t lk) -> int32_t {
+    const int64_t start = (int64_t)blk * A.block_size;
+    int64_t end = start + A.block_size;
+    end = end < lk ? end : (int64_t)lk;
+    return end > start ? (int32_t)(end - start) : 0;
+  };
+  // ---- metadata, all by direct-to-LDS loads: the record of unit u into
+  // slot sl (lanes 0-7 of wave 0), then from it the block-table entry of
+  // every key and the query id of every edge
+  auto fetch_record = [&](int sl, int32_t u) {
+    if (wv == 0 && lane < 8)
+      __builtin_amdgcn_global_load_lds((gvoid*)(units + 8 * (int64_t)u + opaque_lane(lane)),
+                                       (lvoid*)&s_rec[sl][0], 4, 0, 0);
+  };
+  auto fetch_lists = [&](int sl, const Unit& U) {
+    if (tid < kKeys) {
+      const int key = opaque_lane(lane) + 64 * wv;
+      const int kk = key < A.block_size ? key : 0;
+      const int32_t pgl = (int32_t)div_magic((uint32_t)kk, A.ps_magic);
+      __builtin_amdgcn_global_load_lds(
+          (gvoid*)(A.block_tables + (int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb + pgl),
+          (lvoid*)&s_page[sl][64 * wv], 4, 0, 0);
+    }
+    if (tid < U.e1 - U.e0)
+      __builtin_amdgcn_global_load_lds((gvoid*)(P.edges + 2 * ((int64_t)U.e0 + opaque_lane(lane) + 64 * wv)),
+                                       (lvoid*)&s_qid[sl][64 * wv], 4, 0, 0);
+  };
+  // key row offsets and validity bits of the unit in slot sl (parity par)
+  auto form_offsets = [&](int sl, int par) {
+    if (tid < kKeys) {
+      const Unit U = unit_of(sl);
+      const int32_t page = s_page[sl][tid];
+      int64_t off = -1;
+      if (tid < keys_of(U.blk, U.lk) && page >= 0 && page < A.num_pages) {
+        const int32_t pgl = (int32_t)div_magic((uint32_t)tid, A.ps_magic);
+        off = (int64_t)page * page_stride + (int64_t)U.h * A.page_size * kD + (int64_t)(tid - pgl * A.page_size) * kD;
+      }
+      s_off[tid] = off;
+      const uint64_t bits = __ballot(off >= 0);
+      if ((lane & 31) == 0) s_valid[par][tid >> 5] = (uint32_t)(bits >> (lane & 32));
+    }
+  };
+  // ---- direct-to-LDS gather of a block's K and V rows into their padded
+  // regions. Every source address is formed (from the key offsets in LDS)
+  // before the first load goes out: an LDS read behind a direct-to-LDS load
+  // would wait for it.
+  auto gather_kv = [&]() __attribute__((always_inline)) {
+    constexpr int kPerWave = (kVInstr + kWaves - 1) / kWaves;
+    const float* srck[kPerWave];
+    const float* srcv[kPerWave];
+    auto src_of = [&](const float* base, int pitch4, int n) -> const float* {
+      const int c = 64 * n + opaque_lane(lane);
+      const int row = c / pitch4, col = c - row * pitch4;
+      const int64_t off = s_off[row < kKeys ? row : 0];
+      return (row < kKeys && col < kD / 4 && off >= 0) ? base + off + 4 * col
+                                                     : g_zero_row + 4 * (col & (kD / 4 - 1));
+    };
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int n = i * kWaves + wv;
+      srck[i] = src_of(A.k, kKPitch / 4, n < kKInstr ? n : 0);
+      srcv[i] = src_of(A.v, kVPitch / 4, n < kVInstr ? n : 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int n = i * kWaves + wv;
+      if (n < kKInstr) __builtin_amdgcn_global_load_lds((gvoid*)srck[i], (lvoid*)(s_k + 256 * n), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int n = i * kWaves + wv;
+      if (n < kVInstr) __builtin_amdgcn_global_load_lds((gvoid*)srcv[i], (lvoid*)(s_v + 256 * n), 16, 0, 0);
+    }
+  };
+  // q row of tile row `row` of the unit in slot sl (rows past the unit read
+  // its last row: they stay in their own lanes and are never stored)
+  auto q_row = [&](int sl, int32_t h, int32_t rows, int32_t tile, int32_t* qi_out) -> const float* {
+    int32_t row = tile * 32 + lr;
+    row = row < rows ? row : rows - 1;
+    const int32_t qi = s_qid[sl][row / qhead];
+    *qi_out = qi;
+    return A.q + ((int64_t)qi * A.hq + (int64_t)h * qhead + row % qhead) * kD + half * 64;
+  };
+  auto load_q8 = [&](const float* qp, int i0, float4 (&qr)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = i0; i < i0 + 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+  };
+
+  // ---- prologue: records of units 0..2, lists of units 0 and 1, offsets of
+  // unit 0; then unit 0's first q rows, K and V
+  fetch_record(0, unit_at(0));
+  if (unit_at(1) < num_units) fetch_record(1, unit_at(1));
+  if (unit_at(2) < num_units) fetch_record(2, unit_at(2));
+  wait_vm<0>();
+  lds_barrier();
+  fetch_lists(0, unit_of(0));
+  if (unit_at(1) < num_units) fetch_lists(1, unit_of(1));
+  wait_vm<0>();
+  lds_barrier();
+  form_offsets(0, 0);
+  lds_barrier();
+  float4 qr[16];
+  int32_t qi = 0;
+  const float* qp = nullptr;
+  {
+    const Unit U0 = unit_of(0);
+    const int32_t rows0 = (U0.e1 - U0.e0) * qhead;
+    if (wv * 32 < rows0) {
+      qp = q_row(0, U0.h, rows0, wv, &qi);
+      load_q8(qp, 0, qr);
+      load_q8(qp, 8, qr);
+    }
+  }
+  gather_kv();
+
+  for (int32_t j = 0;; ++j) {
+    if (unit_at(j) >= num_units) break;
+    const int ms = j % kSlots, ms1 = (j + 1) % kSlots, ms2 = (j + 2) % kSlots;
+    const bool has1 = unit_at(j + 1) < num_units, has2 = unit_at(j + 2) < num_units;
+    const bool has3 = unit_at(j + 3) < num_units;
+    const Unit U = unit_of(ms);
+    const int64_t block_start = (int64_t)U.blk * A.block_size;
+    const int32_t nkeys = keys_of(U.blk, U.lk);
+    const int32_t rows = (U.e1 - U.e0) * qhead;
+    const int64_t row0 = (int64_t)U.e0 * qhead;
+    const int32_t ntiles = (rows + 31) / 32;
+    uint32_t vm[NKB];
+    bool all_rows;
+    lane_key_bits<NKB>(s_valid[j & 1], opaque_lane(lane) >> 5, vm, all_rows);
+
+    // ---- this unit's K and V rows (and this wave's first q rows, the lists
+    // of unit j + 1 and the record of unit j + 2): this wave's, then every
+    // wave's. Nothing goes to LDS directly from here to the end of the
+    // tiles, so no LDS read below waits on memory.
+    wait_vm<0>();
+    lds_barrier();
+    // the next unit's key offsets
+    if (has1) form_offsets(ms1, (j + 1) & 1);
+
+    bool q_next = false;   // this wave has requested its first q rows of unit j + 1
+    for (int32_t tile = wv; tile < ntiles; tile += kWaves) {
+      {
+        const int ln = opaque_lane(lane);
+        lr = ln & 31;
+        half = ln >> 5;
+      }
+      const int32_t row = tile * 32 + lr;
+      const bool row_ok = row < rows;
+      // key k is alive iff it has a row and (causal) block_start + k <= q + delta
+      int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
+      klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
+      const int32_t kmaxh = (int32_t)(klim < -1 ? -1 : klim) - 4 * half;
+      const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
+      floatx16 sacc[NKB];
+      tile_scores<NKB>(s_k, qr, lr, half, sacc);
+      // ---- the first half of the next q rows: this unit's next tile, or
+      // the next unit's first one
+      bool nq = false;
+      if (tile + kWaves < ntiles) {
+        nq = true;
+        qp = q_row(ms, U.h, rows, tile + kWaves, &qi);
+      } else if (has1) {
+        const Unit U1 = unit_of(ms1);
+        const int32_t rows1 = (U1.e1 - U1.e0) * qhead;
+        q_next = true;
+        nq = wv * 32 < rows1;
+        if (nq) qp = q_row(ms1, U1.h, rows1, wv, &qi);
+      }
+      if (nq) load_q8(qp, 0, qr);
+      float mb2, sum;
+      tile_softmax<NKB>(sacc, full, vm, kmaxh, c2, mb2, sum);
+      floatx16 oacc[kD / 32];
+      tile_pv<NKB>(s_v, sacc, lr, half, oacc);
+      // the second half, before the stores (a wait for a load also waits
+      // for every store issued before it)
+      if (nq) load_q8(qp, 8, qr);
+      if (row_ok) tile_store(A, row0, row, half, oacc, mb2, sum);
+    }
+    // ---- every wave has left this unit's tiles: the next unit's K and V
+    // rows, the first q rows of waves that had no tile here, the lists of
+    // unit j + 2 and the record of unit j + 3 (into this unit's slots). The
+    // LDS reads all come before the first direct-to-LDS load.
+    lds_barrier();
+    if (has1) {
+      const Unit U1 = unit_of(ms1);
+      const int32_t rows1 = (U1.e1 - U1.e0) * qhead;
+      const bool load_first_q = !q_next && wv * 32 < rows1;
+      if (load_first_q) qp = q_row(ms1, U1.h, rows1, wv, &qi);
+      Unit U2{};
+      if (has2) U2 = unit_of(ms2);
+      gather_kv();
+      if (has2) fetch_lists(ms2, U2);
+      if (load_first_q) {
+        load_q8(qp, 0, qr);
+        load_q8(qp, 8, qr);
+      }
+    }
+    if (has3) fetch_record(ms, unit_at(j + 3));
+  }
+  // no direct-to-LDS load may outlive the workgroup's LDS
+  wait_vm<0>();
 }
 
 // Blocks of up to 64 keys: 16-row tiles on v_mfma_f32_16x16x4f32, so that
@@ -644,6 +994,19 @@ hipError_t launch_mfma_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, un
   }
 }
 
+template <int NKB>
+hipError_t launch_mfma_dma(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+  static thread_local int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma_dma<NKB>, 512, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  hipLaunchKernelGGL((k_fwd_mfma_dma<NKB>), dim3((unsigned)per_cu * cus), dim3(512), 0, s, P, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool mfma_enabled() { return true; }
@@ -655,6 +1018,10 @@ hipError_t launch_forward_mfma(const sa_index* idx, const FwdArgs& a, hipStream_
   const int nkb = (a.block_size + 31) / 32;
   if (nkb <= 1) return launch_mfma16_t<1>(P, a, s, grid);
   if (nkb <= 2) return launch_mfma16_t<2>(P, a, s, grid);
+  if (a.kv_format == SA_KV_F32) {
+    if (nkb <= 3) return launch_mfma_dma<3>(P, a, s, grid);
+    return launch_mfma_dma<4>(P, a, s, grid);
+  }
   if (nkb <= 3) return launch_mfma_t<3, 8>(P, a, s, grid);
   return launch_mfma_t<4, 8>(P, a, s, grid);
 }

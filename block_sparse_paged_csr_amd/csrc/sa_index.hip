@@ -1217,12 +1217,89 @@ inline unsigned grid_for(int64_t n, int per) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
+// ------------------------------------------------------------ MFMA unit order
+// The MFMA units again, largest first (by 32-row tiles: 64 buckets; within a
+// bucket in any order), for the 32-row forward's static assignment: dealt in
+// a snake over the workgroups, a size-sorted list gives every workgroup a
+// near-equal share without a queue, and each workgroup knows its next units
+// in advance. One workgroup: an LDS histogram, its scan, an LDS cursor per
+// bucket. Several units a thread per pass, loads first, so that each pass
+// costs one round trip per batch.
+constexpr int kSortThreads = 1024;
+constexpr int kSortBatch = 4;
+constexpr int kSortBuckets = 64;                 // units hold at most 2048 rows = 64 tiles
+
+__device__ inline int unit_bucket(int32_t e0, int32_t e1, int32_t qhead) {
+  const int32_t tiles = ((e1 - e0) * qhead + 31) / 32;
+  const int32_t t = tiles < 1 ? 1 : (tiles > kSortBuckets ? kSortBuckets : tiles);
+  return kSortBuckets - t;                       // bucket 0: the largest units
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_unit_sort(IndexPtrs P, BuildArgs A) {
+  __shared__ int32_t s_cnt[kSortBuckets];
+  __shared__ int32_t s_cur[kSortBuckets];
+  if (P.hdr->status != SA_OK) return;            // a failed build: the forward does not run
+  const int32_t n = P.hdr->num_units_mfma;
+  const int tid = threadIdx.x;
+  if (tid < kSortBuckets) s_cnt[tid] = 0;
+  __syncthreads();
+  const int4* src = reinterpret_cast<const int4*>(P.units_mfma);   // a unit is two int4: (h, j, e0, e1), (b, blk, lk, delta)
+  for (int32_t base = 0; base < n; base += kSortThreads * kSortBatch) {
+    int4 v[kSortBatch];
+#pragma unroll
+    for (int k = 0; k < kSortBatch; ++k) {
+      const int32_t u = base + k * kSortThreads + tid;
+      v[k] = u < n ? src[2 * (int64_t)u] : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kSortBatch; ++k)
+      if (base + k * kSortThreads + tid < n) atomicAdd(&s_cnt[unit_bucket(v[k].z, v[k].w, A.qhead)], 1);
+  }
+  __syncthreads();
+  if (tid < 64) {                                // exclusive scan of the 64 counts in one wave
+    const int c = s_cnt[tid];
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (tid >= off) incl += t;
+    }
+    s_cur[tid] = incl - c;
+  }
+  __syncthreads();
+  int4* dst = reinterpret_cast<int4*>(P.units_sorted);
+  for (int32_t base = 0; base < n; base += kSortThreads * kSortBatch) {
+    int4 lo[kSortBatch], hi[kSortBatch];
+#pragma unroll
+    for (int k = 0; k < kSortBatch; ++k) {
+      const int32_t u = base + k * kSortThreads + tid;
+      const int32_t uu = u < n ? u : 0;
+      lo[k] = src[2 * (int64_t)uu];
+      hi[k] = src[2 * (int64_t)uu + 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kSortBatch; ++k) {
+      if (base + k * kSortThreads + tid < n) {
+        const int32_t pos = atomicAdd(&s_cur[unit_bucket(lo[k].z, lo[k].w, A.qhead)], 1);
+        dst[2 * (int64_t)pos] = lo[k];
+        dst[2 * (int64_t)pos + 1] = hi[k];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 bool fused_build_fits(int64_t tq, int32_t topk, int64_t nbs, int32_t batch, int32_t hkv) {
   return tq * topk <= (int64_t)kFusedThreads * kFusedItems && nbs <= kFusedMaxSlots &&
          tq <= kFusedMaxQ && batch <= kFusedMaxBatch && hkv <= 65535 &&
          fused_lds_bytes(tq, topk, nbs, batch) <= kFusedMaxLds;
+}
+
+// The 32-row MFMA forward for blocks of more than 64 keys walks the units in
+// size order (k_unit_sort); other geometries do not read that list.
+inline bool unit_sort_needed(const BuildArgs& a) {
+  return a.mfma_min_rows != INT32_MAX && a.block_size > 64;
 }
 
 hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) {
@@ -1245,6 +1322,7 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
     }
     const size_t lds = fused_lds_bytes(a);
     hipLaunchKernelGGL(k_index_fused, dim3((unsigned)a.hkv), dim3(kFusedThreads), lds, s, P, a);
+    if (unit_sort_needed(a)) hipLaunchKernelGGL(k_unit_sort, dim3(1), dim3(kSortThreads), 0, s, P, a);
     return hipGetLastError();
   }
   const int64_t slots = (int64_t)a.hkv * a.nbs;
@@ -1286,6 +1364,7 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
   if (rank_grid > 8 * cu_count()) rank_grid = 8 * cu_count();
   hipLaunchKernelGGL(k_index_rank, dim3(rank_grid), dim3(256), (size_t)ra.rank_bitmap_words * 4, s,
                      P, ra);
+  if (unit_sort_needed(a)) hipLaunchKernelGGL(k_unit_sort, dim3(1), dim3(kSortThreads), 0, s, P, a);
   return hipGetLastError();
 }
 

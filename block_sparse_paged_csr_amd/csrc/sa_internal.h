@@ -82,6 +82,7 @@ struct ScratchLayout {
   size_t qinfo;      // int2  [tq]        (sequence b, resolved kv length lk_b) per query
   size_t agg;        // HeadAgg [hkv]     per-head totals published by the fused build
   size_t chunk_agg;  // ChunkAgg [hkv * scan_chunks(nbs)]  per-chunk sums of the slot scan
+  size_t units_sorted;  // Unit [max_units]  the MFMA units, largest first (k_unit_sort)
   size_t end;
 };
 
@@ -132,6 +133,7 @@ struct IndexPtrs {
   int2* qinfo;
   HeadAgg* agg;
   ChunkAgg* chunk_agg;
+  Unit* units_sorted;
 };
 
 struct BuildArgs {
