@@ -670,3 +670,118 @@ def test_multikernel_build_aggregation(case, agg, monkeypatch):
     check_units(arrs, info, ref, idx.c.cap_edges, w)
     out, lse = run_attention(w, d_in)
     _check_output(w, out, lse)
+
+
+# ------------------------------------------------------------------ decode-shaped builds
+# Every sequence holds one query (cu[b] = b), as in decode batches: padding,
+# repeated picks in a row (several edges in one slot), blocks past the used
+# length, empty rows, one pick a row, 33 picks, 1024 rows, slots large enough
+# for MFMA units, and a batch with tq == batch whose cu is not of that form.
+# Index bit-exact, units checked, output against the oracle; both build paths.
+
+def _decode_case(seed, batch, hkv, topk, msb, ppb=4, ps=4, qhead=2, d=16, dup=0.1, pad=0.2,
+                 short=0.0, cu=None):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bs = ps * ppb
+    max_pages = msb * ppb
+    if cu is None:
+        cu = np.arange(batch + 1, dtype=np.int64)
+    tq = int(cu[-1])
+    kv = rng.integers(1, msb * bs + 1, size=batch)
+    used = np.where(rng.random(batch) < short, rng.integers(0, bs, size=batch), kv).astype(np.int32)
+    pages = [int(math.ceil(k / ps)) for k in kv]
+    num_pages = int(sum(pages)) + 2
+    perm = rng.permutation(num_pages)
+    tbl = np.full((batch, max_pages), -1, dtype=np.int32)
+    o = 0
+    for b in range(batch):
+        tbl[b, : pages[b]] = perm[o:o + pages[b]]
+        o += pages[b]
+    sel = np.full((tq, hkv, topk), -1, dtype=np.int32)
+    for q in range(tq):
+        b = int(np.searchsorted(cu, q, side="right") - 1)
+        hi = max(1, int(math.ceil(kv[b] / bs)))
+        for h in range(hkv):
+            k = min(topk, hi)
+            row = np.full(topk, -1, dtype=np.int64)
+            row[:k] = rng.choice(hi, size=k, replace=False)
+            row = rng.permutation(row)
+            if topk > 1 and dup > 0:
+                dups = rng.random(topk) < dup
+                row[dups] = row[0]
+            row[rng.random(topk) < pad] = -1
+            sel[q, h] = row
+    hq = hkv * qhead
+    return W.Workload("decode_edge", rng.standard_normal((tq, hq, d), dtype=np.float32),
+                      rng.standard_normal((num_pages, hkv, ps, d), dtype=np.float32),
+                      rng.standard_normal((num_pages, hkv, ps, d), dtype=np.float32),
+                      sel, tbl, cu, used, hq, hkv, d, bs, ps, topk, 1.0 / math.sqrt(d),
+                      bool(seed % 2))
+
+
+DECODE_EDGE = [
+    # (batch, hkv, topk, msb, ppb, ps, qhead, d, dup, pad, short)
+    (32, 8, 16, 128, 4, 16, 4, 128, 0.1, 0.1, 0.1),   # the decode shape, kv shortened
+    (7, 3, 5, 20, 2, 4, 2, 16, 0.3, 0.3, 0.2),        # 8 lanes a row
+    (1, 1, 1, 3, 1, 4, 1, 8, 0.0, 0.0, 0.0),          # one pick
+    (16, 4, 33, 40, 1, 8, 2, 16, 0.2, 0.2, 0.1),      # 64 lanes a row
+    (64, 16, 4, 50, 2, 4, 2, 16, 0.2, 0.3, 0.3),      # 1024 rows
+    (40, 2, 16, 30, 4, 4, 2, 16, 0.0, 0.5, 0.6),      # many blocks past lk, empty rows
+    (24, 2, 8, 12, 4, 32, 16, 128, 0.5, 0.1, 0.0),    # 128-key blocks, duplicates: MFMA units
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_EDGE)))
+def test_decode_shaped_build(case, build_path):
+    batch, hkv, topk, msb, ppb, ps, qhead, d, dup, pad, short = DECODE_EDGE[case]
+    w = _decode_case(9500 + case, batch, hkv, topk, msb, ppb, ps, qhead, d, dup, pad, short)
+    _print_case("decode_shaped_build", idx=case, tq=w.tq, hkv=hkv, topk=topk, path=build_path)
+    d_in = dev_inputs(w)
+    idx = run_index(w, d_in)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+    # the output: the query-outer oracle attends over the union of a row's
+    # blocks and so takes rows without repeated picks (the same draw, dup=0)
+    w = _decode_case(9500 + case, batch, hkv, topk, msb, ppb, ps, qhead, d, 0.0, pad, short)
+    out, lse = run_attention(w, dev_inputs(w))
+    _check_output(w, out, lse)
+
+
+def test_decode_shaped_build_falls_back_on_other_cu(build_path):
+    # tq == batch, but one empty sequence and one with two queries
+    cu = np.array([0, 1, 1, 3, 4, 5, 6, 7, 8], dtype=np.int64)
+    w = _decode_case(9600, 8, 2, 6, 10, 2, 4, 2, 16, 0.2, 0.2, 0.0, cu=cu)
+    _print_case("decode_shaped_fallback", tq=w.tq, path=build_path)
+    d_in = dev_inputs(w)
+    idx = run_index(w, d_in)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+
+
+@pytest.mark.parametrize("where", ["first", "last", "both"])
+def test_decode_shaped_build_errors(where, build_path):
+    w = _decode_case(9700, 12, 3, 8, 16, 4, 4, 2, 16, 0.1, 0.1, 0.0)
+    msb = w.max_pages // (w.block_size // w.page_size)
+    d = dev_inputs(w)
+    _print_case("decode_shaped_errors", where=where, path=build_path)
+    sel = w.selected.copy()
+    flat = sel.reshape(-1)
+    if where in ("first", "both"):
+        flat[5] = msb
+    if where in ("last", "both"):
+        flat[-3] = -7
+    got = _device_error(w, d, sel=torch.from_numpy(sel).cuda())
+    ref = _oracle_error(w, selected=sel)
+    assert (got.kind, got.expected, got.got) == (ref.kind, ref.expected, ref.got)
+    # a page id past the pool in a touched page of a kept block (a later
+    # head's entry, so that the last head's check must see it)
+    tbl = w.block_tables.copy()
+    q, h, r = 7, 2, int(np.nonzero(w.selected[7, 2] >= 0)[0][0])
+    v = int(w.selected[q, h, r])
+    ppb = w.block_size // w.page_size
+    tbl[q, v * ppb] = w.k_pages.shape[0] + 5
+    got = _device_error(w, d, bt=torch.from_numpy(tbl).cuda())
+    ref = _oracle_error(w, block_tables=tbl)
+    assert (got.kind, got.what, got.expected, got.got) == (ref.kind, ref.what, ref.expected, ref.got)
