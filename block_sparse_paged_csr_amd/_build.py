@@ -18,9 +18,14 @@ SOURCES = ["sa_api.hip", "sa_index.hip", "sa_forward.hip", "sa_forward_wave.hip"
 
 # Packed fp32 VALU forms are kept out of the generated code; the compiler
 # only warns on the host pass that it does not know the feature.
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-command-line-argument"]
+# Per-file flags. The MFMA kernels keep their matrix accumulators in ordinary
+# VGPRs: the chunked kernel rescales its output accumulators between chunks,
+# which in accumulation registers would cost a copy each way (the other
+# kernels of that file compile to the same code either way).
+FILE_FLAGS = {"sa_forward_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -31,15 +36,37 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    """Compile every source to an object (in parallel, each with its own
+    flags), then link the shared library."""
+    import tempfile
+    names = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    with tempfile.TemporaryDirectory(prefix="sa_build_") as odir:
+        procs, objs = [], []
+        for name in names:
+            obj = os.path.join(odir, name + ".o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(name, []), *extra_flags, "-c",
+                   os.path.join(CSRC, name), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                 text=True)))
+            objs.append(obj)
+        failed = []
+        for name, p in procs:
+            out, _ = p.communicate()
+            if p.returncode != 0:
+                sys.stderr.write(out)
+                failed.append(name)
+        if failed:
+            raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -237,8 +237,17 @@ sa_status sa_index_plan(int64_t tq, int32_t hkv, int32_t topk, int32_t batch, in
   idx->max_edges = max_edges;
   idx->cap_edges = sa::kCapRows / qhead > 0 ? sa::kCapRows / qhead : 1;
   if (idx->cap_edges > sa::kCapUnitEdges) idx->cap_edges = sa::kCapUnitEdges;
-  const bool mfma_ok = head_dim == sa::kMfmaHeadDim && block_size <= sa::kMfmaMaxBlock &&
+  const bool mfma_ok = ((head_dim == sa::kMfmaHeadDim && block_size <= sa::kMfmaMaxBlock) ||
+                        sa::mfma_general_fits(head_dim, block_size)) &&
                        sa::mfma_enabled();
+  // The chunked kernel holds one 32-row tile a wave across a block's chunks:
+  // for blocks of more than one chunk a unit takes at most a workgroup's
+  // tiles, so that each chunk is gathered once a unit.
+  if (mfma_ok && sa::mfma_general_fits(head_dim, block_size) &&
+      block_size > sa::mfma_general_chunk_keys(head_dim, block_size)) {
+    const int32_t cap = sa::mfma_general_tile_rows(head_dim) / qhead;
+    idx->cap_edges = cap < 1 ? 1 : (cap < idx->cap_edges ? cap : idx->cap_edges);
+  }
   // Where the one-wave-per-unit kernel fits (head_dim 128, blocks of at most
   // 64 keys, qhead <= 16) it takes every slot: a slot with more than 16 rows
   // becomes several 16-row units that read the same block close together in

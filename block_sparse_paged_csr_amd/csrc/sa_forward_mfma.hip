@@ -69,23 +69,24 @@ __device__ __forceinline__ void lane_key_bits(const uint32_t* valid, int half, u
 
 // S^T = K . Q^T over d for the lane's row (lane % 32); the K operands of
 // each step are read one step ahead.
-template <int NKB>
-__device__ __forceinline__ void tile_scores(const float* sk, const float4 (&qr)[16], int lr, int half,
+template <int NKB, int D = kD>
+__device__ __forceinline__ void tile_scores(const float* sk, const float4 (&qr)[D / 8], int lr, int half,
                                             floatx16 (&sacc)[NKB]) {
+  constexpr int KP = D + 4, M4 = D / 8;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
   float4 kc[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
-    kc[kb] = *reinterpret_cast<const float4*>(&sk[(kb * 32 + lr) * kKPitch + half * 64]);
+    kc[kb] = *reinterpret_cast<const float4*>(&sk[(kb * 32 + lr) * KP + half * (D / 2)]);
   __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
 #pragma unroll
-  for (int m4 = 0; m4 < 16; ++m4) {
+  for (int m4 = 0; m4 < M4; ++m4) {
     float4 kn[NKB];
-    if (m4 < 15) {
+    if (m4 < M4 - 1) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        kn[kb] = *reinterpret_cast<const float4*>(&sk[(kb * 32 + lr) * kKPitch + half * 64 + (m4 + 1) * 4]);
+        kn[kb] = *reinterpret_cast<const float4*>(&sk[(kb * 32 + lr) * KP + half * (D / 2) + (m4 + 1) * 4]);
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -95,9 +96,9 @@ __device__ __forceinline__ void tile_scores(const float* sk, const float4 (&qr)[
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[kb].w, qr[m4].w, sacc[kb], 0, 0, 0);
     }
     // the next step's LDS reads go out before this step's products
-    if (m4 < 15) __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
+    if (m4 < M4 - 1) __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
     __builtin_amdgcn_sched_group_barrier(0x0008, 4 * NKB, 0);
-    if (m4 < 15) {
+    if (m4 < M4 - 1) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
     }
@@ -185,50 +186,54 @@ __device__ __forceinline__ void tile_softmax(floatx16 (&sacc)[NKB], bool full, c
 
 // O^T = V^T . P^T; the k pair of MFMA (kb, r) is keys kappa and kappa + 4.
 // The V operands of each pair of r are read one pair ahead.
-template <int NKB>
+template <int NKB, int D = kD>
 __device__ __forceinline__ void tile_pv(const float* sv, const floatx16 (&sacc)[NKB], int lr, int half,
-                                        floatx16 (&oacc)[kD / 32]) {
+                                        floatx16 (&oacc)[D / 32], bool accumulate = false) {
+  constexpr int VP = D + 8;
+  if (!accumulate) {
 #pragma unroll
-  for (int db = 0; db < kD / 32; ++db) oacc[db] = zero16();
-  float vc[2][kD / 32];
-  auto read_v = [&](int r0, float (&dst)[2][kD / 32]) __attribute__((always_inline)) {
+    for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
+  }
+  float vc[2][D / 32];
+  auto read_v = [&](int r0, float (&dst)[2][D / 32]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = r0 + j, kb = r / 16, rr = r % 16;
-      const float* vrow = &sv[(kb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4)) * kVPitch + lr];
+      const float* vrow = &sv[(kb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4)) * VP + lr];
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db) dst[j][db] = vrow[db * 32];
+      for (int db = 0; db < D / 32; ++db) dst[j][db] = vrow[db * 32];
     }
   };
   read_v(0, vc);
-  __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
+  __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (D / 32), 0);
 #pragma unroll
   for (int r0 = 0; r0 < 16 * NKB; r0 += 2) {
-    float vn[2][kD / 32];
+    float vn[2][D / 32];
     if (r0 + 2 < 16 * NKB) read_v(r0 + 2, vn);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int db = 0; db < kD / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vc[j][db], sacc[(r0 + j) / 16][(r0 + j) % 16],
                                                         oacc[db], 0, 0, 0);
-    if (r0 + 2 < 16 * NKB) __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (kD / 32), 0);
-    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * (kD / 32), 0);
+    if (r0 + 2 < 16 * NKB) __builtin_amdgcn_sched_group_barrier(0x0100, 2 * (D / 32), 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * (D / 32), 0);
     if (r0 + 2 < 16 * NKB) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int db = 0; db < kD / 32; ++db) vc[j][db] = vn[j][db];
+        for (int db = 0; db < D / 32; ++db) vc[j][db] = vn[j][db];
     }
   }
 }
 
 // The tile's partial row `row` of the unit (o unnormalised, m in natural-log units).
+template <int D = kD>
 __device__ __forceinline__ void tile_store(const FwdArgs& A, int64_t row0, int32_t row, int half,
-                                           const floatx16 (&oacc)[kD / 32], float mb2, float sum) {
-  float* op = A.o + (row0 + row) * kD + 4 * half;
+                                           const floatx16 (&oacc)[D / 32], float mb2, float sum) {
+  float* op = A.o + (row0 + row) * D + 4 * half;
 #pragma unroll
-  for (int db = 0; db < kD / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       *reinterpret_cast<float4*>(op + db * 32 + 8 * g) =
@@ -713,6 +718,200 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
   wait_vm<0>();
 }
 
+// Other geometries on the matrix cores: head_dim 64, 128 or 256 and blocks of
+// any size (for head_dim 128, those of more than 128 keys). The block goes
+// through LDS in chunks of 32 * NKB keys, one after the other; a 32-row tile
+// keeps its row max, row sum and unnormalised output in registers across the
+// chunks and rescales them when a later chunk raises the max (the online
+// softmax of the combine, here inside one block), so the partials are those
+// of the whole block: max over its alive scores, the sum of exp(s - max) and
+// the weighted sum of V rows. Same tile layout as above (S^T = K . Q^T,
+// O^T = V^T . P^T on v_mfma_f32_32x32x2f32), with the q row and the output
+// accumulators held across the chunks; head_dim 128 and 256 run four waves a
+// workgroup (one a SIMD) for their registers, head_dim 64 eight. The build caps the units of
+// multi-chunk blocks at one tile a wave, so each chunk is gathered once a
+// unit; a one-chunk block is gathered once for all of a unit's tiles. The
+// gathers go through registers (16-bit pages are converted there).
+template <int D, int NKB, int WAVES, int KVF>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES == 4 ? 1 : 2)))
+void k_fwd_mfma_gen(IndexPtrs P, FwdArgs A) {
+  constexpr int kThreads = WAVES * 64;
+  constexpr int C = NKB * 32;                       // keys a chunk
+  constexpr int KP = D + 4, VP = D + 8;             // LDS row pitches (floats), as above
+  constexpr int kIters = C * (D / 4) / kThreads;    // gather float4 per thread (K and V each)
+  static_assert(C * (D / 4) % kThreads == 0 && kThreads % (D / 4) == 0, "gather tiling");
+  __shared__ __align__(16) float s_k[C * KP];
+  __shared__ __align__(16) float s_v[C * VP];
+  __shared__ int64_t s_off[C];
+  __shared__ int32_t s_qid[kMaxUnitEdges];
+  __shared__ uint32_t s_valid[NKB];
+
+  const DevHeader* hdr = P.hdr;
+  if (hdr->status != SA_OK) return;
+  const int32_t num_units = hdr->num_units_mfma;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int lr = lane & 31, half = lane >> 5;
+  const int32_t qhead = A.qhead;
+  const int64_t page_stride = (int64_t)A.hkv * A.page_size * D;
+  const float c2 = A.scale_log2;
+  const int32_t nchunks = (A.block_size + C - 1) / C;
+
+  // row offsets and validity bits of chunk c's keys (key c*C + i of the block)
+  auto chunk_meta = [&](const Unit& U, int32_t nkeys, int32_t c) {
+    for (int i = tid; i < C; i += kThreads) {
+      const int32_t key = c * C + i;
+      int64_t off = -1;
+      if (key < nkeys) {
+        const int32_t pgl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
+        const int32_t page = A.block_tables[(int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb + pgl];
+        if (page >= 0 && page < A.num_pages)
+          off = (int64_t)page * page_stride + (int64_t)U.h * A.page_size * D + (int64_t)(key - pgl * A.page_size) * D;
+      }
+      s_off[i] = off;
+      const uint64_t bits = __ballot(off >= 0);
+      if ((lane & 31) == 0) s_valid[i >> 5] = (uint32_t)(bits >> (lane & 32));
+    }
+  };
+  // the chunk's K and V rows into LDS (zero rows where a key has none), in
+  // batches of kBatch float4 of each, so that the registers they take stay
+  // few next to the q row and the output held across the chunks
+  constexpr int kBatch = kIters < 4 ? kIters : 4;
+  static_assert(kIters % kBatch == 0, "gather batches");
+  auto gather = [&]() {
+    const int c4 = tid % (D / 4);
+#pragma unroll
+    for (int i0 = 0; i0 < kIters; i0 += kBatch) {
+      float4 kv[kBatch], vv[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t off = s_off[(tid + (i0 + i) * kThreads) / (D / 4)];
+        kv[i] = off >= 0 ? load_kv4<KVF>(A.k, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vv[i] = off >= 0 ? load_kv4<KVF>(A.v, off + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int key = (tid + (i0 + i) * kThreads) / (D / 4);
+        *reinterpret_cast<float4*>(&s_k[key * KP + c4 * 4]) = kv[i];
+        *reinterpret_cast<float4*>(&s_v[key * VP + c4 * 4]) = vv[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);    // one batch in registers at a time
+    }
+  };
+
+  for (int32_t u = blockIdx.x; u < num_units; u += gridDim.x) {
+    const Unit U = P.units_mfma[u];
+    const int64_t block_start = (int64_t)U.blk * A.block_size;
+    int64_t block_end = block_start + A.block_size;
+    block_end = block_end < U.lk ? block_end : (int64_t)U.lk;
+    const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
+    const int32_t n_e = U.e1 - U.e0;
+    const int32_t rows = n_e * qhead;
+    const int64_t row0 = (int64_t)U.e0 * qhead;
+    const int32_t ntiles = (rows + 31) / 32;
+    const int32_t rounds = (ntiles + WAVES - 1) / WAVES;
+
+    __syncthreads();                                  // the previous unit's LDS reads are done
+    for (int e = tid; e < n_e; e += kThreads) s_qid[e] = P.edges[2 * (int64_t)(U.e0 + e)];
+    if (nchunks == 1) {
+      chunk_meta(U, nkeys, 0);
+      __syncthreads();
+      gather();
+    }
+    __syncthreads();
+
+    for (int32_t rd = 0; rd < rounds; ++rd) {
+      const int32_t tile = rd * WAVES + wv;
+      const bool has = tile < ntiles;
+      const int32_t row = tile * 32 + lr;
+      const bool row_ok = row < rows;
+      // q of the lane's row (rows past the unit read its last row; never stored)
+      float4 qr[D / 8];
+      int32_t qi = 0;
+      if (has) {
+        const int32_t rr = row < rows ? row : rows - 1;
+        qi = s_qid[rr / qhead];
+        const float* qp = A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + rr % qhead) * D + half * (D / 2);
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+      }
+      // last alive key of the lane's row within the block (causal bound, valid range)
+      int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
+      klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
+      floatx16 oacc[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
+      float m_run = -INFINITY, l_run = 0.f;           // base-2, scaled units
+
+      for (int32_t c = 0; c < nchunks; ++c) {
+        if (nchunks > 1) {
+          __syncthreads();                            // the previous chunk's LDS reads are done
+          chunk_meta(U, nkeys, c);
+          __syncthreads();
+          gather();
+          __syncthreads();
+        }
+        if (!has) continue;
+        uint32_t vm[NKB];
+        bool all_rows;
+        lane_key_bits<NKB>(s_valid, half, vm, all_rows);
+        const int64_t kl = klim - (int64_t)c * C;      // last alive key index within this chunk
+        const int32_t kmaxh = (int32_t)(kl < -1 ? -1 : (kl > C - 1 ? C - 1 : kl)) - 4 * half;
+        const bool full = __all(!row_ok || kl >= C - 1) && all_rows;
+        floatx16 sacc[NKB];
+        tile_scores<NKB, D>(s_k, qr, lr, half, sacc);
+        // scaled scores (dead keys -inf), the chunk's max, and the running
+        // max, sum and output brought to the new max
+        float ext = -INFINITY;
+        if (full) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              sacc[kb][r] *= c2;
+              ext = fmaxf(ext, sacc[kb][r]);
+            }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            uint32_t w = vm[kb];
+            asm volatile("" : "+v"(w));
+            const uint32_t aw = w & keys_upto(kmaxh - kb * 32);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              sacc[kb][r] = ((aw >> r) & 1u) ? sacc[kb][r] * c2 : -INFINITY;
+              ext = fmaxf(ext, sacc[kb][r]);
+            }
+          }
+        }
+        ext = fmaxf(ext, __shfl_xor(ext, 32, 64));
+        const float m_new = fmaxf(m_run, ext);
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
+        const float nref = none ? 0.f : -m_new;
+        float sum4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(sacc[kb][r] + nref);           // exp2(-inf) = 0
+            sacc[kb][r] = p;
+            sum4[r & 3] += p;
+          }
+        float sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
+        sum += __shfl_xor(sum, 32, 64);
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        tile_pv<NKB, D>(s_v, sacc, lr, half, oacc, true);
+      }
+      if (has && row_ok) tile_store<D>(A, row0, row, half, oacc, m_run, l_run);
+    }
+  }
+}
+
 // Blocks of up to 64 keys: 16-row tiles on v_mfma_f32_16x16x4f32, so that
 // units of 17..64 rows (most units of mixed batches) keep 2..4 waves busy.
 // The block's K and V are staged in LDS once per unit as above; each wave then
@@ -1007,14 +1206,53 @@ hipError_t launch_mfma_dma(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, 
   return hipGetLastError();
 }
 
+template <int D, int NKB, int WAVES>
+hipError_t launch_mfma_gen(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+  auto launch = [&](auto kernel) -> hipError_t {
+    static thread_local int per_cu = 0;
+    if (per_cu == 0) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, WAVES * 64, 0) != hipSuccess || n < 1) n = 1;
+      per_cu = n;
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)per_cu * cus), dim3(WAVES * 64), 0, s, P, a);
+    return hipGetLastError();
+  };
+  switch (a.kv_format) {
+    case SA_KV_BF16: return launch(k_fwd_mfma_gen<D, NKB, WAVES, SA_KV_BF16>);
+    case SA_KV_F16: return launch(k_fwd_mfma_gen<D, NKB, WAVES, SA_KV_F16>);
+    default: return launch(k_fwd_mfma_gen<D, NKB, WAVES, SA_KV_F32>);
+  }
+}
+
 }  // namespace
 
 bool mfma_enabled() { return true; }
 
+bool mfma_general_fits(int head_dim, int block_size) {
+  return (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+         !(head_dim == kD && block_size <= kMaxKeys);
+}
+
+int mfma_general_tile_rows(int head_dim) { return head_dim == 64 ? 8 * 32 : 4 * 32; }
+
+int mfma_general_chunk_keys(int head_dim, int block_size) {
+  if (head_dim == 256) return block_size <= 32 ? 32 : 64;
+  if (head_dim == 64) return block_size <= 64 ? 64 : 128;
+  return 128;
+}
+
 hipError_t launch_forward_mfma(const sa_index* idx, const FwdArgs& a, hipStream_t s,
                                unsigned grid) {
-  if (a.head_dim != kD || a.block_size > kMaxKeys) return hipErrorInvalidValue;
   const IndexPtrs P = index_ptrs(idx);
+  if (mfma_general_fits(a.head_dim, a.block_size)) {
+    const int chunk = mfma_general_chunk_keys(a.head_dim, a.block_size);
+    if (a.head_dim == 64) return chunk == 64 ? launch_mfma_gen<64, 2, 8>(P, a, s, grid)
+                                             : launch_mfma_gen<64, 4, 8>(P, a, s, grid);
+    if (a.head_dim == 128) return launch_mfma_gen<128, 4, 4>(P, a, s, grid);
+    return chunk == 32 ? launch_mfma_gen<256, 1, 4>(P, a, s, grid) : launch_mfma_gen<256, 2, 4>(P, a, s, grid);
+  }
+  if (a.head_dim != kD || a.block_size > kMaxKeys) return hipErrorInvalidValue;
   const int nkb = (a.block_size + 31) / 32;
   if (nkb <= 1) return launch_mfma16_t<1>(P, a, s, grid);
   if (nkb <= 2) return launch_mfma16_t<2>(P, a, s, grid);

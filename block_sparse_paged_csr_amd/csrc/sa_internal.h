@@ -187,6 +187,13 @@ ScratchLayout scratch_layout(const sa_index* idx);
 
 // Whether the MFMA forward kernel is part of the library.
 bool mfma_enabled();
+// The chunked MFMA kernel: head_dim 64, 128 or 256 and blocks the fixed
+// kernels do not take (head_dim 128 with blocks of up to 128 keys); rows of
+// one tile a wave (the unit cap for blocks of more than one chunk) and keys
+// a chunk.
+bool mfma_general_fits(int head_dim, int block_size);
+int mfma_general_tile_rows(int head_dim);
+int mfma_general_chunk_keys(int head_dim, int block_size);
 // Compute units of the current device (cached per host thread).
 unsigned cu_count();
 

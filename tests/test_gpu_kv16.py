@@ -123,14 +123,18 @@ def test_ragged_workload_bf16_sampled():
 
 
 # Geometries of the other forward kernels: the wavefront kernel (head_dim
-# other than 128), the 16-row MFMA kernel (blocks <= 64 keys, qhead > 16) and
-# the 32-row MFMA kernel (blocks of 96 / 128 keys).
+# other than 128), the 16-row MFMA kernel (blocks <= 64 keys, qhead > 16),
+# the 32-row MFMA kernel (blocks of 96 / 128 keys) and the chunked MFMA
+# kernel (head_dim 64 with 256-key blocks, 128 with 256, 256 with 128).
 OTHER = [
     dict(head_dim=32, qhead=2, page_size=4, pages_per_block=2, qo_max=6, kv_max=120, topk=4),
     dict(head_dim=64, qhead=4, page_size=8, pages_per_block=4, qo_max=6, kv_max=300, topk=5),
     dict(head_dim=128, qhead=20, page_size=16, pages_per_block=4, qo_max=200, kv_max=600, topk=6),
     dict(head_dim=128, qhead=8, page_size=32, pages_per_block=4, qo_max=200, kv_max=1200, topk=6),
     dict(head_dim=128, qhead=4, page_size=32, pages_per_block=3, qo_max=150, kv_max=900, topk=5),
+    dict(head_dim=64, qhead=8, page_size=32, pages_per_block=8, qo_max=80, kv_max=1500, topk=4),
+    dict(head_dim=128, qhead=8, page_size=64, pages_per_block=4, qo_max=80, kv_max=1500, topk=4),
+    dict(head_dim=256, qhead=8, page_size=16, pages_per_block=8, qo_max=50, kv_max=700, topk=4),
 ]
 
 

@@ -149,10 +149,11 @@ def test_random_d128_split_units(seed):
     _check_output(w, out, lse)
 
 
-# Head dims away from 128 take the wavefront-reduction kernel, built for
-# head_dim/4 rounded up to a power of two (1 .. 64 float4 columns): dims
-# that are not a power of two mask the padded columns, and head_dim 256 with
-# 16 GQA lanes is the largest qhead * head_dim the library takes (4096).
+# Head dims other than 64, 128 and 256 take the wavefront-reduction kernel
+# only, built for head_dim/4 rounded up to a power of two (1 .. 64 float4
+# columns): dims that are not a power of two mask the padded columns, and
+# head_dim 256 with 16 GQA lanes is the largest qhead * head_dim the library
+# takes (4096; its slots of 32 rows or more take the chunked MFMA kernel).
 WAVE_DIMS = [(4, 3), (12, 5), (100, 2), (132, 3), (256, 16), (256, 1), (40, 7), (252, 4)]
 
 
@@ -167,7 +168,8 @@ def test_random_head_dims_wave_kernel(case):
     idx = run_index(w, d_in)
     ref = oracle_index(w)
     info, arrs = assert_index_equal(idx, ref)
-    assert info["num_units_mfma"] == 0
+    if d not in (64, 128, 256):
+        assert info["num_units_mfma"] == 0
     check_units(arrs, info, ref, idx.c.cap_edges, w)
     out, lse = run_attention(w, d_in)
     _check_output(w, out, lse)
@@ -220,6 +222,32 @@ def test_random_d128_wide_gqa_mfma_units(seed):
     _check_output(w, out, lse)
 
 
+# The chunked MFMA kernel end to end: head_dim 64, 128 and 256 with blocks
+# of one chunk, several chunks and a partial last chunk (block sizes that are
+# not a multiple of the chunk), page holes, ids past the used length, GQA
+# widths up to 16 lanes and either causal mode; units of multi-chunk blocks
+# capped at one tile a wave. (head_dim, page_size, pages_per_block, qhead)
+GENERAL_GEOM = [(64, 16, 4, 8), (64, 32, 8, 4), (64, 48, 4, 16), (128, 64, 3, 8), (128, 32, 8, 4),
+                (256, 16, 2, 16), (256, 32, 2, 8), (256, 16, 6, 4), (128, 80, 2, 16), (64, 8, 4, 2)]
+
+
+@pytest.mark.parametrize("case", range(len(GENERAL_GEOM)))
+def test_random_general_mfma(case):
+    d, ps, ppb, qhead = GENERAL_GEOM[case]
+    w = W.make_random(7700 + case, batch=1 + case % 3, qo_max=40 if d == 256 else 70,
+                      kv_max=ps * ppb * 6, hkv=1 + case % 2, qhead=qhead, head_dim=d,
+                      page_size=ps, pages_per_block=ppb, topk=3 + case % 3, causal=case % 2 == 1)
+    _print_case("random_general_mfma", idx=case, head_dim=d, bs=w.block_size, qhead=qhead, tq=w.tq)
+    d_in = dev_inputs(w)
+    idx = run_index(w, d_in)
+    ref = oracle_index(w)
+    info, arrs = assert_index_equal(idx, ref)
+    assert info["num_units_mfma"] > 0
+    check_units(arrs, info, ref, idx.c.cap_edges, w)
+    out, lse = run_attention(w, d_in)
+    _check_output(w, out, lse)
+
+
 # Partial-level parity on every forward kernel: (o, m, l) per edge and lane
 # against the oracle, so that the reference point m (which the combine cannot
 # see) is checked on each of them.
@@ -228,6 +256,10 @@ def test_random_d128_wide_gqa_mfma_units(seed):
 #   mfma16: head_dim 128, blocks <= 64 keys, qhead > 16: 16-row MFMA tiles
 #   mfma:   head_dim 128, blocks of 96 / 128 keys: 32-row MFMA tiles (slots
 #           under 32 rows take the wavefront kernel)
+#   gen64, gen128, gen256: the chunked MFMA kernel on head_dim 64 (blocks of
+#           64, 128, 256 keys: one or two 128-key chunks), 128 (blocks of 192
+#           and 256 keys) and 256 (blocks of 32, 64, 128 keys: 32- and 64-key
+#           chunks), where a later chunk can raise a row's max
 PARTIAL_KERNELS = {
     "wave": dict(head_dim=32, page_size=2, pages_per_block=(2, 3), qhead=(1, 2, 3),
                  qo_max=4, kv_max=48, topk=3),
@@ -237,6 +269,12 @@ PARTIAL_KERNELS = {
                    qo_max=40, kv_max=260, topk=3),
     "mfma": dict(head_dim=128, page_size=32, pages_per_block=(3, 4), qhead=(4, 8, 16),
                  qo_max=60, kv_max=600, topk=3),
+    "gen64": dict(head_dim=64, page_size=32, pages_per_block=(2, 4, 8), qhead=(4, 8, 16),
+                  qo_max=60, kv_max=900, topk=3),
+    "gen128": dict(head_dim=128, page_size=64, pages_per_block=(3, 4), qhead=(4, 8, 16),
+                   qo_max=60, kv_max=900, topk=3),
+    "gen256": dict(head_dim=256, page_size=16, pages_per_block=(2, 4, 8), qhead=(4, 8, 16),
+                   qo_max=50, kv_max=500, topk=3),
 }
 
 
@@ -256,7 +294,7 @@ def test_random_partials_match_kvouter_ref(kernel, seed):
     idx = run_index(w, d)
     ref = oracle_index(w)
     info, _ = assert_index_equal(idx, ref)
-    if kernel in ("mfma16", "mfma"):
+    if kernel in ("mfma16", "mfma") or kernel.startswith("gen"):
         assert info["num_units_mfma"] > 0, "no unit reached the MFMA kernel"
     else:
         assert info["num_units_mfma"] == 0
