@@ -50,7 +50,10 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default=DEFAULT_CONFIG,
-                   choices=["tiny", "decode", "prefill", "ragged", "skewed"])
+                   choices=["tiny", "decode", "prefill", "ragged", "skewed",
+                            "prefill_d64", "prefill_d256", "prefill_bs256"],
+                   help="one of the five workloads, or the prefill recipe at head_dim 64 / 256 "
+                        "or with 256-key blocks (the chunked MFMA kernel's geometries)")
     p.add_argument("--rotate", type=int, default=4, help="independent input batches cycled")
     p.add_argument("--kv-dtype", default="f32", choices=["f32", "bf16", "fp16"],
                    help="storage of the K/V pages (16-bit: sa_forward_kv16, fp32 arithmetic)")
@@ -402,18 +405,27 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def forward_kernels(w, fused=False):
+def forward_kernels(w, fused=False, kv_dtype="f32"):
     """The kernels one sa_forward launches for this geometry: the one-wave
     kernel alone where it fits (head_dim 128, blocks <= 64 keys, qhead <= 16),
-    else the wavefront-reduction kernel and the MFMA kernel; with `fused`, the
-    one kernel of sa_forward_combine."""
+    else the wavefront-reduction kernel and an MFMA kernel (16-row tiles for
+    head_dim 128 and blocks <= 64 keys; 32-row tiles with direct-to-LDS
+    gathers for fp32 pages and blocks of 65..128 keys, with register gathers
+    for 16-bit pages; the chunked kernel for head_dim 64 / 256 and larger
+    blocks); with `fused`, the one kernel of sa_forward_combine."""
     qhead = w.hq // w.hkv
     nch = (w.block_size + 15) // 16
     if fused:
         return f"k_fwd_fused<{nch}>", None
     if w.head_dim == 128 and w.block_size <= 64 and qhead <= 16:
         return f"k_fwd_small<{nch}>", None
-    return "k_fwd_wave", "k_fwd_mfma"
+    if w.head_dim == 128 and w.block_size <= 64:
+        return "k_fwd_wave", "k_fwd_mfma16"
+    if w.head_dim == 128 and w.block_size <= 128:
+        return "k_fwd_wave", "k_fwd_mfma_dma" if kv_dtype == "f32" else "k_fwd_mfma"
+    if w.head_dim in (64, 128, 256):
+        return "k_fwd_wave", "k_fwd_mfma_gen"
+    return "k_fwd_wave", None
 
 
 def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32", fused=False):
@@ -424,7 +436,7 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32", fused=False
     fp32 MFMA. `traffic` comes from the committed FETCH_SIZE + WRITE_SIZE
     summary for this workload, and only while the kernel's source is the one
     the counters were taken on."""
-    small, mfma = forward_kernels(w, fused)
+    small, mfma = forward_kernels(w, fused, kv_dtype)
     if kv_dtype != "f32":
         small = small.replace(">", f", {kv_dtype}>")
     ridge = FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)

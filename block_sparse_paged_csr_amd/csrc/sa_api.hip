@@ -138,6 +138,8 @@ ScratchLayout scratch_layout(const sa_index* idx) {
   o = align256(o + sizeof(ChunkAgg) * (size_t)idx->hkv * (size_t)scan_chunks(idx->nbs));
   L.units_sorted = o;
   o = align256(o + sizeof(Unit) * (size_t)idx->max_units);
+  L.sort_hist = o;
+  o = align256(o + sizeof(int32_t) * ((size_t)kSortGrid * kSortBuckets + 1));
   L.end = o;
   return L;
 }
@@ -166,6 +168,7 @@ IndexPtrs index_ptrs(const sa_index* idx) {
   P.agg = reinterpret_cast<HeadAgg*>(b + L.agg);
   P.chunk_agg = reinterpret_cast<ChunkAgg*>(b + L.chunk_agg);
   P.units_sorted = reinterpret_cast<Unit*>(b + L.units_sorted);
+  P.sort_hist = reinterpret_cast<int32_t*>(b + L.sort_hist);
   return P;
 }
 

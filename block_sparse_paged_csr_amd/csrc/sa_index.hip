@@ -123,6 +123,7 @@ __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
     h->num_slots = 0;
     h->queue_mfma = 0;
     h->done_mfma = 0;
+    P.sort_hist[kSortGrid * kSortBuckets] = 0;   // the unit sort's counter
     h->queue_wave = 0;
     h->done_wave = 0;
     h->geom[0] = (int32_t)A.tq;
@@ -1185,6 +1186,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
       hd->num_slots = (int64_t)s_base_ns + ns_h;
       hd->queue_mfma = 0;
       hd->done_mfma = 0;
+      P.sort_hist[kSortGrid * kSortBuckets] = 0;   // the unit sort's counter
       hd->queue_wave = 0;
       hd->done_wave = 0;
       hd->geom[0] = (int32_t)A.tq;
@@ -1222,12 +1224,13 @@ inline unsigned grid_for(int64_t n, int per) {
 // bucket in any order), for the 32-row forward's static assignment: dealt in
 // a snake over the workgroups, a size-sorted list gives every workgroup a
 // near-equal share without a queue, and each workgroup knows its next units
-// in advance. One workgroup: an LDS histogram, its scan, an LDS cursor per
-// bucket. Several units a thread per pass, loads first, so that each pass
-// costs one round trip per batch.
-constexpr int kSortThreads = 1024;
-constexpr int kSortBatch = 4;
-constexpr int kSortBuckets = 64;                 // units hold at most 2048 rows = 64 tiles
+// in advance. A counting sort in two launches: kSortGrid workgroups count
+// their ranges of units into per-workgroup bucket counts, and the last one
+// to finish turns the counts into bucket-major offsets; then each workgroup
+// moves its units to their places. (The order inside a bucket may differ
+// from run to run; each unit's partials do not depend on where it runs.)
+constexpr int kSortThreads = 256;
+constexpr int kSortUnitsPerThread = 8;
 
 __device__ inline int unit_bucket(int32_t e0, int32_t e1, int32_t qhead) {
   const int32_t tiles = ((e1 - e0) * qhead + 31) / 32;
@@ -1235,51 +1238,100 @@ __device__ inline int unit_bucket(int32_t e0, int32_t e1, int32_t qhead) {
   return kSortBuckets - t;                       // bucket 0: the largest units
 }
 
-__global__ __launch_bounds__(kSortThreads) void k_unit_sort(IndexPtrs P, BuildArgs A) {
+// units [u0, u1) of workgroup g of the sort's grid
+__device__ inline void sort_range(int32_t n, int32_t& u0, int32_t& u1) {
+  const int32_t per = (n + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
+  u0 = (int32_t)blockIdx.x * per;
+  u1 = u0 + per < n ? u0 + per : n;
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_unit_count(IndexPtrs P, BuildArgs A) {
   __shared__ int32_t s_cnt[kSortBuckets];
-  __shared__ int32_t s_cur[kSortBuckets];
+  __shared__ bool s_last;
   if (P.hdr->status != SA_OK) return;            // a failed build: the forward does not run
   const int32_t n = P.hdr->num_units_mfma;
   const int tid = threadIdx.x;
   if (tid < kSortBuckets) s_cnt[tid] = 0;
   __syncthreads();
-  const int4* src = reinterpret_cast<const int4*>(P.units_mfma);   // a unit is two int4: (h, j, e0, e1), (b, blk, lk, delta)
-  for (int32_t base = 0; base < n; base += kSortThreads * kSortBatch) {
-    int4 v[kSortBatch];
+  int32_t u0, u1;
+  sort_range(n, u0, u1);
+  const int2* e01 = reinterpret_cast<const int2*>(P.units_mfma);   // (e0, e1): int2 2u + 1 of a unit
+  for (int32_t base = u0; base < u1; base += kSortThreads * kSortUnitsPerThread) {
+    int2 v[kSortUnitsPerThread];
 #pragma unroll
-    for (int k = 0; k < kSortBatch; ++k) {
+    for (int k = 0; k < kSortUnitsPerThread; ++k) {
       const int32_t u = base + k * kSortThreads + tid;
-      v[k] = u < n ? src[2 * (int64_t)u] : make_int4(0, 0, 0, 0);
+      v[k] = e01[4 * (int64_t)(u < u1 ? u : u0) + 1];
     }
 #pragma unroll
-    for (int k = 0; k < kSortBatch; ++k)
-      if (base + k * kSortThreads + tid < n) atomicAdd(&s_cnt[unit_bucket(v[k].z, v[k].w, A.qhead)], 1);
+    for (int k = 0; k < kSortUnitsPerThread; ++k)
+      if (base + k * kSortThreads + tid < u1) atomicAdd(&s_cnt[unit_bucket(v[k].x, v[k].y, A.qhead)], 1);
   }
   __syncthreads();
-  if (tid < 64) {                                // exclusive scan of the 64 counts in one wave
-    const int c = s_cnt[tid];
-    int incl = c;
+  int32_t* hist = P.sort_hist;                   // [bucket][workgroup], then the counter
+  if (tid < kSortBuckets) hist[tid * kSortGrid + blockIdx.x] = s_cnt[tid];
+  // the last workgroup to finish turns the counts into offsets
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int32_t done = atomicAdd(&hist[kSortGrid * kSortBuckets], 1);
+    s_last = done == (int32_t)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  // exclusive scan over (bucket, workgroup) in that order: thread t holds
+  // kSortGrid*64/256 consecutive counts
+  constexpr int kPer = kSortGrid * kSortBuckets / kSortThreads;
+  __shared__ int32_t s_part[kSortThreads];
+  int32_t c[kPer], sum = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off, 64);
-      if (tid >= off) incl += t;
-    }
-    s_cur[tid] = incl - c;
+  for (int k = 0; k < kPer; ++k) {
+    const int32_t i = tid * kPer + k;
+    const int32_t b = i / kSortGrid, g = i - b * kSortGrid;
+    c[k] = g < (int32_t)gridDim.x ? __hip_atomic_load(&hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    sum += c[k];
   }
+  s_part[tid] = sum;
   __syncthreads();
+  for (int off = 1; off < kSortThreads; off <<= 1) {    // inclusive scan of the partial sums
+    const int32_t t = tid >= off ? s_part[tid - off] : 0;
+    __syncthreads();
+    s_part[tid] += t;
+    __syncthreads();
+  }
+  int32_t run = s_part[tid] - sum;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    hist[tid * kPer + k] = run;
+    run += c[k];
+  }
+  if (tid == 0) hist[kSortGrid * kSortBuckets] = 0;      // the counter, for the next build
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_unit_place(IndexPtrs P, BuildArgs A) {
+  __shared__ int32_t s_cur[kSortBuckets];
+  if (P.hdr->status != SA_OK) return;
+  const int32_t n = P.hdr->num_units_mfma;
+  const int tid = threadIdx.x;
+  if (tid < kSortBuckets) s_cur[tid] = P.sort_hist[tid * kSortGrid + blockIdx.x];
+  __syncthreads();
+  int32_t u0, u1;
+  sort_range(n, u0, u1);
+  const int4* src = reinterpret_cast<const int4*>(P.units_mfma);    // a unit is two int4
   int4* dst = reinterpret_cast<int4*>(P.units_sorted);
-  for (int32_t base = 0; base < n; base += kSortThreads * kSortBatch) {
-    int4 lo[kSortBatch], hi[kSortBatch];
+  for (int32_t base = u0; base < u1; base += kSortThreads * kSortUnitsPerThread) {
+    int4 lo[kSortUnitsPerThread], hi[kSortUnitsPerThread];
 #pragma unroll
-    for (int k = 0; k < kSortBatch; ++k) {
+    for (int k = 0; k < kSortUnitsPerThread; ++k) {
       const int32_t u = base + k * kSortThreads + tid;
-      const int32_t uu = u < n ? u : 0;
+      const int32_t uu = u < u1 ? u : u0;
       lo[k] = src[2 * (int64_t)uu];
       hi[k] = src[2 * (int64_t)uu + 1];
     }
 #pragma unroll
-    for (int k = 0; k < kSortBatch; ++k) {
-      if (base + k * kSortThreads + tid < n) {
+    for (int k = 0; k < kSortUnitsPerThread; ++k) {
+      if (base + k * kSortThreads + tid < u1) {
         const int32_t pos = atomicAdd(&s_cur[unit_bucket(lo[k].z, lo[k].w, A.qhead)], 1);
         dst[2 * (int64_t)pos] = lo[k];
         dst[2 * (int64_t)pos + 1] = hi[k];
@@ -1296,10 +1348,21 @@ bool fused_build_fits(int64_t tq, int32_t topk, int64_t nbs, int32_t batch, int3
          fused_lds_bytes(tq, topk, nbs, batch) <= kFusedMaxLds;
 }
 
-// The 32-row MFMA forward for blocks of more than 64 keys walks the units in
-// size order (k_unit_sort); other geometries do not read that list.
-inline bool unit_sort_needed(const BuildArgs& a) {
-  return a.mfma_min_rows != INT32_MAX && a.block_size > 64;
+// The 32-row MFMA forward for head_dim 128 and blocks of 65..128 keys walks
+// the units in size order (the unit sort); other geometries do not read that
+// list. (A 16-bit forward on such an index takes the register-gather kernel,
+// which pulls units from a queue.)
+inline bool unit_sort_needed(const sa_index* idx, const BuildArgs& a) {
+  return a.mfma_min_rows != INT32_MAX && idx->head_dim == kMfmaHeadDim && a.block_size > 64 &&
+         a.block_size <= kMfmaMaxBlock;
+}
+
+// The sort's two launches; a grid of fewer workgroups than units.
+inline void launch_unit_sort(const sa_index* idx, const IndexPtrs& P, const BuildArgs& a, hipStream_t s) {
+  int64_t g = (idx->max_units + 1023) / 1024;
+  g = g < 1 ? 1 : (g > kSortGrid ? kSortGrid : g);
+  hipLaunchKernelGGL(k_unit_count, dim3((unsigned)g), dim3(kSortThreads), 0, s, P, a);
+  hipLaunchKernelGGL(k_unit_place, dim3((unsigned)g), dim3(kSortThreads), 0, s, P, a);
 }
 
 hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) {
@@ -1322,7 +1385,7 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
     }
     const size_t lds = fused_lds_bytes(a);
     hipLaunchKernelGGL(k_index_fused, dim3((unsigned)a.hkv), dim3(kFusedThreads), lds, s, P, a);
-    if (unit_sort_needed(a)) hipLaunchKernelGGL(k_unit_sort, dim3(1), dim3(kSortThreads), 0, s, P, a);
+    if (unit_sort_needed(idx, a)) launch_unit_sort(idx, P, a, s);
     return hipGetLastError();
   }
   const int64_t slots = (int64_t)a.hkv * a.nbs;
@@ -1364,7 +1427,7 @@ hipError_t launch_build(const sa_index* idx, const BuildArgs& a, hipStream_t s) 
   if (rank_grid > 8 * cu_count()) rank_grid = 8 * cu_count();
   hipLaunchKernelGGL(k_index_rank, dim3(rank_grid), dim3(256), (size_t)ra.rank_bitmap_words * 4, s,
                      P, ra);
-  if (unit_sort_needed(a)) hipLaunchKernelGGL(k_unit_sort, dim3(1), dim3(kSortThreads), 0, s, P, a);
+  if (unit_sort_needed(idx, a)) launch_unit_sort(idx, P, a, s);
   return hipGetLastError();
 }
 

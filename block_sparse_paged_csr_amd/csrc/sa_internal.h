@@ -82,7 +82,8 @@ struct ScratchLayout {
   size_t qinfo;      // int2  [tq]        (sequence b, resolved kv length lk_b) per query
   size_t agg;        // HeadAgg [hkv]     per-head totals published by the fused build
   size_t chunk_agg;  // ChunkAgg [hkv * scan_chunks(nbs)]  per-chunk sums of the slot scan
-  size_t units_sorted;  // Unit [max_units]  the MFMA units, largest first (k_unit_sort)
+  size_t units_sorted;  // Unit [max_units]  the MFMA units, largest first (unit sort)
+  size_t sort_hist;  // int32 [kSortGrid * 64 + 1] per-workgroup bucket counts, then offsets; a counter
   size_t end;
 };
 
@@ -94,6 +95,10 @@ struct alignas(64) HeadAgg {
   unsigned long long err;     // smallest error key seen by the head (~0ull: none)
   uint64_t flag;
 };
+
+// Workgroups of the MFMA unit sort (a counting sort over 64 size buckets).
+constexpr int kSortGrid = 256;
+constexpr int kSortBuckets = 64;                 // units hold at most 2048 rows = 64 tiles
 
 // Slots scanned by one workgroup of the multi-kernel build.
 constexpr int kScanChunkSlots = 2048;
@@ -134,6 +139,7 @@ struct IndexPtrs {
   HeadAgg* agg;
   ChunkAgg* chunk_agg;
   Unit* units_sorted;
+  int32_t* sort_hist;
 };
 
 struct BuildArgs {

@@ -161,11 +161,12 @@ def make_decode(seed: int = 1, with_kv: bool = True) -> Workload:
                     topk, 1.0 / math.sqrt(d), True)
 
 
-def make_prefill(seed: int = 2, with_kv: bool = True) -> Workload:
+def make_prefill(seed: int = 2, with_kv: bool = True, head_dim: int = 128,
+                 block_size: int = 128, name: str = "prefill") -> Workload:
     rng = np.random.Generator(np.random.PCG64(seed))
     B, qo, kv = 4, 1024, 16384
-    hq, hkv, d = 64, 8, 128
-    ps, bs, topk = 64, 128, 32
+    hq, hkv, d = 64, 8, head_dim
+    ps, bs, topk = min(64, block_size), block_size, 32
     max_pages = kv // ps
     num_pages = B * max_pages
     cu = np.arange(B + 1, dtype=np.int64) * qo
@@ -182,7 +183,7 @@ def make_prefill(seed: int = 2, with_kv: bool = True) -> Workload:
             ids = np.concatenate([[0], recent, rand])
             sel[q, h] = rng.permutation(ids)
     qv, kp, vp = _draw_qkv(rng, tq, hq, num_pages, hkv, ps, d, with_kv)
-    return Workload("prefill", qv, kp, vp, sel, tbl, cu, used, hq, hkv, d, bs, ps,
+    return Workload(name, qv, kp, vp, sel, tbl, cu, used, hq, hkv, d, bs, ps,
                     topk, 1.0 / math.sqrt(d), True)
 
 
@@ -256,6 +257,16 @@ _MAKERS = {
     "ragged": make_ragged,
     "skewed": make_skewed,
 }
+
+# The prefill recipe at other head dims and block sizes (the chunked MFMA
+# kernel's geometries): not among the five workloads, for measurement only.
+VARIANT_NAMES = ("prefill_d64", "prefill_d256", "prefill_bs256")
+_MAKERS.update({
+    "prefill_d64": lambda seed, with_kv: make_prefill(seed, with_kv, 64, 128, "prefill_d64"),
+    "prefill_d256": lambda seed, with_kv: make_prefill(seed, with_kv, 256, 64, "prefill_d256"),
+    "prefill_bs256": lambda seed, with_kv: make_prefill(seed, with_kv, 128, 256, "prefill_bs256"),
+})
+CONFIG_SEEDS.update({name: CONFIG_SEEDS["prefill"] for name in VARIANT_NAMES})
 
 
 def make_config(name: str, seed: Optional[int] = None, with_kv: bool = True) -> Workload:
