@@ -122,8 +122,16 @@ __device__ __forceinline__ uint32_t keys_upto(int32_t x) {
   const uint32_t lo = (1u << (4 * grp)) - 1u;
   return lo | (((1u << (w < 4u ? w : 4u)) - 1u) << (4 * grp));
 }
-template <int NKB>
-__device__ __forceinline__ void tile_softmax(floatx16 (&sacc)[NKB], bool full, const uint32_t (&vm)[NKB],
+//
+// kRaw: vm holds the block's validity words themselves (bit k: key 32kb + k
+// has a row), read where they are needed instead of kept as per-lane masks.
+// Accumulator r of the lane then stands for bit 8*(r/4) + r%4 of the word
+// shifted right by 4*half.
+__device__ __forceinline__ uint32_t bits_upto(int32_t x) {
+  return x < 0 ? 0u : (x >= 31 ? 0xffffffffu : (2u << x) - 1u);
+}
+template <int NKB, bool kRaw = false>
+__device__ __forceinline__ void tile_softmax(floatx16 (&sacc)[NKB], bool full, const uint32_t* vm, int half,
                                              int32_t kmaxh, float c2, float& mb2, float& sum) {
   const bool up = c2 >= 0.f;
   if (!full) {
@@ -133,10 +141,16 @@ __device__ __forceinline__ void tile_softmax(floatx16 (&sacc)[NKB], bool full, c
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       uint32_t w = vm[kb];
-      asm volatile("" : "+v"(w));
-      const uint32_t aw = w & keys_upto(kmaxh - kb * 32);
+      if (kRaw) {
+        const uint32_t aw = (w >> (4 * half)) & 0x0f0f0f0fu & bits_upto(kmaxh - kb * 32);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = ((aw >> r) & 1u) ? sacc[kb][r] : dead;
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = ((aw >> (8 * (r / 4) + r % 4)) & 1u) ? sacc[kb][r] : dead;
+      } else {
+        asm volatile("" : "+v"(w));
+        const uint32_t aw = w & keys_upto(kmaxh - kb * 32);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = ((aw >> r) & 1u) ? sacc[kb][r] : dead;
+      }
     }
   }
   float ext = up ? -INFINITY : INFINITY;
@@ -244,18 +258,169 @@ __device__ __forceinline__ void tile_store(const FwdArgs& A, int64_t row0, int32
   }
 }
 
-// NKB: 32-key blocks per KV block (block_size <= 32 * NKB); WAVES per workgroup.
+// ---- pieces of one 16-row tile on v_mfma_f32_16x16x4f32 (same LDS layout),
+// for the direct-to-LDS kernel below. Operand layout (lane li = lane % 16 of
+// lane group g = lane / 16):
+//   S^T[key, row]: MFMA t, component c takes d = 16t + 4g + c; lane (li, g)
+//                  gets row li, keys 16ch + 4g + r (r = 0..3) of 16-key chunk ch
+//   O^T[d, row]:   output row i of MFMA block db stands for d = 4i + (db & 3) + 64 (db >> 2)
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline floatx4 zero4v() {
+  floatx4 z;
+  z[0] = z[1] = z[2] = z[3] = 0.f;
+  return z;
+}
+
+// Raw scores of row li over the NCH 16-key chunks; q in qr[0..7] (d = 16t + 4g ..).
+template <int NCH>
+__device__ __forceinline__ void tile16_scores(const float* sk, const float4 (&qr)[16], int li, int g,
+                                              float (&s)[NCH][4]) {
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    floatx4 sa0 = zero4v(), sa1 = zero4v();
+    const float* kr = &sk[(16 * ch + li) * kKPitch + 4 * g];
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+      const float4 ka = *reinterpret_cast<const float4*>(kr + 16 * t);
+      const float4 kb = *reinterpret_cast<const float4*>(kr + 16 * (t + 1));
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[t].x, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.x, qr[t + 1].x, sa1, 0, 0, 0);
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[t].y, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.y, qr[t + 1].y, sa1, 0, 0, 0);
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[t].z, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.z, qr[t + 1].z, sa1, 0, 0, 0);
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[t].w, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.w, qr[t + 1].w, sa1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // bound how far LDS reads run ahead
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[ch][r] = sa0[r] + sa1[r];
+  }
+}
+
+// Mask, max and sum of row li as tile_softmax does for 32-row tiles: key
+// 16ch + 4g + r of the lane is alive iff its bit in the block's validity words
+// is set and it is at most kmax.
+template <int NCH>
+__device__ __forceinline__ void tile16_softmax(float (&s)[NCH][4], bool full, const uint32_t* valid, int g,
+                                               int32_t kmax, float c2, float& mb2, float& sum) {
+  const bool up = c2 >= 0.f;
+  if (!full) {
+    const float dead = up ? -INFINITY : INFINITY;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int32_t x = kmax - 16 * ch - 4 * g;   // keys r <= x of this group are in range
+      uint32_t w = (valid[ch >> 1] >> (16 * (ch & 1) + 4 * g)) & 15u;
+      w &= x < 0 ? 0u : (x >= 3 ? 15u : (2u << x) - 1u);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[ch][r] = ((w >> r) & 1u) ? s[ch][r] : dead;
+    }
+  }
+  float ext = up ? -INFINITY : INFINITY;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ext = up ? fmaxf(ext, s[ch][r]) : fminf(ext, s[ch][r]);
+#pragma unroll
+  for (int x = 16; x <= 32; x *= 2) {
+    const float other = __shfl_xor(ext, x, 64);
+    ext = up ? fmaxf(ext, other) : fminf(ext, other);
+  }
+  const bool none = up ? ext == -INFINITY : ext == INFINITY;
+  mb2 = none ? -INFINITY : ext * c2;
+  const float nref = none ? 0.f : -mb2;
+  float sum4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float p = __builtin_amdgcn_exp2f(fmaf(s[ch][r], c2, nref));
+      if (!full) p = fmaxf(p, 0.f);
+      s[ch][r] = p;
+      sum4[r] += p;
+    }
+  sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
+  sum += __shfl_xor(sum, 16, 64);
+  sum += __shfl_xor(sum, 32, 64);
+}
+
+// O^T = V^T . P^T over the NCH chunks; the k index of MFMA (ch, r) is key 16ch + 4g + r.
+template <int NCH>
+__device__ __forceinline__ void tile16_pv(const float* sv, const float (&s)[NCH][4], int li, int g,
+                                          floatx4 (&oacc)[8]) {
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float* vr = &sv[(16 * ch + 4 * g + r) * kVPitch + 4 * li];
+      const floatx4 v0 = *reinterpret_cast<const floatx4*>(vr);
+      const floatx4 v1 = *reinterpret_cast<const floatx4*>(vr + 64);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const floatx4 acc = (ch == 0 && r == 0) ? zero4v() : oacc[db];
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(db < 4 ? v0[db & 3] : v1[db & 3], s[ch][r], acc, 0, 0, 0);
+      }
+      if (r & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Row `row` of the unit from a 16-row tile: lane (li, g) holds d = 16g + 4v +
+// (db & 3) + 64 (db >> 2) in oacc[db][v].
+__device__ __forceinline__ void tile16_store(const FwdArgs& A, int64_t row0, int32_t row, int g,
+                                             const floatx4 (&oacc)[8], float mb2, float sum) {
+  float* dst = A.o + (row0 + row) * kD + 16 * g;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    *reinterpret_cast<floatx4*>(dst + 4 * v) = floatx4{oacc[0][v], oacc[1][v], oacc[2][v], oacc[3][v]};
+    *reinterpret_cast<floatx4*>(dst + 64 + 4 * v) = floatx4{oacc[4][v], oacc[5][v], oacc[6][v], oacc[7][v]};
+  }
+  if (g == 0) {
+    A.m[row0 + row] = mb2 * kLn2;
+    A.l[row0 + row] = sum;
+  }
+}
+
+// A unit's rows in 16-row quanta, dealt to the four SIMDs of the workgroup in
+// near-equal contiguous shares (the unit ends when its largest share does).
+// A share of q quanta is q / 2 32-row tiles and, for odd q, one 16-row tile
+// last. Waves w and w + 4 of a workgroup run on the same SIMD; share w % 4 is
+// theirs and they take its tiles alternately (a wave alone on the SIMD still
+// keeps the matrix pipe nearly busy, and 16-row tiles cost more per row).
+struct SimdShare {
+  int32_t start;     // first row of the share
+  int32_t npieces;   // tiles in the share
+  int32_t n32;       // 32-row tiles; tile n32, if any, is the 16-row one
+};
+__device__ __forceinline__ SimdShare simd_share(int32_t rows, int simd) {
+  const int32_t quanta = (rows + 15) >> 4, base = quanta >> 2, extra = quanta & 3;
+  const int32_t q = base + (simd < extra ? 1 : 0);
+  return SimdShare{16 * (simd * base + (simd < extra ? simd : extra)), (q >> 1) + (q & 1), q >> 1};
+}
+// The same deal seen from wave wv: its tile k starts 64k rows after its first
+// (same meaning of the fields, for the wave's own tiles).
+__device__ __forceinline__ SimdShare wave_share(int32_t rows, int wv) {
+  const SimdShare sh = simd_share(rows, wv & 3);
+  const int second = wv >> 2;
+  const int32_t n32 = sh.n32 > second ? (sh.n32 - second + 1) >> 1 : 0;
+  const bool with16 = sh.npieces > sh.n32 && sh.n32 >= second && ((sh.n32 - second) & 1) == 0;
+  return SimdShare{sh.start + 32 * second, n32 + (with16 ? 1 : 0), n32};
+}
+
+// NKB: 32-key blocks per KV block (block_size <= 32 * NKB); 16-bit pages (KVF).
 //
 // Each wave runs its tiles as a software pipeline so that the matrix pipe is
 // not left waiting on memory: the unit's query ids sit in LDS, and the next
-// tile's q rows (scaled by softmax_scale * log2 e as they load) are fetched
-// right after the current tile's QK products have read theirs, so their
-// round trip overlaps the softmax and the PV products. The LDS operands of
-// each group of matrix instructions are read one group ahead.
-template <int NKB, int WAVES, int KVF>
-__global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
-  constexpr int kWaves = WAVES;
-  constexpr int kThreads = WAVES * 64;
+// tile's q rows are fetched right after the current tile's QK products have
+// read theirs, so their round trip overlaps the softmax and the PV products.
+// The LDS operands of each group of matrix instructions are read one group
+// ahead. A unit's rows are dealt to the waves as in the direct-to-LDS kernel
+// below (wave_share), so both compute every row with the same tile shape.
+template <int NKB, int KVF>
+__global__ __launch_bounds__(512) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
+  constexpr int kWaves = 8;
+  constexpr int kThreads = kWaves * 64;
   constexpr int kKeys = NKB * 32;
   constexpr int kIters = kKeys * (kD / 4) / kThreads;   // gather float4 per thread (K and V each)
   static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
@@ -280,24 +445,34 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
   const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
   const float c2 = A.scale_log2;
 
-  // q row of tile row `row` (lanes 0-31 take d 0..63, lanes 32-63 d 64..127).
-  // A row past the unit reads the unit's last row instead: each row's scores,
-  // probabilities and output stay in that row's own lanes and such rows are
-  // never stored, so the loads need no branch and no select, and the compiler
-  // waits for them only where the QK products use them. The float4 groups
-  // [i0, i0 + 8) of the row are loaded.
-  auto q_row = [&](const Unit& U, int32_t rows, int32_t tile, int32_t* qi_out) -> const float* {
-    int32_t row = tile * 32 + lr;
+  // q of the lane's row in the piece that starts at row prow: a 32-row tile
+  // takes half of row prow + lane % 32 (float4 i at 4i), a 16-row tile row
+  // prow + lane % 16 at d = 16t + 4g (float4 t at 16t). A row past the unit
+  // reads the unit's last row instead: each row's scores, probabilities and
+  // output stay in that row's own lanes and such rows are never stored, so
+  // the loads need no branch, and the compiler waits for them only where the
+  // QK products use them.
+  auto piece_q = [&](const Unit& U, int32_t rows, int32_t prow, bool is16, int32_t* qi_out) -> const float* {
+    int32_t row = prow + (is16 ? (lane & 15) : lr);
     row = row < rows ? row : rows - 1;
     const int32_t qi = s_qid[row / qhead];
     *qi_out = qi;
-    return A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + row % qhead) * kD + half * 64;
+    return A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + row % qhead) * kD +
+           (is16 ? 4 * ((lane >> 4) & 3) : 64 * half);
   };
-  auto load_q8 = [&](const float* qp, int i0, float4 (&qr)[16]) __attribute__((always_inline)) {
+  auto load_q_first = [&](const float* qp, bool is16, float4 (&qr)[16]) __attribute__((always_inline)) {
+    if (is16) {
 #pragma unroll
-    for (int i = i0; i < i0 + 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+      for (int i = 0; i < 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 16 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+    }
   };
-
+  auto load_q_rest = [&](const float* qp, float4 (&qr)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 8; i < 16; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+  };
   for (int32_t u = blockIdx.x;;) {
     if (u >= num_units) break;
     const Unit U = P.units_mfma[u];
@@ -311,7 +486,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
     const int32_t n_e = U.e1 - U.e0;
     const int32_t rows = n_e * qhead;
     const int64_t row0 = (int64_t)U.e0 * qhead;
-    const int32_t ntiles = (rows + 31) / 32;
+    const SimdShare sh = wave_share(rows, wv);
 
     // ---- row offset of each key (-1: past the valid range or no page), the
     // validity bits, and the query id of each edge of the unit
@@ -330,15 +505,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
     for (int e = tid; e < n_e; e += kThreads) s_qid[e] = P.edges[2 * (int64_t)(U.e0 + e)];
     __syncthreads();
 
-    // ---- this wave's first tile: q requested now, so that it arrives while
+    // ---- this wave's first piece: q requested now, so that it arrives while
     // the block is gathered
-    int32_t tile = wv;
     float4 qr[16];
     int32_t qi = 0;
-    const float* qp = tile < ntiles ? q_row(U, rows, tile, &qi) : nullptr;
-    if (tile < ntiles) {
-      load_q8(qp, 0, qr);
-      load_q8(qp, 8, qr);
+    const float* qp = nullptr;
+    if (sh.npieces > 0) {
+      const bool is16 = sh.n32 == 0;
+      qp = piece_q(U, rows, sh.start, is16, &qi);
+      load_q_first(qp, is16, qr);
+      if (!is16) load_q_rest(qp, qr);
     }
 
     // ---- gather K and V of the block into LDS (zero rows past the valid range)
@@ -362,14 +538,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
     }
     __syncthreads();
 
-    // Keys held by this lane in the S^T accumulators: kb*32 + 8*(r/4) + 4*half + r%4.
-    // Bit r of vm[kb] says whether that key has a row.
-    uint32_t vm[NKB];
-    bool all_rows;
-    lane_key_bits<NKB>(s_valid, half, vm, all_rows);
+    // every key of the block has a row (uniform)
+    bool all_rows = true;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) all_rows = all_rows && s_valid[kb] == 0xffffffffu;
 
-    while (tile < ntiles) {
-      const int32_t row = tile * 32 + lr;
+    // this wave's 32-row tiles, then its 16-row tile
+    for (int32_t p = 0; p < sh.n32; ++p) {
+      const int32_t row = sh.start + 64 * p + lr;
       const bool row_ok = row < rows;
       // Key k is alive iff it has a row and (causal) block_start + k <= q + delta;
       // kmaxh folds the causal bound for this lane's keys (32-bit compares).
@@ -382,25 +558,40 @@ __global__ __launch_bounds__(WAVES * 64) void k_fwd_mfma(IndexPtrs P, FwdArgs A)
       floatx16 sacc[NKB];
       tile_scores<NKB>(s_k, qr, lr, half, sacc);
 
-      // ---- the first half of the next tile's q, into the registers the
-      // products above have read (the second half follows the PV products)
-      const int32_t next = tile + kWaves;
-      if (next < ntiles) {
-        qp = q_row(U, rows, next, &qi);
-        load_q8(qp, 0, qr);
+      // ---- the first q loads of the wave's next piece, into the registers
+      // the products above have read (the rest follow the PV products)
+      const bool nq = p + 1 < sh.npieces, nq16 = p + 1 == sh.n32;
+      if (nq) {
+        qp = piece_q(U, rows, sh.start + 64 * (p + 1), nq16, &qi);
+        load_q_first(qp, nq16, qr);
       }
 
       float mb2, sum;
-      tile_softmax<NKB>(sacc, full, vm, kmaxh, c2, mb2, sum);
+      tile_softmax<NKB, true>(sacc, full, s_valid, half, kmaxh, c2, mb2, sum);
       floatx16 oacc[kD / 32];
       tile_pv<NKB>(s_v, sacc, lr, half, oacc);
 
-      // ---- the second half of the next tile's q. Issued before this tile's
+      // ---- the rest of the next piece's q. Issued before this tile's
       // stores: a wait for a load also waits for every store issued before it
-      if (next < ntiles) load_q8(qp, 8, qr);
+      if (nq && !nq16) load_q_rest(qp, qr);
 
       if (row_ok) tile_store(A, row0, row, half, oacc, mb2, sum);
-      tile = next;
+    }
+    if (sh.n32 < sh.npieces) {
+      const int li = lane & 15, gq = lane >> 4;
+      const int32_t row = sh.start + 64 * sh.n32 + li;
+      const bool row_ok = row < rows;
+      int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
+      klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
+      const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
+      const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
+      float s16[2 * NKB][4];
+      tile16_scores<2 * NKB>(s_k, qr, li, gq, s16);
+      float mb2, sum;
+      tile16_softmax<2 * NKB>(s16, full, s_valid, gq, kmax, c2, mb2, sum);
+      floatx4 o16[8];
+      tile16_pv<2 * NKB>(s_v, s16, li, gq, o16);
+      if (row_ok) tile16_store(A, row0, row, gq, o16, mb2, sum);
     }
     __syncthreads();                       // LDS of this unit no longer read
     if (tid == 0) s_unit = (int)gridDim.x + (int)atomicAdd(&hdr->queue_mfma, 1u);
@@ -502,10 +693,9 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
   const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
   const float c2 = A.scale_log2;
   const int32_t* units = reinterpret_cast<const int32_t*>(P.units_sorted);   // largest first
-  // Per-lane constants (row lane lr, half of the lanes) are formed again from
+  // Per-lane constants (row lane, half of the lanes) are formed again from
   // an opaque lane index where they are used, instead of being kept live
   // across the unit loop: the tile code needs nearly every register.
-  int lr = lane & 31, half = lane >> 5;
 
   // a record from LDS, in scalar registers (the fields are uniform)
   auto unit_of = [&](int sl) {
@@ -589,18 +779,33 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       if (n < kVInstr) __builtin_amdgcn_global_load_lds((gvoid*)srcv[i], (lvoid*)(s_v + 256 * n), 16, 0, 0);
     }
   };
-  // q row of tile row `row` of the unit in slot sl (rows past the unit read
-  // its last row: they stay in their own lanes and are never stored)
-  auto q_row = [&](int sl, int32_t h, int32_t rows, int32_t tile, int32_t* qi_out) -> const float* {
-    int32_t row = tile * 32 + lr;
+  // q of the lane's row in the piece that starts at row prow of the unit in
+  // slot sl: a 32-row tile takes half of row prow + lane % 32 (float4 i at
+  // 4i), a 16-row tile row prow + lane % 16 at d = 16t + 4g (float4 t at
+  // 16t). Rows past the unit read its last row: they stay in their own lanes
+  // and are never stored.
+  auto piece_q = [&](int sl, int32_t h, int32_t rows, int32_t prow, bool is16, int32_t* qi_out) -> const float* {
+    const int ln = opaque_lane(lane);
+    int32_t row = prow + (is16 ? (ln & 15) : (ln & 31));
     row = row < rows ? row : rows - 1;
     const int32_t qi = s_qid[sl][row / qhead];
     *qi_out = qi;
-    return A.q + ((int64_t)qi * A.hq + (int64_t)h * qhead + row % qhead) * kD + half * 64;
+    return A.q + ((int64_t)qi * A.hq + (int64_t)h * qhead + row % qhead) * kD +
+           (is16 ? 4 * ((ln >> 4) & 3) : 64 * (ln >> 5));
   };
-  auto load_q8 = [&](const float* qp, int i0, float4 (&qr)[16]) __attribute__((always_inline)) {
+  // the first q loads of a piece (all of a 16-row tile's), then the rest of a 32-row tile's
+  auto load_q_first = [&](const float* qp, bool is16, float4 (&qr)[16]) __attribute__((always_inline)) {
+    if (is16) {
 #pragma unroll
-    for (int i = i0; i < i0 + 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+      for (int i = 0; i < 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 16 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
+    }
+  };
+  auto load_q_rest = [&](const float* qp, float4 (&qr)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 8; i < 16; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
   };
 
   // ---- prologue: records of units 0..2, lists of units 0 and 1, offsets of
@@ -619,13 +824,16 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
   float4 qr[16];
   int32_t qi = 0;
   const float* qp = nullptr;
+  const int simd = wv & 3, second = wv >> 2;   // wave wv runs on SIMD wv % 4 with wave wv ^ 4
   {
     const Unit U0 = unit_of(0);
     const int32_t rows0 = (U0.e1 - U0.e0) * qhead;
-    if (wv * 32 < rows0) {
-      qp = q_row(0, U0.h, rows0, wv, &qi);
-      load_q8(qp, 0, qr);
-      load_q8(qp, 8, qr);
+    const SimdShare sh = simd_share(rows0, simd);
+    if (second < sh.npieces) {
+      const bool is16 = second == sh.n32;
+      qp = piece_q(0, U0.h, rows0, sh.start + 32 * second, is16, &qi);
+      load_q_first(qp, is16, qr);
+      if (!is16) load_q_rest(qp, qr);
     }
   }
   gather_kv();
@@ -640,10 +848,11 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
     const int32_t nkeys = keys_of(U.blk, U.lk);
     const int32_t rows = (U.e1 - U.e0) * qhead;
     const int64_t row0 = (int64_t)U.e0 * qhead;
-    const int32_t ntiles = (rows + 31) / 32;
-    uint32_t vm[NKB];
-    bool all_rows;
-    lane_key_bits<NKB>(s_valid[j & 1], opaque_lane(lane) >> 5, vm, all_rows);
+    const SimdShare sh = simd_share(rows, simd);
+    // every key of the block has a row (uniform)
+    bool all_rows = true;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) all_rows = all_rows && s_valid[j & 1][kb] == 0xffffffffu;
 
     // ---- this unit's K and V rows (and this wave's first q rows, the lists
     // of unit j + 1 and the record of unit j + 2): this wave's, then every
@@ -655,13 +864,29 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
     if (has1) form_offsets(ms1, (j + 1) & 1);
 
     bool q_next = false;   // this wave has requested its first q rows of unit j + 1
-    for (int32_t tile = wv; tile < ntiles; tile += kWaves) {
-      {
-        const int ln = opaque_lane(lane);
-        lr = ln & 31;
-        half = ln >> 5;
+    // The q rows of this wave's next piece: its next one in this unit, or
+    // its first one in unit j + 1. Returns whether there is one; its kind in nq16.
+    auto next_q = [&](int32_t p, bool& nq16) -> bool {
+      if (p + 2 < sh.npieces) {
+        nq16 = p + 2 == sh.n32;
+        qp = piece_q(ms, U.h, rows, sh.start + 32 * (p + 2), nq16, &qi);
+        return true;
       }
-      const int32_t row = tile * 32 + lr;
+      if (!has1) return false;
+      const Unit U1 = unit_of(ms1);
+      const int32_t rows1 = (U1.e1 - U1.e0) * qhead;
+      const SimdShare sh1 = simd_share(rows1, simd);
+      q_next = true;
+      if (second >= sh1.npieces) return false;
+      nq16 = second == sh1.n32;
+      qp = piece_q(ms1, U1.h, rows1, sh1.start + 32 * second, nq16, &qi);
+      return true;
+    };
+    // this wave's 32-row tiles (every other one of the share), then the
+    // share's 16-row tile if it is this wave's turn
+    for (int32_t p = second; p < sh.n32; p += 2) {
+      const int ln = opaque_lane(lane), lr = ln & 31, half = ln >> 5;
+      const int32_t row = sh.start + 32 * p + lr;
       const bool row_ok = row < rows;
       // key k is alive iff it has a row and (causal) block_start + k <= q + delta
       int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
@@ -670,28 +895,38 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
       floatx16 sacc[NKB];
       tile_scores<NKB>(s_k, qr, lr, half, sacc);
-      // ---- the first half of the next q rows: this unit's next tile, or
-      // the next unit's first one
-      bool nq = false;
-      if (tile + kWaves < ntiles) {
-        nq = true;
-        qp = q_row(ms, U.h, rows, tile + kWaves, &qi);
-      } else if (has1) {
-        const Unit U1 = unit_of(ms1);
-        const int32_t rows1 = (U1.e1 - U1.e0) * qhead;
-        q_next = true;
-        nq = wv * 32 < rows1;
-        if (nq) qp = q_row(ms1, U1.h, rows1, wv, &qi);
-      }
-      if (nq) load_q8(qp, 0, qr);
+      // ---- the first half of the next q rows (all of them for a 16-row tile)
+      bool nq16 = false;
+      const bool nq = next_q(p, nq16);
+      if (nq) load_q_first(qp, nq16, qr);
       float mb2, sum;
-      tile_softmax<NKB>(sacc, full, vm, kmaxh, c2, mb2, sum);
+      tile_softmax<NKB, true>(sacc, full, s_valid[j & 1], half, kmaxh, c2, mb2, sum);
       floatx16 oacc[kD / 32];
       tile_pv<NKB>(s_v, sacc, lr, half, oacc);
       // the second half, before the stores (a wait for a load also waits
       // for every store issued before it)
-      if (nq) load_q8(qp, 8, qr);
+      if (nq && !nq16) load_q_rest(qp, qr);
       if (row_ok) tile_store(A, row0, row, half, oacc, mb2, sum);
+    }
+    if (sh.n32 < sh.npieces && sh.n32 >= second && ((sh.n32 - second) & 1) == 0) {
+      const int ln = opaque_lane(lane), li = ln & 15, gq = ln >> 4;
+      const int32_t row = sh.start + 32 * sh.n32 + li;
+      const bool row_ok = row < rows;
+      int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
+      klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
+      const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
+      const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
+      float s16[2 * NKB][4];
+      tile16_scores<2 * NKB>(s_k, qr, li, gq, s16);
+      bool nq16 = false;
+      const bool nq = next_q(sh.n32, nq16);
+      if (nq) load_q_first(qp, nq16, qr);
+      float mb2, sum;
+      tile16_softmax<2 * NKB>(s16, full, s_valid[j & 1], gq, kmax, c2, mb2, sum);
+      floatx4 o16[8];
+      tile16_pv<2 * NKB>(s_v, s16, li, gq, o16);
+      if (nq && !nq16) load_q_rest(qp, qr);
+      if (row_ok) tile16_store(A, row0, row, gq, o16, mb2, sum);
     }
     // ---- every wave has left this unit's tiles: the next unit's K and V
     // rows, the first q rows of waves that had no tile here, the lists of
@@ -701,15 +936,17 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
     if (has1) {
       const Unit U1 = unit_of(ms1);
       const int32_t rows1 = (U1.e1 - U1.e0) * qhead;
-      const bool load_first_q = !q_next && wv * 32 < rows1;
-      if (load_first_q) qp = q_row(ms1, U1.h, rows1, wv, &qi);
+      const SimdShare sh1 = simd_share(rows1, simd);
+      const bool load_first_q = !q_next && second < sh1.npieces;
+      const bool first16 = second == sh1.n32;
+      if (load_first_q) qp = piece_q(ms1, U1.h, rows1, sh1.start + 32 * second, first16, &qi);
       Unit U2{};
       if (has2) U2 = unit_of(ms2);
       gather_kv();
       if (has2) fetch_lists(ms2, U2);
       if (load_first_q) {
-        load_q8(qp, 0, qr);
-        load_q8(qp, 8, qr);
+        load_q_first(qp, first16, qr);
+        if (!first16) load_q_rest(qp, qr);
       }
     }
     if (has3) fetch_record(ms, unit_at(j + 3));
@@ -920,14 +1157,6 @@ void k_fwd_mfma_gen(IndexPtrs P, FwdArgs A) {
 //   S^T[key, row]: MFMA t, component c, lane group g takes d = 16t + 4g + c
 //   O^T[d, row]:   output row i of MFMA block db stands for d = 4i + (db & 3) + 64 (db >> 2)
 // and an exact softmax over the block from register-resident scores.
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ inline floatx4 zero4v() {
-  floatx4 z;
-  z[0] = z[1] = z[2] = z[3] = 0.f;
-  return z;
-}
-
 template <int NKB, int KVF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_mfma16(IndexPtrs P, FwdArgs A) {
   constexpr int kWaves = 4;
@@ -1170,27 +1399,24 @@ hipError_t launch_mfma16_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, 
   }
 }
 
-template <int NKB, int WAVES, int KVF>
+template <int NKB, int KVF>
 hipError_t launch_mfma_kv(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
   static thread_local int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma<NKB, WAVES, KVF>, WAVES * 64, 0) !=
-            hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma<NKB, KVF>, 512, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
-  hipLaunchKernelGGL((k_fwd_mfma<NKB, WAVES, KVF>), dim3((unsigned)per_cu * cus), dim3(WAVES * 64), 0, s, P, a);
+  hipLaunchKernelGGL((k_fwd_mfma<NKB, KVF>), dim3((unsigned)per_cu * cus), dim3(512), 0, s, P, a);
   return hipGetLastError();
 }
 
-template <int NKB, int WAVES>
+// 16-bit pages (fp32 pages take the direct-to-LDS kernel)
+template <int NKB>
 hipError_t launch_mfma_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
-  switch (a.kv_format) {
-    case SA_KV_BF16: return launch_mfma_kv<NKB, WAVES, SA_KV_BF16>(P, a, s, cus);
-    case SA_KV_F16: return launch_mfma_kv<NKB, WAVES, SA_KV_F16>(P, a, s, cus);
-    default: return launch_mfma_kv<NKB, WAVES, SA_KV_F32>(P, a, s, cus);
-  }
+  return a.kv_format == SA_KV_BF16 ? launch_mfma_kv<NKB, SA_KV_BF16>(P, a, s, cus)
+                                   : launch_mfma_kv<NKB, SA_KV_F16>(P, a, s, cus);
 }
 
 template <int NKB>
@@ -1260,8 +1486,8 @@ hipError_t launch_forward_mfma(const sa_index* idx, const FwdArgs& a, hipStream_
     if (nkb <= 3) return launch_mfma_dma<3>(P, a, s, grid);
     return launch_mfma_dma<4>(P, a, s, grid);
   }
-  if (nkb <= 3) return launch_mfma_t<3, 8>(P, a, s, grid);
-  return launch_mfma_t<4, 8>(P, a, s, grid);
+  if (nkb <= 3) return launch_mfma_t<3>(P, a, s, grid);
+  return launch_mfma_t<4>(P, a, s, grid);
 }
 
 }  // namespace sa
