@@ -755,12 +755,15 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
     constexpr int kPerWave = (kVInstr + kWaves - 1) / kWaves;
     const float* srck[kPerWave];
     const float* srcv[kPerWave];
+    // Branch-free: a key without a row reads the zero line (its probability
+    // is 0, and its V row must be finite); a padding chunk, never read, and
+    // the tail past the last key take any chunk of a row in the block.
     auto src_of = [&](const float* base, int pitch4, int n) -> const float* {
       const int c = 64 * n + opaque_lane(lane);
       const int row = c / pitch4, col = c - row * pitch4;
       const int64_t off = s_off[row < kKeys ? row : 0];
-      return (row < kKeys && col < kD / 4 && off >= 0) ? base + off + 4 * col
-                                                     : g_zero_row + 4 * (col & (kD / 4 - 1));
+      const float* rowp = off >= 0 ? base + off : g_zero_row;
+      return rowp + 4 * (col < kD / 4 ? col : kD / 4 - 1);
     };
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
@@ -768,15 +771,18 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       srck[i] = src_of(A.k, kKPitch / 4, n < kKInstr ? n : 0);
       srcv[i] = src_of(A.v, kVPitch / 4, n < kVInstr ? n : 0);
     }
+    // the rounds in which every wave has an instruction need no test
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int n = i * kWaves + wv;
-      if (n < kKInstr) __builtin_amdgcn_global_load_lds((gvoid*)srck[i], (lvoid*)(s_k + 256 * n), 16, 0, 0);
+      if (i < kKInstr / kWaves || n < kKInstr)
+        __builtin_amdgcn_global_load_lds((gvoid*)srck[i], (lvoid*)(s_k + 256 * n), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int n = i * kWaves + wv;
-      if (n < kVInstr) __builtin_amdgcn_global_load_lds((gvoid*)srcv[i], (lvoid*)(s_v + 256 * n), 16, 0, 0);
+      if (i < kVInstr / kWaves || n < kVInstr)
+        __builtin_amdgcn_global_load_lds((gvoid*)srcv[i], (lvoid*)(s_v + 256 * n), 16, 0, 0);
     }
   };
   // q of the lane's row in the piece that starts at row prow of the unit in
