@@ -422,7 +422,7 @@ def forward_kernels(w, fused=False, kv_dtype="f32"):
     if w.head_dim == 128 and w.block_size <= 64:
         return "k_fwd_wave", "k_fwd_mfma16"
     if w.head_dim == 128 and w.block_size <= 128:
-        return "k_fwd_wave", "k_fwd_mfma_dma" if kv_dtype == "f32" else "k_fwd_mfma"
+        return "k_fwd_wave", "k_fwd_mfma_dma"
     if w.head_dim in (64, 128, 256):
         return "k_fwd_wave", "k_fwd_mfma_gen"
     return "k_fwd_wave", None

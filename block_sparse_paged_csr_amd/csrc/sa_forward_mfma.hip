@@ -4,14 +4,14 @@
 // GQA lane qh, (o, m, l) of alice-llm 2.0.0 forward.rs process_work_unit over
 // the block's valid, causally alive positions.
 //
-// Persistent workgroups take units from a device queue: 8 waves, one per CU,
-// for blocks of up to 128 keys; 4 waves and two per CU for blocks of up to 64
-// keys (LDS sized to the block), so one workgroup gathers while the other
-// computes. For each unit the workgroup first resolves each key's K/V row
-// offset through the block table, then gathers the block's K and V rows once
-// into LDS with all loads in flight (row pitch padded so the MFMA operand
-// reads do not conflict). Each wave then takes 32-row tiles of the unit and
-// computes them on fp32 matrix cores (v_mfma_f32_32x32x2f32):
+// Persistent workgroups, one per CU for blocks of up to 128 keys (the
+// direct-to-LDS kernel, units dealt statically in size order; the chunked
+// kernel for other geometries), two per CU for blocks of up to 64 keys (the
+// 16-row kernel). For each unit the workgroup resolves each key's K/V row
+// offset through the block table and brings the block's K and V rows into
+// LDS once, all loads in flight (rows padded or swizzled so that the MFMA
+// operand reads do not conflict). The waves then compute the unit's 32-row
+// tiles on fp32 matrix cores (v_mfma_f32_32x32x2f32):
 //
 //   S^T[key, row] = K[key, :] . Q[row, :]       A = K from LDS, B = Q^T in registers
 //   O^T[d, row]  += V[key, d] * P[row, key]      A = V^T from LDS, B = P^T in registers
@@ -46,7 +46,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // Most edges in one MFMA unit (cap_edges <= kMaxUnitEdges, see the plan).
 constexpr int kMaxUnitEdges = kCapUnitEdges;
 
-// ---- pieces of one 32-row tile, shared by the two 32-row kernels below
+// ---- pieces of one 32-row tile (fp32 rows in LDS), shared by the direct-to-LDS
+// and chunked kernels below
 // (K and V rows in LDS with pitches kKPitch and kVPitch floats).
 
 // Bit r of the result for 32-key block kb: key kb*32 + 8*(r/4) + 4*half + r%4
@@ -382,6 +383,187 @@ __device__ __forceinline__ void tile16_store(const FwdArgs& A, int64_t row0, int
   }
 }
 
+// ---- the same tiles from 16-bit pages. The block's K and V rows stay raw
+// 16-bit words in LDS, 16 chunks of 8 words a row with no padding. In K,
+// chunk c of row r sits at chunk c ^ (r & 15) of the row, which spreads the
+// 32 rows of one operand read over all the banks; V is stored as is (an
+// operand read of the 32-row tiles covers one whole row, and its addresses
+// then fold into immediate offsets; the 16-row tiles' reads of rows four
+// apart meet in the same banks, a 2-way conflict, which measured cheaper
+// than forming swizzled V addresses). Each word becomes its exact fp32 value
+// as it enters the matrix cores, in the order the fp32 tiles use, so both
+// formats give the same bits on the same values.
+__device__ __forceinline__ int swz16(int row, int chunk) { return row * 128 + ((chunk ^ (row & 15)) << 3); }
+
+template <int KVF>
+__device__ __forceinline__ float4 cvt4(uint32_t lo, uint32_t hi) {
+  return make_float4(kv16_to_f32<KVF>(lo & 0xffffu), kv16_to_f32<KVF>(lo >> 16), kv16_to_f32<KVF>(hi & 0xffffu),
+                     kv16_to_f32<KVF>(hi >> 16));
+}
+
+// tile_scores: chunk half*8 + p of the lane's key row holds d = half*64 + 8p .. +7,
+// the operands of steps 2p and 2p + 1.
+template <int NKB, int KVF>
+__device__ __forceinline__ void tile_scores16(const uint16_t* sk, const float4 (&qr)[16], int lr, int half,
+                                              floatx16 (&sacc)[NKB]) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
+  uint4 kc[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) kc[kb] = *reinterpret_cast<const uint4*>(&sk[swz16(kb * 32 + lr, half * 8)]);
+  __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    uint4 kn[NKB];
+    if (p < 7) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        kn[kb] = *reinterpret_cast<const uint4*>(&sk[swz16(kb * 32 + lr, half * 8 + p + 1)]);
+    }
+    // the step's operands converted first, then its products (each
+    // accumulator takes them in the fp32 tiles' order)
+    float4 klo[NKB], khi[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      klo[kb] = cvt4<KVF>(kc[kb].x, kc[kb].y);
+      khi[kb] = cvt4<KVF>(kc[kb].z, kc[kb].w);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x0002, 8 * NKB, 0);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const float4 q = qr[2 * p + sub];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float4 k = sub == 0 ? klo[kb] : khi[kb];
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.x, q.x, sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.y, q.y, sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.z, q.z, sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.w, q.w, sacc[kb], 0, 0, 0);
+      }
+    }
+    if (p < 7) __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 8 * NKB, 0);
+    if (p < 7) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
+    }
+  }
+}
+
+// tile_pv: lane lr reads words 4 phi(lr) .. + 3 of a key row, with
+// phi(8g + 4h + c) = 8g + 2c + h (g, c < 4, h < 2), so output row m of MFMA
+// block db stands for d = 4 phi(m) + db: the rows that lanes lr and lr + 32
+// hold side by side are adjacent d, and each store of tile_store16 writes 32
+// contiguous bytes of a row, as the fp32 tiles' stores do.
+__device__ __forceinline__ int pv16_word(int lr) { return 4 * (8 * (lr >> 3) + 2 * (lr & 3) + ((lr >> 2) & 1)); }
+template <int NKB, int KVF>
+__device__ __forceinline__ void tile_pv16(const uint16_t* sv, const floatx16 (&sacc)[NKB], int lr, int half,
+                                          floatx16 (&oacc)[4]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = zero16();
+  uint2 vc[2];
+  auto read_v = [&](int r0, uint2 (&dst)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = r0 + j, kb = r / 16, rr = r % 16;
+      const int key = kb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4);
+      dst[j] = *reinterpret_cast<const uint2*>(&sv[key * 128 + pv16_word(lr)]);
+    }
+  };
+  read_v(0, vc);
+  __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+#pragma unroll
+  for (int r0 = 0; r0 < 16 * NKB; r0 += 2) {
+    uint2 vn[2];
+    if (r0 + 2 < 16 * NKB) read_v(r0 + 2, vn);
+    const float4 v0 = cvt4<KVF>(vc[0].x, vc[0].y), v1 = cvt4<KVF>(vc[1].x, vc[1].y);
+    __builtin_amdgcn_sched_group_barrier(0x0002, 8, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float4 v = j == 0 ? v0 : v1;
+      const float p = sacc[(r0 + j) / 16][(r0 + j) % 16];
+      oacc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.x, p, oacc[0], 0, 0, 0);
+      oacc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.y, p, oacc[1], 0, 0, 0);
+      oacc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.z, p, oacc[2], 0, 0, 0);
+      oacc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.w, p, oacc[3], 0, 0, 0);
+    }
+    if (r0 + 2 < 16 * NKB) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 8, 0);
+    if (r0 + 2 < 16 * NKB) {
+      vc[0] = vn[0];
+      vc[1] = vn[1];
+    }
+  }
+}
+
+// Accumulator i = 4g + c of block db holds d = 4 phi(8g + 4half + c) + db =
+// 32g + 8c + 4half + db of row `row`.
+__device__ __forceinline__ void tile_store16(const FwdArgs& A, int64_t row0, int32_t row, int half,
+                                             const floatx16 (&oacc)[4], float mb2, float sum) {
+  float* op = A.o + (row0 + row) * kD + 4 * half;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<float4*>(op + 32 * g + 8 * c) =
+          make_float4(oacc[0][4 * g + c], oacc[1][4 * g + c], oacc[2][4 * g + c], oacc[3][4 * g + c]);
+  if (half == 0) {
+    A.m[row0 + row] = mb2 * kLn2;
+    A.l[row0 + row] = sum;
+  }
+}
+
+// 16-row tiles: K words d = 16t + 4g .. +3 and V words 4li .. 4li + 3 (and + 64)
+// of their key rows, the fp32 tiles' operands.
+template <int NCH, int KVF>
+__device__ __forceinline__ void tile16_scores16(const uint16_t* sk, const float4 (&qr)[16], int li, int g,
+                                                float (&s)[NCH][4]) {
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    floatx4 sa0 = zero4v(), sa1 = zero4v();
+    const int row = 16 * ch + li;
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+      const uint2 wa = *reinterpret_cast<const uint2*>(&sk[swz16(row, 2 * t + (g >> 1)) + 4 * (g & 1)]);
+      const uint2 wb = *reinterpret_cast<const uint2*>(&sk[swz16(row, 2 * (t + 1) + (g >> 1)) + 4 * (g & 1)]);
+      const float4 ka = cvt4<KVF>(wa.x, wa.y), kb = cvt4<KVF>(wb.x, wb.y);
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[t].x, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.x, qr[t + 1].x, sa1, 0, 0, 0);
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[t].y, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.y, qr[t + 1].y, sa1, 0, 0, 0);
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[t].z, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.z, qr[t + 1].z, sa1, 0, 0, 0);
+      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[t].w, sa0, 0, 0, 0);
+      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.w, qr[t + 1].w, sa1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // bound how far LDS reads run ahead
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[ch][r] = sa0[r] + sa1[r];
+  }
+}
+
+template <int NCH, int KVF>
+__device__ __forceinline__ void tile16_pv16(const uint16_t* sv, const float (&s)[NCH][4], int li, int g,
+                                            floatx4 (&oacc)[8]) {
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * ch + 4 * g + r;
+      const uint2 w0 = *reinterpret_cast<const uint2*>(&sv[row * 128 + 4 * li]);
+      const uint2 w1 = *reinterpret_cast<const uint2*>(&sv[row * 128 + 64 + 4 * li]);
+      const float4 a = cvt4<KVF>(w0.x, w0.y), b = cvt4<KVF>(w1.x, w1.y);
+      const float v0[4] = {a.x, a.y, a.z, a.w}, v1[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const floatx4 acc = (ch == 0 && r == 0) ? zero4v() : oacc[db];
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(db < 4 ? v0[db & 3] : v1[db & 3], s[ch][r], acc, 0, 0, 0);
+      }
+      if (r & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // A unit's rows in 16-row quanta, dealt to the four SIMDs of the workgroup in
 // near-equal contiguous shares (the unit ends when its largest share does).
 // A share of q quanta is q / 2 32-row tiles and, for odd q, one 16-row tile
@@ -398,220 +580,10 @@ __device__ __forceinline__ SimdShare simd_share(int32_t rows, int simd) {
   const int32_t q = base + (simd < extra ? 1 : 0);
   return SimdShare{16 * (simd * base + (simd < extra ? simd : extra)), (q >> 1) + (q & 1), q >> 1};
 }
-// The same deal seen from wave wv: its tile k starts 64k rows after its first
-// (same meaning of the fields, for the wave's own tiles).
-__device__ __forceinline__ SimdShare wave_share(int32_t rows, int wv) {
-  const SimdShare sh = simd_share(rows, wv & 3);
-  const int second = wv >> 2;
-  const int32_t n32 = sh.n32 > second ? (sh.n32 - second + 1) >> 1 : 0;
-  const bool with16 = sh.npieces > sh.n32 && sh.n32 >= second && ((sh.n32 - second) & 1) == 0;
-  return SimdShare{sh.start + 32 * second, n32 + (with16 ? 1 : 0), n32};
-}
 
-// NKB: 32-key blocks per KV block (block_size <= 32 * NKB); 16-bit pages (KVF).
-//
-// Each wave runs its tiles as a software pipeline so that the matrix pipe is
-// not left waiting on memory: the unit's query ids sit in LDS, and the next
-// tile's q rows are fetched right after the current tile's QK products have
-// read theirs, so their round trip overlaps the softmax and the PV products.
-// The LDS operands of each group of matrix instructions are read one group
-// ahead. A unit's rows are dealt to the waves as in the direct-to-LDS kernel
-// below (wave_share), so both compute every row with the same tile shape.
-template <int NKB, int KVF>
-__global__ __launch_bounds__(512) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
-  constexpr int kWaves = 8;
-  constexpr int kThreads = kWaves * 64;
-  constexpr int kKeys = NKB * 32;
-  constexpr int kIters = kKeys * (kD / 4) / kThreads;   // gather float4 per thread (K and V each)
-  static_assert(kKeys * (kD / 4) % kThreads == 0, "gather tiling");
-  static_assert(kThreads % (kD / 4) == 0, "a thread gathers one column of its keys");
-  __shared__ __align__(16) float s_k[kKeys * kKPitch];
-  __shared__ __align__(16) float s_v[kKeys * kVPitch];
-  __shared__ int64_t s_off[kKeys];
-  __shared__ int32_t s_qid[kMaxUnitEdges];
-  __shared__ uint32_t s_valid[NKB];       // bit k of word kb: key kb*32 + k has a row
-  __shared__ int s_unit;
-
-  DevHeader* hdr = P.hdr;
-  if (hdr->status != SA_OK) return;
-  const int32_t num_units = hdr->num_units_mfma;
-  // Workgroup g starts on unit g, then pulls units gridDim.x, gridDim.x+1, ...
-  // from the queue. Workgroups without a first unit leave at once, so an
-  // empty list costs no atomics.
-  if ((int32_t)blockIdx.x >= num_units) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int lr = lane & 31, half = lane >> 5;
-  const int32_t qhead = A.qhead;
-  const int64_t page_stride = (int64_t)A.hkv * A.page_size * kD;
-  const float c2 = A.scale_log2;
-
-  // q of the lane's row in the piece that starts at row prow: a 32-row tile
-  // takes half of row prow + lane % 32 (float4 i at 4i), a 16-row tile row
-  // prow + lane % 16 at d = 16t + 4g (float4 t at 16t). A row past the unit
-  // reads the unit's last row instead: each row's scores, probabilities and
-  // output stay in that row's own lanes and such rows are never stored, so
-  // the loads need no branch, and the compiler waits for them only where the
-  // QK products use them.
-  auto piece_q = [&](const Unit& U, int32_t rows, int32_t prow, bool is16, int32_t* qi_out) -> const float* {
-    int32_t row = prow + (is16 ? (lane & 15) : lr);
-    row = row < rows ? row : rows - 1;
-    const int32_t qi = s_qid[row / qhead];
-    *qi_out = qi;
-    return A.q + ((int64_t)qi * A.hq + (int64_t)U.h * qhead + row % qhead) * kD +
-           (is16 ? 4 * ((lane >> 4) & 3) : 64 * half);
-  };
-  auto load_q_first = [&](const float* qp, bool is16, float4 (&qr)[16]) __attribute__((always_inline)) {
-    if (is16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 16 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
-    }
-  };
-  auto load_q_rest = [&](const float* qp, float4 (&qr)[16]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 8; i < 16; ++i) qr[i] = *reinterpret_cast<const float4*>(qp + 4 * i);
-  };
-  for (int32_t u = blockIdx.x;;) {
-    if (u >= num_units) break;
-    const Unit U = P.units_mfma[u];
-    const int64_t lk = U.lk;
-    const int64_t block_start = (int64_t)U.blk * A.block_size;
-    int64_t block_end = block_start + A.block_size;
-    block_end = block_end < lk ? block_end : lk;
-    const int32_t nkeys = block_end > block_start ? (int32_t)(block_end - block_start) : 0;
-    const int64_t bt_row = (int64_t)U.b * A.max_pages + (int64_t)U.blk * A.ppb;
-    const int64_t head_off = (int64_t)U.h * A.page_size * kD;
-    const int32_t n_e = U.e1 - U.e0;
-    const int32_t rows = n_e * qhead;
-    const int64_t row0 = (int64_t)U.e0 * qhead;
-    const SimdShare sh = wave_share(rows, wv);
-
-    // ---- row offset of each key (-1: past the valid range or no page), the
-    // validity bits, and the query id of each edge of the unit
-    for (int key = tid; key < kKeys; key += kThreads) {
-      int64_t off = -1;
-      if (key < nkeys) {
-        const int32_t pgl = (int32_t)div_magic((uint32_t)key, A.ps_magic);
-        const int32_t page = A.block_tables[bt_row + pgl];
-        if (page >= 0 && page < A.num_pages)
-          off = (int64_t)page * page_stride + head_off + (int64_t)(key - pgl * A.page_size) * kD;
-      }
-      s_off[key] = off;
-      const uint64_t bits = __ballot(off >= 0);
-      if ((lane & 31) == 0) s_valid[key >> 5] = (uint32_t)(bits >> (lane & 32));
-    }
-    for (int e = tid; e < n_e; e += kThreads) s_qid[e] = P.edges[2 * (int64_t)(U.e0 + e)];
-    __syncthreads();
-
-    // ---- this wave's first piece: q requested now, so that it arrives while
-    // the block is gathered
-    float4 qr[16];
-    int32_t qi = 0;
-    const float* qp = nullptr;
-    if (sh.npieces > 0) {
-      const bool is16 = sh.n32 == 0;
-      qp = piece_q(U, rows, sh.start, is16, &qi);
-      load_q_first(qp, is16, qr);
-      if (!is16) load_q_rest(qp, qr);
-    }
-
-    // ---- gather K and V of the block into LDS (zero rows past the valid range)
-    {
-      const int c4 = tid % (kD / 4);
-      int64_t offs[kIters];
-#pragma unroll
-      for (int i = 0; i < kIters; ++i) offs[i] = s_off[(tid + i * kThreads) / (kD / 4)];
-      float4 kv[kIters], vv[kIters];
-#pragma unroll
-      for (int i = 0; i < kIters; ++i) {
-        kv[i] = offs[i] >= 0 ? load_kv4<KVF>(A.k, offs[i] + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        vv[i] = offs[i] >= 0 ? load_kv4<KVF>(A.v, offs[i] + c4 * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < kIters; ++i) {
-        const int key = (tid + i * kThreads) / (kD / 4);
-        *reinterpret_cast<float4*>(&s_k[key * kKPitch + c4 * 4]) = kv[i];
-        *reinterpret_cast<float4*>(&s_v[key * kVPitch + c4 * 4]) = vv[i];
-      }
-    }
-    __syncthreads();
-
-    // every key of the block has a row (uniform)
-    bool all_rows = true;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) all_rows = all_rows && s_valid[kb] == 0xffffffffu;
-
-    // this wave's 32-row tiles, then its 16-row tile
-    for (int32_t p = 0; p < sh.n32; ++p) {
-      const int32_t row = sh.start + 64 * p + lr;
-      const bool row_ok = row < rows;
-      // Key k is alive iff it has a row and (causal) block_start + k <= q + delta;
-      // kmaxh folds the causal bound for this lane's keys (32-bit compares).
-      int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
-      klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
-      const int32_t kmaxh = (int32_t)(klim < -1 ? -1 : klim) - 4 * half;
-      // every key of the tile alive for every row: the masks can be skipped
-      const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
-
-      floatx16 sacc[NKB];
-      tile_scores<NKB>(s_k, qr, lr, half, sacc);
-
-      // ---- the first q loads of the wave's next piece, into the registers
-      // the products above have read (the rest follow the PV products)
-      const bool nq = p + 1 < sh.npieces, nq16 = p + 1 == sh.n32;
-      if (nq) {
-        qp = piece_q(U, rows, sh.start + 64 * (p + 1), nq16, &qi);
-        load_q_first(qp, nq16, qr);
-      }
-
-      float mb2, sum;
-      tile_softmax<NKB, true>(sacc, full, s_valid, half, kmaxh, c2, mb2, sum);
-      floatx16 oacc[kD / 32];
-      tile_pv<NKB>(s_v, sacc, lr, half, oacc);
-
-      // ---- the rest of the next piece's q. Issued before this tile's
-      // stores: a wait for a load also waits for every store issued before it
-      if (nq && !nq16) load_q_rest(qp, qr);
-
-      if (row_ok) tile_store(A, row0, row, half, oacc, mb2, sum);
-    }
-    if (sh.n32 < sh.npieces) {
-      const int li = lane & 15, gq = lane >> 4;
-      const int32_t row = sh.start + 64 * sh.n32 + li;
-      const bool row_ok = row < rows;
-      int64_t klim = A.causal ? (int64_t)qi + U.delta - block_start : (int64_t)nkeys - 1;
-      klim = klim < (int64_t)nkeys - 1 ? klim : (int64_t)nkeys - 1;
-      const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
-      const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
-      float s16[2 * NKB][4];
-      tile16_scores<2 * NKB>(s_k, qr, li, gq, s16);
-      float mb2, sum;
-      tile16_softmax<2 * NKB>(s16, full, s_valid, gq, kmax, c2, mb2, sum);
-      floatx4 o16[8];
-      tile16_pv<2 * NKB>(s_v, s16, li, gq, o16);
-      if (row_ok) tile16_store(A, row0, row, gq, o16, mb2, sum);
-    }
-    __syncthreads();                       // LDS of this unit no longer read
-    if (tid == 0) s_unit = (int)gridDim.x + (int)atomicAdd(&hdr->queue_mfma, 1u);
-    __syncthreads();
-    u = s_unit;
-  }
-  // The last participating workgroup out resets the queue for the next launch.
-  if (tid == 0) {
-    __threadfence();
-    const unsigned active = num_units < (int32_t)gridDim.x ? (unsigned)num_units : gridDim.x;
-    const unsigned done = atomicAdd(&hdr->done_mfma, 1u);
-    if (done == active - 1) {
-      atomicExch(&hdr->queue_mfma, 0u);
-      atomicExch(&hdr->done_mfma, 0u);
-    }
-  }
-}
-
-// fp32 pages, blocks of 65..128 keys: the same tiles, with everything a unit
-// reads from memory besides q brought into LDS by direct-to-LDS loads
+// Blocks of 65..128 keys, fp32 or 16-bit pages (KVF; 16-bit words stay raw in
+// LDS, see tile_scores16): the same tiles, with everything a unit reads from
+// memory besides q brought into LDS by direct-to-LDS loads
 // (global_load_lds: each lane moves 4 or 16 bytes from its own global address
 // into LDS; no registers hold the data):
 //   - the block-table entries and query ids of the unit two ahead go out
@@ -619,7 +591,8 @@ __global__ __launch_bounds__(512) void k_fwd_mfma(IndexPtrs P, FwdArgs A) {
 //     offsets of the next unit are formed from them when a unit starts;
 //   - the next unit's K and V rows go out as soon as every wave has left
 //     this unit's tiles, all in flight at once (about 17 wave instructions
-//     of 1 KB), and one wait and one barrier publish them;
+//     of 1 KB each for fp32 pages, 8 for 16-bit ones), and one wait and one
+//     barrier publish them;
 //   - each wave's first q rows of the next unit load after its last QK
 //     products of this unit.
 // Within a unit the waves run their tiles without further barriers, so the
@@ -663,14 +636,16 @@ __device__ __forceinline__ int opaque_lane(int lane) {
   return lane;
 }
 
-template <int NKB>
+template <int NKB, int KVF>
 __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
   constexpr int kWaves = 8;
   constexpr int kThreads = kWaves * 64;
   constexpr int kKeys = NKB * 32;
-  constexpr int kKInstr = (kKeys * (kKPitch / 4) + 63) / 64;   // wave instructions filling the K region
-  constexpr int kVInstr = (kKeys * (kVPitch / 4) + 63) / 64;
-  constexpr int kVMin = kVInstr / kWaves;                     // V instructions of every wave, at least
+  constexpr bool kF32 = KVF == SA_KV_F32;
+  // wave instructions (64 chunks of 16 bytes) filling the K and V regions:
+  // padded fp32 rows, or unpadded rows of 16-bit words
+  constexpr int kKInstr = kF32 ? (kKeys * (kKPitch / 4) + 63) / 64 : kKeys / 4;
+  constexpr int kVInstr = kF32 ? (kKeys * (kVPitch / 4) + 63) / 64 : kKeys / 4;
   static_assert(kKeys <= kThreads && kMaxUnitEdges <= kThreads, "one key and one edge per thread");
   static_assert(kMaxUnitEdges % 64 == 0, "query ids move in whole waves");
   __shared__ __align__(16) float s_k[kKInstr * 256];
@@ -758,18 +733,29 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
     // Branch-free: a key without a row reads the zero line (its probability
     // is 0, and its V row must be finite); a padding chunk, never read, and
     // the tail past the last key take any chunk of a row in the block.
-    auto src_of = [&](const float* base, int pitch4, int n) -> const float* {
+    // (pitch4: float4 chunks a padded fp32 row; swizzled: the 16-bit K layout)
+    auto src_of = [&](const float* base, int pitch4, int n, bool swizzled) -> const float* {
       const int c = 64 * n + opaque_lane(lane);
-      const int row = c / pitch4, col = c - row * pitch4;
-      const int64_t off = s_off[row < kKeys ? row : 0];
-      const float* rowp = off >= 0 ? base + off : g_zero_row;
-      return rowp + 4 * (col < kD / 4 ? col : kD / 4 - 1);
+      if constexpr (kF32) {
+        const int row = c / pitch4, col = c - row * pitch4;
+        const int64_t off = s_off[row < kKeys ? row : 0];
+        const float* rowp = off >= 0 ? base + off : g_zero_row;
+        return rowp + 4 * (col < kD / 4 ? col : kD / 4 - 1);
+      } else {
+        // chunk c of the region: row c / 16, which holds chunk (c % 16) ^ (row % 16)
+        // of the key's row in K and chunk c % 16 in V
+        const int row = c >> 4, chunk = (c & 15) ^ (swizzled ? row & 15 : 0);
+        const int64_t off = s_off[row];
+        const uint16_t* rowp = off >= 0 ? reinterpret_cast<const uint16_t*>(base) + off
+                                        : reinterpret_cast<const uint16_t*>(g_zero_row);
+        return reinterpret_cast<const float*>(rowp + 8 * chunk);
+      }
     };
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int n = i * kWaves + wv;
-      srck[i] = src_of(A.k, kKPitch / 4, n < kKInstr ? n : 0);
-      srcv[i] = src_of(A.v, kVPitch / 4, n < kVInstr ? n : 0);
+      srck[i] = src_of(A.k, kKPitch / 4, n < kKInstr ? n : 0, true);
+      srcv[i] = src_of(A.v, kVPitch / 4, n < kVInstr ? n : 0, false);
     }
     // the rounds in which every wave has an instruction need no test
 #pragma unroll
@@ -900,7 +886,8 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       const int32_t kmaxh = (int32_t)(klim < -1 ? -1 : klim) - 4 * half;
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
       floatx16 sacc[NKB];
-      tile_scores<NKB>(s_k, qr, lr, half, sacc);
+      if constexpr (kF32) tile_scores<NKB>(s_k, qr, lr, half, sacc);
+      else tile_scores16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, lr, half, sacc);
       // ---- the first half of the next q rows (all of them for a 16-row tile)
       bool nq16 = false;
       const bool nq = next_q(p, nq16);
@@ -908,11 +895,15 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       float mb2, sum;
       tile_softmax<NKB, true>(sacc, full, s_valid[j & 1], half, kmaxh, c2, mb2, sum);
       floatx16 oacc[kD / 32];
-      tile_pv<NKB>(s_v, sacc, lr, half, oacc);
+      if constexpr (kF32) tile_pv<NKB>(s_v, sacc, lr, half, oacc);
+      else tile_pv16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), sacc, lr, half, oacc);
       // the second half, before the stores (a wait for a load also waits
       // for every store issued before it)
       if (nq && !nq16) load_q_rest(qp, qr);
-      if (row_ok) tile_store(A, row0, row, half, oacc, mb2, sum);
+      if (row_ok) {
+        if constexpr (kF32) tile_store(A, row0, row, half, oacc, mb2, sum);
+        else tile_store16(A, row0, row, half, oacc, mb2, sum);
+      }
     }
     if (sh.n32 < sh.npieces && sh.n32 >= second && ((sh.n32 - second) & 1) == 0) {
       const int ln = opaque_lane(lane), li = ln & 15, gq = ln >> 4;
@@ -923,14 +914,16 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
       float s16[2 * NKB][4];
-      tile16_scores<2 * NKB>(s_k, qr, li, gq, s16);
+      if constexpr (kF32) tile16_scores<2 * NKB>(s_k, qr, li, gq, s16);
+      else tile16_scores16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, li, gq, s16);
       bool nq16 = false;
       const bool nq = next_q(sh.n32, nq16);
       if (nq) load_q_first(qp, nq16, qr);
       float mb2, sum;
       tile16_softmax<2 * NKB>(s16, full, s_valid[j & 1], gq, kmax, c2, mb2, sum);
       floatx4 o16[8];
-      tile16_pv<2 * NKB>(s_v, s16, li, gq, o16);
+      if constexpr (kF32) tile16_pv<2 * NKB>(s_v, s16, li, gq, o16);
+      else tile16_pv16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), s16, li, gq, o16);
       if (nq && !nq16) load_q_rest(qp, qr);
       if (row_ok) tile16_store(A, row0, row, gq, o16, mb2, sum);
     }
@@ -1406,36 +1399,25 @@ hipError_t launch_mfma16_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, 
 }
 
 template <int NKB, int KVF>
-hipError_t launch_mfma_kv(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
+hipError_t launch_mfma_dma_kv(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
   static thread_local int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma<NKB, KVF>, 512, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma_dma<NKB, KVF>, 512, 0) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
   }
-  hipLaunchKernelGGL((k_fwd_mfma<NKB, KVF>), dim3((unsigned)per_cu * cus), dim3(512), 0, s, P, a);
+  hipLaunchKernelGGL((k_fwd_mfma_dma<NKB, KVF>), dim3((unsigned)per_cu * cus), dim3(512), 0, s, P, a);
   return hipGetLastError();
-}
-
-// 16-bit pages (fp32 pages take the direct-to-LDS kernel)
-template <int NKB>
-hipError_t launch_mfma_t(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
-  return a.kv_format == SA_KV_BF16 ? launch_mfma_kv<NKB, SA_KV_BF16>(P, a, s, cus)
-                                   : launch_mfma_kv<NKB, SA_KV_F16>(P, a, s, cus);
 }
 
 template <int NKB>
 hipError_t launch_mfma_dma(const IndexPtrs& P, const FwdArgs& a, hipStream_t s, unsigned cus) {
-  static thread_local int per_cu = 0;
-  if (per_cu == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd_mfma_dma<NKB>, 512, 0) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
+  switch (a.kv_format) {
+    case SA_KV_BF16: return launch_mfma_dma_kv<NKB, SA_KV_BF16>(P, a, s, cus);
+    case SA_KV_F16: return launch_mfma_dma_kv<NKB, SA_KV_F16>(P, a, s, cus);
+    default: return launch_mfma_dma_kv<NKB, SA_KV_F32>(P, a, s, cus);
   }
-  hipLaunchKernelGGL((k_fwd_mfma_dma<NKB>), dim3((unsigned)per_cu * cus), dim3(512), 0, s, P, a);
-  return hipGetLastError();
 }
 
 template <int D, int NKB, int WAVES>
@@ -1488,12 +1470,8 @@ hipError_t launch_forward_mfma(const sa_index* idx, const FwdArgs& a, hipStream_
   const int nkb = (a.block_size + 31) / 32;
   if (nkb <= 1) return launch_mfma16_t<1>(P, a, s, grid);
   if (nkb <= 2) return launch_mfma16_t<2>(P, a, s, grid);
-  if (a.kv_format == SA_KV_F32) {
-    if (nkb <= 3) return launch_mfma_dma<3>(P, a, s, grid);
-    return launch_mfma_dma<4>(P, a, s, grid);
-  }
-  if (nkb <= 3) return launch_mfma_t<3>(P, a, s, grid);
-  return launch_mfma_t<4>(P, a, s, grid);
+  if (nkb <= 3) return launch_mfma_dma<3>(P, a, s, grid);
+  return launch_mfma_dma<4>(P, a, s, grid);
 }
 
 }  // namespace sa

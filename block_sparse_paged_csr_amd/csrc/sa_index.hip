@@ -121,11 +121,7 @@ __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
     h->num_units_wave = 0;
     h->num_units_mfma = 0;
     h->num_slots = 0;
-    h->queue_mfma = 0;
-    h->done_mfma = 0;
     P.sort_hist[kSortGrid * kSortBuckets] = 0;   // the unit sort's counter
-    h->queue_wave = 0;
-    h->done_wave = 0;
     h->geom[0] = (int32_t)A.tq;
     h->geom[1] = A.hkv;
     h->geom[2] = A.topk;
@@ -1184,11 +1180,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
       hd->num_units_wave = uw0 + uw_h;
       hd->num_units_mfma = um0 + um_h;
       hd->num_slots = (int64_t)s_base_ns + ns_h;
-      hd->queue_mfma = 0;
-      hd->done_mfma = 0;
       P.sort_hist[kSortGrid * kSortBuckets] = 0;   // the unit sort's counter
-      hd->queue_wave = 0;
-      hd->done_wave = 0;
       hd->geom[0] = (int32_t)A.tq;
       hd->geom[1] = A.hkv;
       hd->geom[2] = A.topk;
@@ -1348,10 +1340,9 @@ bool fused_build_fits(int64_t tq, int32_t topk, int64_t nbs, int32_t batch, int3
          fused_lds_bytes(tq, topk, nbs, batch) <= kFusedMaxLds;
 }
 
-// The 32-row MFMA forward for head_dim 128 and blocks of 65..128 keys walks
-// the units in size order (the unit sort); other geometries do not read that
-// list. (A 16-bit forward on such an index takes the register-gather kernel,
-// which pulls units from a queue.)
+// The 32-row MFMA forward for head_dim 128 and blocks of 65..128 keys (fp32
+// or 16-bit pages) walks the units in size order (the unit sort); other
+// geometries do not read that list.
 inline bool unit_sort_needed(const sa_index* idx, const BuildArgs& a) {
   return a.mfma_min_rows != INT32_MAX && idx->head_dim == kMfmaHeadDim && a.block_size > 64 &&
          a.block_size <= kMfmaMaxBlock;

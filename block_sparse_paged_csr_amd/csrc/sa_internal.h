@@ -62,10 +62,6 @@ struct alignas(256) DevHeader {
   int32_t num_units_wave;
   int32_t num_units_mfma;
   int64_t num_slots;
-  uint32_t queue_mfma;          // dynamic unit queue of the MFMA kernel
-  uint32_t done_mfma;           // workgroups finished (last one resets the queue)
-  uint32_t queue_wave;
-  uint32_t done_wave;
   int32_t geom[8];              // planned geometry fingerprint
 };
 static_assert(sizeof(DevHeader) == 256, "header is one 256-byte block");
