@@ -139,7 +139,7 @@ ScratchLayout scratch_layout(const sa_index* idx) {
   L.units_sorted = o;
   o = align256(o + sizeof(Unit) * (size_t)idx->max_units);
   L.sort_hist = o;
-  o = align256(o + sizeof(int32_t) * ((size_t)kSortGrid * kSortBuckets + 1));
+  o = align256(o + sizeof(int32_t) * (size_t)kSortHistInts);
   L.end = o;
   return L;
 }

@@ -658,10 +658,21 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
 
   const DevHeader* hdr = P.hdr;
   if (hdr->status != SA_OK) return;
-  const int32_t num_units = hdr->num_units_mfma;
+  // The units, sorted by size (within groups of (sequence, head) pairs where
+  // the sort found the groups balanced: workgroup g, on XCD g % 8, then
+  // takes the units of group g % 8, and its XCD's L2 serves their q rows),
+  // dealt in a snake: units [lo, hi) to the Gs workgroups of the share.
+  const int32_t* sinfo = P.sort_hist + kSortHistInfo;
   const int32_t G = gridDim.x, g = blockIdx.x;
-  if (g >= num_units) return;
-  auto unit_at = [&](int32_t k) -> int32_t { return k * G + ((k & 1) ? G - 1 - g : g); };
+  int32_t lo = 0, hi = hdr->num_units_mfma, Gs = G, gs = g;
+  if (sinfo[0] != 0 && G % kSortGroups == 0) {
+    lo = sinfo[1 + g % kSortGroups];
+    hi = sinfo[2 + g % kSortGroups];
+    Gs = G / kSortGroups;
+    gs = g / kSortGroups;
+  }
+  auto unit_at = [&](int32_t k) -> int32_t { return lo + k * Gs + ((k & 1) ? Gs - 1 - gs : gs); };
+  if (unit_at(0) >= hi) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
   const int32_t qhead = A.qhead;
@@ -803,12 +814,12 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
   // ---- prologue: records of units 0..2, lists of units 0 and 1, offsets of
   // unit 0; then unit 0's first q rows, K and V
   fetch_record(0, unit_at(0));
-  if (unit_at(1) < num_units) fetch_record(1, unit_at(1));
-  if (unit_at(2) < num_units) fetch_record(2, unit_at(2));
+  if (unit_at(1) < hi) fetch_record(1, unit_at(1));
+  if (unit_at(2) < hi) fetch_record(2, unit_at(2));
   wait_vm<0>();
   lds_barrier();
   fetch_lists(0, unit_of(0));
-  if (unit_at(1) < num_units) fetch_lists(1, unit_of(1));
+  if (unit_at(1) < hi) fetch_lists(1, unit_of(1));
   wait_vm<0>();
   lds_barrier();
   form_offsets(0, 0);
@@ -831,10 +842,10 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
   gather_kv();
 
   for (int32_t j = 0;; ++j) {
-    if (unit_at(j) >= num_units) break;
+    if (unit_at(j) >= hi) break;
     const int ms = j % kSlots, ms1 = (j + 1) % kSlots, ms2 = (j + 2) % kSlots;
-    const bool has1 = unit_at(j + 1) < num_units, has2 = unit_at(j + 2) < num_units;
-    const bool has3 = unit_at(j + 3) < num_units;
+    const bool has1 = unit_at(j + 1) < hi, has2 = unit_at(j + 2) < hi;
+    const bool has3 = unit_at(j + 3) < hi;
     const Unit U = unit_of(ms);
     const int64_t block_start = (int64_t)U.blk * A.block_size;
     const int32_t nkeys = keys_of(U.blk, U.lk);

@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
     P.qinfo[q] = make_int2(b, (int32_t)kv_len_dev(A.used, b, A.msb, A.block_size));
   }
   if (blockIdx.x != 0) return;
+  for (int x = threadIdx.x; x < kSortBuckets; x += 256) P.sort_hist[kSortHistTotals + x] = 0;   // the sort's totals
   if (threadIdx.x == 0) {
     DevHeader* h = P.hdr;
     h->err_key = ~0ull;
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
     h->num_units_wave = 0;
     h->num_units_mfma = 0;
     h->num_slots = 0;
-    P.sort_hist[kSortGrid * kSortBuckets] = 0;   // the unit sort's counter
+    P.sort_hist[kSortHistCounter] = 0;           // the unit sort's counter
     h->geom[0] = (int32_t)A.tq;
     h->geom[1] = A.hkv;
     h->geom[2] = A.topk;
@@ -1166,6 +1167,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
       dst[u] = Unit{h, j, e_base + s0, e_base + s1, b, blk, lk, dl};
     }
   }
+  if (h == hkv - 1)
+    for (int x = tid; x < kSortBuckets; x += kFusedThreads) P.sort_hist[kSortHistTotals + x] = 0;   // the sort's totals
   if (tid == 0) {
     P.num_sel[h] = ns_h;
     P.edge_head_base[h] = hb;
@@ -1180,7 +1183,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
       hd->num_units_wave = uw0 + uw_h;
       hd->num_units_mfma = um0 + um_h;
       hd->num_slots = (int64_t)s_base_ns + ns_h;
-      P.sort_hist[kSortGrid * kSortBuckets] = 0;   // the unit sort's counter
+      P.sort_hist[kSortHistCounter] = 0;           // the unit sort's counter
       hd->geom[0] = (int32_t)A.tq;
       hd->geom[1] = A.hkv;
       hd->geom[2] = A.topk;
@@ -1224,10 +1227,13 @@ inline unsigned grid_for(int64_t n, int per) {
 constexpr int kSortThreads = 256;
 constexpr int kSortUnitsPerThread = 8;
 
-__device__ inline int unit_bucket(int32_t e0, int32_t e1, int32_t qhead) {
-  const int32_t tiles = ((e1 - e0) * qhead + 31) / 32;
-  const int32_t t = tiles < 1 ? 1 : (tiles > kSortBuckets ? kSortBuckets : tiles);
-  return kSortBuckets - t;                       // bucket 0: the largest units
+// Bucket of a unit: group (b * hkv + h) % kSortGroups, then size (32-row
+// tiles, bucket 0 of a group the largest).
+__device__ inline int unit_bucket(const int4& lo, int32_t b, int32_t hkv, int32_t qhead) {
+  const int32_t tiles = ((lo.w - lo.z) * qhead + 31) / 32;   // lo = (h, j, e0, e1)
+  const int32_t t = tiles < 1 ? 1 : (tiles > kSortSizes ? kSortSizes : tiles);
+  const int grp = (int)(((int64_t)b * hkv + lo.x) & (kSortGroups - 1));
+  return grp * kSortSizes + (kSortSizes - t);
 }
 
 // units [u0, u1) of workgroup g of the sort's grid
@@ -1237,52 +1243,94 @@ __device__ inline void sort_range(int32_t n, int32_t& u0, int32_t& u1) {
   u1 = u0 + per < n ? u0 + per : n;
 }
 
+// Counts per (bucket, workgroup), bucket-major with the grid's size as the
+// stride, and the buckets' totals. The last workgroup to finish chooses the
+// list's order and turns the counts into offsets: by group, then size
+// within a group, when every group holds within 10% of an even share of the
+// tiles (each XCD then takes one group, so its L2 serves the q rows of an
+// eighth of the (sequence, head) pairs); by size alone (the groups of a size
+// together) otherwise.
 __global__ __launch_bounds__(kSortThreads) void k_unit_count(IndexPtrs P, BuildArgs A) {
   __shared__ int32_t s_cnt[kSortBuckets];
   __shared__ bool s_last;
+  __shared__ int32_t s_grouped;
   if (P.hdr->status != SA_OK) return;            // a failed build: the forward does not run
   const int32_t n = P.hdr->num_units_mfma;
   const int tid = threadIdx.x;
-  if (tid < kSortBuckets) s_cnt[tid] = 0;
+  const int32_t G = (int32_t)gridDim.x;
+  for (int x = tid; x < kSortBuckets; x += kSortThreads) s_cnt[x] = 0;
   __syncthreads();
   int32_t u0, u1;
   sort_range(n, u0, u1);
-  const int2* e01 = reinterpret_cast<const int2*>(P.units_mfma);   // (e0, e1): int2 2u + 1 of a unit
+  const int4* src = reinterpret_cast<const int4*>(P.units_mfma);    // a unit is two int4: (h, j, e0, e1), (b, ...)
   for (int32_t base = u0; base < u1; base += kSortThreads * kSortUnitsPerThread) {
-    int2 v[kSortUnitsPerThread];
+    int4 lo[kSortUnitsPerThread];
+    int32_t bq[kSortUnitsPerThread];
 #pragma unroll
     for (int k = 0; k < kSortUnitsPerThread; ++k) {
       const int32_t u = base + k * kSortThreads + tid;
-      v[k] = e01[4 * (int64_t)(u < u1 ? u : u0) + 1];
+      const int32_t uu = u < u1 ? u : u0;
+      lo[k] = src[2 * (int64_t)uu];
+      bq[k] = reinterpret_cast<const int32_t*>(src + 2 * (int64_t)uu + 1)[0];
     }
 #pragma unroll
     for (int k = 0; k < kSortUnitsPerThread; ++k)
-      if (base + k * kSortThreads + tid < u1) atomicAdd(&s_cnt[unit_bucket(v[k].x, v[k].y, A.qhead)], 1);
+      if (base + k * kSortThreads + tid < u1) atomicAdd(&s_cnt[unit_bucket(lo[k], bq[k], A.hkv, A.qhead)], 1);
   }
   __syncthreads();
-  int32_t* hist = P.sort_hist;                   // [bucket][workgroup], then the counter
-  if (tid < kSortBuckets) hist[tid * kSortGrid + blockIdx.x] = s_cnt[tid];
-  // the last workgroup to finish turns the counts into offsets
+  int32_t* hist = P.sort_hist;
+  for (int x = tid; x < kSortBuckets; x += kSortThreads) {
+    hist[x * G + blockIdx.x] = s_cnt[x];
+    if (s_cnt[x] != 0) atomicAdd(&hist[kSortHistTotals + x], s_cnt[x]);
+  }
+  // the last workgroup to finish orders the list
   __threadfence();
   __syncthreads();
   if (tid == 0) {
-    const int32_t done = atomicAdd(&hist[kSortGrid * kSortBuckets], 1);
-    s_last = done == (int32_t)gridDim.x - 1;
+    const int32_t done = atomicAdd(&hist[kSortHistCounter], 1);
+    s_last = done == G - 1;
   }
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  // exclusive scan over (bucket, workgroup) in that order: thread t holds
-  // kSortGrid*64/256 consecutive counts
-  constexpr int kPer = kSortGrid * kSortBuckets / kSortThreads;
-  __shared__ int32_t s_part[kSortThreads];
-  int32_t c[kPer], sum = 0;
+  const int32_t* tot = hist + kSortHistTotals;
+  if (tid < 64) {
+    // tiles of each group: lane x < kSortGroups sums its group's sizes
+    int64_t w = 0;
+    if (tid < kSortGroups)
+      for (int sz = 0; sz < kSortSizes; ++sz)
+        w += (int64_t)__hip_atomic_load(&tot[tid * kSortSizes + sz], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) *
+             (kSortSizes - sz);
+    int64_t wmax = w, wsum = w;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int32_t i = tid * kPer + k;
-    const int32_t b = i / kSortGrid, g = i - b * kSortGrid;
-    c[k] = g < (int32_t)gridDim.x ? __hip_atomic_load(&hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-    sum += c[k];
+    for (int off = 32; off >= 1; off >>= 1) {
+      const int64_t om = __shfl_xor(wmax, off, 64), os = __shfl_xor(wsum, off, 64);
+      wmax = om > wmax ? om : wmax;
+      wsum += os;
+    }
+    if (tid == 0) s_grouped = wsum > 0 && 10 * kSortGroups * wmax <= 11 * wsum;
+  }
+  __syncthreads();
+  const bool grouped = s_grouped != 0;
+  // exclusive scan over the list's order: position i of the order is bucket
+  // grp * kSortSizes + sz, workgroup g, with i = ((grp, sz) or (sz, grp)) * G + g
+  // (walked incrementally: bucket bkt of the order and workgroup g)
+  auto phys = [&](int32_t bkt, int32_t g) -> int32_t {
+    const int32_t b2 = grouped ? bkt : (bkt % kSortGroups) * kSortSizes + bkt / kSortGroups;
+    return b2 * G + g;
+  };
+  const int32_t total = kSortBuckets * G;
+  const int32_t per = (total + kSortThreads - 1) / kSortThreads;
+  const int32_t i0 = tid * per, i1 = i0 + per < total ? i0 + per : total;
+  const int32_t bkt0 = i0 / G, g0 = i0 - bkt0 * G;
+  __shared__ int32_t s_part[kSortThreads];
+  int32_t sum = 0;
+  for (int32_t i = i0, bkt = bkt0, g = g0; i < i1; ++i) {
+    sum += __hip_atomic_load(&hist[phys(bkt, g)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (++g == G) {
+      g = 0;
+      ++bkt;
+    }
   }
   s_part[tid] = sum;
   __syncthreads();
@@ -1293,12 +1341,29 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_count(IndexPtrs P, BuildA
     __syncthreads();
   }
   int32_t run = s_part[tid] - sum;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    hist[tid * kPer + k] = run;
-    run += c[k];
+  for (int32_t i = i0, bkt = bkt0, g = g0; i < i1; ++i) {
+    const int32_t p = phys(bkt, g);
+    const int32_t c = hist[p];
+    hist[p] = run;
+    run += c;
+    if (++g == G) {
+      g = 0;
+      ++bkt;
+    }
   }
-  if (tid == 0) hist[kSortGrid * kSortBuckets] = 0;      // the counter, for the next build
+  __syncthreads();
+  // for the forward: the order, and each group's first unit
+  if (tid == 0) {
+    int32_t* info = hist + kSortHistInfo;
+    info[0] = grouped ? 1 : 0;
+    int32_t o = 0;
+    for (int x = 0; x < kSortGroups; ++x) {
+      info[1 + x] = o;
+      for (int sz = 0; sz < kSortSizes; ++sz) o += tot[x * kSortSizes + sz];
+    }
+    info[1 + kSortGroups] = o;
+    hist[kSortHistCounter] = 0;                    // the counter, for the next build
+  }
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_unit_place(IndexPtrs P, BuildArgs A) {
@@ -1306,7 +1371,8 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_place(IndexPtrs P, BuildA
   if (P.hdr->status != SA_OK) return;
   const int32_t n = P.hdr->num_units_mfma;
   const int tid = threadIdx.x;
-  if (tid < kSortBuckets) s_cur[tid] = P.sort_hist[tid * kSortGrid + blockIdx.x];
+  const int32_t G = (int32_t)gridDim.x;
+  for (int x = tid; x < kSortBuckets; x += kSortThreads) s_cur[x] = P.sort_hist[x * G + blockIdx.x];
   __syncthreads();
   int32_t u0, u1;
   sort_range(n, u0, u1);
@@ -1324,7 +1390,7 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_place(IndexPtrs P, BuildA
 #pragma unroll
     for (int k = 0; k < kSortUnitsPerThread; ++k) {
       if (base + k * kSortThreads + tid < u1) {
-        const int32_t pos = atomicAdd(&s_cur[unit_bucket(lo[k].z, lo[k].w, A.qhead)], 1);
+        const int32_t pos = atomicAdd(&s_cur[unit_bucket(lo[k], hi[k].x, A.hkv, A.qhead)], 1);
         dst[2 * (int64_t)pos] = lo[k];
         dst[2 * (int64_t)pos + 1] = hi[k];
       }

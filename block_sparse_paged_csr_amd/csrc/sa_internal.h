@@ -79,7 +79,7 @@ struct ScratchLayout {
   size_t agg;        // HeadAgg [hkv]     per-head totals published by the fused build
   size_t chunk_agg;  // ChunkAgg [hkv * scan_chunks(nbs)]  per-chunk sums of the slot scan
   size_t units_sorted;  // Unit [max_units]  the MFMA units, largest first (unit sort)
-  size_t sort_hist;  // int32 [kSortGrid * 64 + 1] per-workgroup bucket counts, then offsets; a counter
+  size_t sort_hist;  // int32 [kSortHistInts]: the unit sort's counts, counter, totals and group offsets
   size_t end;
 };
 
@@ -92,9 +92,22 @@ struct alignas(64) HeadAgg {
   uint64_t flag;
 };
 
-// Workgroups of the MFMA unit sort (a counting sort over 64 size buckets).
+// The MFMA unit sort: a counting sort over (group, size) buckets in up to
+// kSortGrid workgroups. A unit's group is (b * hkv + h) % kSortGroups, one
+// group for each XCD; its size bucket counts 32-row tiles, largest first
+// (units hold at most 2048 rows = 64 tiles). The sort array holds the
+// per-(bucket, workgroup) counts, then offsets [kSortBuckets * kSortGrid];
+// the workgroups' counter [1]; the buckets' totals [kSortBuckets]; and what
+// the forward reads [kSortGroups + 2]: whether the list is in groups, then
+// the groups' first units (kSortGroups + 1 offsets).
 constexpr int kSortGrid = 256;
-constexpr int kSortBuckets = 64;                 // units hold at most 2048 rows = 64 tiles
+constexpr int kSortSizes = 64;
+constexpr int kSortGroups = 8;
+constexpr int kSortBuckets = kSortSizes * kSortGroups;
+constexpr int kSortHistCounter = kSortBuckets * kSortGrid;
+constexpr int kSortHistTotals = kSortHistCounter + 1;
+constexpr int kSortHistInfo = kSortHistTotals + kSortBuckets;
+constexpr int kSortHistInts = kSortHistInfo + kSortGroups + 2;
 
 // Slots scanned by one workgroup of the multi-kernel build.
 constexpr int kScanChunkSlots = 2048;
