@@ -110,7 +110,6 @@ __global__ __launch_bounds__(256) void k_index_init(IndexPtrs P, BuildArgs A) {
     P.qinfo[q] = make_int2(b, (int32_t)kv_len_dev(A.used, b, A.msb, A.block_size));
   }
   if (blockIdx.x != 0) return;
-  for (int x = threadIdx.x; x < kSortBuckets; x += 256) P.sort_hist[kSortHistTotals + x] = 0;   // the sort's totals
   if (threadIdx.x == 0) {
     DevHeader* h = P.hdr;
     h->err_key = ~0ull;
@@ -1167,8 +1166,6 @@ __global__ __launch_bounds__(kFusedThreads) void k_index_fused(IndexPtrs P, Buil
       dst[u] = Unit{h, j, e_base + s0, e_base + s1, b, blk, lk, dl};
     }
   }
-  if (h == hkv - 1)
-    for (int x = tid; x < kSortBuckets; x += kFusedThreads) P.sort_hist[kSortHistTotals + x] = 0;   // the sort's totals
   if (tid == 0) {
     P.num_sel[h] = ns_h;
     P.edge_head_base[h] = hb;
@@ -1215,16 +1212,16 @@ inline unsigned grid_for(int64_t n, int per) {
 }
 
 // ------------------------------------------------------------ MFMA unit order
-// The MFMA units again, largest first (by 32-row tiles: 64 buckets; within a
-// bucket in any order), for the 32-row forward's static assignment: dealt in
-// a snake over the workgroups, a size-sorted list gives every workgroup a
-// near-equal share without a queue, and each workgroup knows its next units
-// in advance. A counting sort in two launches: kSortGrid workgroups count
-// their ranges of units into per-workgroup bucket counts, and the last one
-// to finish turns the counts into bucket-major offsets; then each workgroup
+// The MFMA units again, largest first (by 32-row tiles; within a bucket in
+// any order), for the 32-row forward's static assignment: dealt in a snake
+// over the workgroups, a size-sorted list gives every workgroup a near-equal
+// share without a queue, and each workgroup knows its next units in advance.
+// A counting sort in two launches of up to kSortGrid workgroups: each counts
+// its range of units into per-workgroup bucket counts, and the last one to
+// finish turns the counts into bucket-major offsets; then each workgroup
 // moves its units to their places. (The order inside a bucket may differ
 // from run to run; each unit's partials do not depend on where it runs.)
-constexpr int kSortThreads = 256;
+constexpr int kSortThreads = 512;
 constexpr int kSortUnitsPerThread = 8;
 
 // Bucket of a unit: group (b * hkv + h) % kSortGroups, then size (32-row
@@ -1243,22 +1240,24 @@ __device__ inline void sort_range(int32_t n, int32_t& u0, int32_t& u1) {
   u1 = u0 + per < n ? u0 + per : n;
 }
 
-// Counts per (bucket, workgroup), bucket-major with the grid's size as the
-// stride, and the buckets' totals. The last workgroup to finish chooses the
-// list's order and turns the counts into offsets: by group, then size
-// within a group, when every group holds within 10% of an even share of the
-// tiles (each XCD then takes one group, so its L2 serves the q rows of an
-// eighth of the (sequence, head) pairs); by size alone (the groups of a size
-// together) otherwise.
+// Counts per (bucket, workgroup), bucket-major with the grid's size (a
+// multiple of 4) as the stride. The last workgroup to finish chooses the
+// list's order and turns the counts into offsets, thread x for bucket x:
+// by group, then size within a group, when every group holds within 10% of
+// an even share of the tiles (each XCD then takes one group, so its L2
+// serves the q rows of an eighth of the (sequence, head) pairs); by size
+// alone (the groups of a size together) otherwise.
 __global__ __launch_bounds__(kSortThreads) void k_unit_count(IndexPtrs P, BuildArgs A) {
+  static_assert(kSortBuckets == kSortThreads && kSortSizes == 64 && kSortGroups == kSortThreads / 64,
+                "thread x of the sort holds bucket x: wave w holds group w, lane l its size index l");
+  static_assert(kSortGrid % 4 == 0, "a bucket's counts as int4");
   __shared__ int32_t s_cnt[kSortBuckets];
   __shared__ bool s_last;
-  __shared__ int32_t s_grouped;
   if (P.hdr->status != SA_OK) return;            // a failed build: the forward does not run
   const int32_t n = P.hdr->num_units_mfma;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t G = (int32_t)gridDim.x;
-  for (int x = tid; x < kSortBuckets; x += kSortThreads) s_cnt[x] = 0;
+  s_cnt[tid] = 0;
   __syncthreads();
   int32_t u0, u1;
   sort_range(n, u0, u1);
@@ -1279,10 +1278,7 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_count(IndexPtrs P, BuildA
   }
   __syncthreads();
   int32_t* hist = P.sort_hist;
-  for (int x = tid; x < kSortBuckets; x += kSortThreads) {
-    hist[x * G + blockIdx.x] = s_cnt[x];
-    if (s_cnt[x] != 0) atomicAdd(&hist[kSortHistTotals + x], s_cnt[x]);
-  }
+  hist[tid * G + blockIdx.x] = s_cnt[tid];
   // the last workgroup to finish orders the list
   __threadfence();
   __syncthreads();
@@ -1293,65 +1289,87 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_count(IndexPtrs P, BuildA
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  const int32_t* tot = hist + kSortHistTotals;
-  if (tid < 64) {
-    // tiles of each group: lane x < kSortGroups sums its group's sizes
-    int64_t w = 0;
-    if (tid < kSortGroups)
-      for (int sz = 0; sz < kSortSizes; ++sz)
-        w += (int64_t)__hip_atomic_load(&tot[tid * kSortSizes + sz], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) *
-             (kSortSizes - sz);
-    int64_t wmax = w, wsum = w;
+  __shared__ int32_t s_tot[kSortBuckets], s_base[kSortBuckets], s_wsum[kSortThreads / 64];
+  __shared__ int32_t s_gn[kSortGroups];
+  __shared__ int64_t s_w[kSortGroups];
+  __shared__ int32_t s_grouped;
+  // this thread's bucket over the workgroups, in registers
+  int4* col = reinterpret_cast<int4*>(hist + tid * G);
+  int32_t c[kSortGrid];
+#pragma unroll
+  for (int q = 0; q < kSortGrid / 4; ++q) {
+    const int4 v = 4 * q < G ? col[q] : make_int4(0, 0, 0, 0);
+    c[4 * q] = v.x;
+    c[4 * q + 1] = v.y;
+    c[4 * q + 2] = v.z;
+    c[4 * q + 3] = v.w;
+  }
+  int32_t tot = 0;
+#pragma unroll
+  for (int g = 0; g < kSortGrid; ++g) tot += c[g];
+  s_tot[tid] = tot;
+  {
+    // this wave's group: its units and tiles
+    int32_t un = tot;
+    int64_t w = (int64_t)tot * (kSortSizes - lane);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-      const int64_t om = __shfl_xor(wmax, off, 64), os = __shfl_xor(wsum, off, 64);
-      wmax = om > wmax ? om : wmax;
-      wsum += os;
+      un += __shfl_xor(un, off, 64);
+      w += __shfl_xor(w, off, 64);
     }
-    if (tid == 0) s_grouped = wsum > 0 && 10 * kSortGroups * wmax <= 11 * wsum;
+    if (lane == 0) {
+      s_gn[wave] = un;
+      s_w[wave] = w;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t wmax = 0, wsum = 0;
+    for (int k = 0; k < kSortGroups; ++k) {
+      wmax = s_w[k] > wmax ? s_w[k] : wmax;
+      wsum += s_w[k];
+    }
+    s_grouped = wsum > 0 && 10 * kSortGroups * wmax <= 11 * wsum;
   }
   __syncthreads();
   const bool grouped = s_grouped != 0;
-  // exclusive scan over the list's order: position i of the order is bucket
-  // grp * kSortSizes + sz, workgroup g, with i = ((grp, sz) or (sz, grp)) * G + g
-  // (walked incrementally: bucket bkt of the order and workgroup g)
-  auto phys = [&](int32_t bkt, int32_t g) -> int32_t {
-    const int32_t b2 = grouped ? bkt : (bkt % kSortGroups) * kSortSizes + bkt / kSortGroups;
-    return b2 * G + g;
-  };
-  const int32_t total = kSortBuckets * G;
-  const int32_t per = (total + kSortThreads - 1) / kSortThreads;
-  const int32_t i0 = tid * per, i1 = i0 + per < total ? i0 + per : total;
-  const int32_t bkt0 = i0 / G, g0 = i0 - bkt0 * G;
-  __shared__ int32_t s_part[kSortThreads];
-  int32_t sum = 0;
-  for (int32_t i = i0, bkt = bkt0, g = g0; i < i1; ++i) {
-    sum += __hip_atomic_load(&hist[phys(bkt, g)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (++g == G) {
-      g = 0;
-      ++bkt;
+  // thread o: position o of the list's order, bucket o (group-major) or
+  // (o % groups) * sizes + o / groups (size-major); exclusive scan of the
+  // totals in that order
+  const int32_t bo = grouped ? tid : (tid % kSortGroups) * kSortSizes + tid / kSortGroups;
+  const int32_t to = s_tot[bo];
+  int32_t incl = to;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int32_t before = 0;
+  for (int v = 0; v < wave; ++v) before += s_wsum[v];
+  s_base[bo] = before + incl - to;
+  __syncthreads();
+  // offsets of this thread's bucket: its first place, then the workgroups
+  // in order (an empty bucket is never read)
+  if (tot != 0) {
+    int32_t run = s_base[tid];
+#pragma unroll
+    for (int q = 0; q < kSortGrid / 4; ++q) {
+      if (4 * q < G) {
+        int4 v;
+        v.x = run;
+        run += c[4 * q];
+        v.y = run;
+        run += c[4 * q + 1];
+        v.z = run;
+        run += c[4 * q + 2];
+        v.w = run;
+        run += c[4 * q + 3];
+        col[q] = v;
+      }
     }
   }
-  s_part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kSortThreads; off <<= 1) {    // inclusive scan of the partial sums
-    const int32_t t = tid >= off ? s_part[tid - off] : 0;
-    __syncthreads();
-    s_part[tid] += t;
-    __syncthreads();
-  }
-  int32_t run = s_part[tid] - sum;
-  for (int32_t i = i0, bkt = bkt0, g = g0; i < i1; ++i) {
-    const int32_t p = phys(bkt, g);
-    const int32_t c = hist[p];
-    hist[p] = run;
-    run += c;
-    if (++g == G) {
-      g = 0;
-      ++bkt;
-    }
-  }
-  __syncthreads();
   // for the forward: the order, and each group's first unit
   if (tid == 0) {
     int32_t* info = hist + kSortHistInfo;
@@ -1359,7 +1377,7 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_count(IndexPtrs P, BuildA
     int32_t o = 0;
     for (int x = 0; x < kSortGroups; ++x) {
       info[1 + x] = o;
-      for (int sz = 0; sz < kSortSizes; ++sz) o += tot[x * kSortSizes + sz];
+      o += s_gn[x];
     }
     info[1 + kSortGroups] = o;
     hist[kSortHistCounter] = 0;                    // the counter, for the next build
@@ -1372,14 +1390,16 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_place(IndexPtrs P, BuildA
   const int32_t n = P.hdr->num_units_mfma;
   const int tid = threadIdx.x;
   const int32_t G = (int32_t)gridDim.x;
-  for (int x = tid; x < kSortBuckets; x += kSortThreads) s_cur[x] = P.sort_hist[x * G + blockIdx.x];
+  s_cur[tid] = P.sort_hist[tid * G + blockIdx.x];
   __syncthreads();
   int32_t u0, u1;
   sort_range(n, u0, u1);
-  const int4* src = reinterpret_cast<const int4*>(P.units_mfma);    // a unit is two int4
-  int4* dst = reinterpret_cast<int4*>(P.units_sorted);
+  // a unit is two 4-int vectors (native vectors: the arrays stay in registers)
+  typedef int32_t v4i __attribute__((ext_vector_type(4)));
+  const v4i* src = reinterpret_cast<const v4i*>(P.units_mfma);
+  v4i* dst = reinterpret_cast<v4i*>(P.units_sorted);
   for (int32_t base = u0; base < u1; base += kSortThreads * kSortUnitsPerThread) {
-    int4 lo[kSortUnitsPerThread], hi[kSortUnitsPerThread];
+    v4i lo[kSortUnitsPerThread], hi[kSortUnitsPerThread];
 #pragma unroll
     for (int k = 0; k < kSortUnitsPerThread; ++k) {
       const int32_t u = base + k * kSortThreads + tid;
@@ -1390,7 +1410,8 @@ __global__ __launch_bounds__(kSortThreads) void k_unit_place(IndexPtrs P, BuildA
 #pragma unroll
     for (int k = 0; k < kSortUnitsPerThread; ++k) {
       if (base + k * kSortThreads + tid < u1) {
-        const int32_t pos = atomicAdd(&s_cur[unit_bucket(lo[k], hi[k].x, A.hkv, A.qhead)], 1);
+        const int4 l = make_int4(lo[k].x, lo[k].y, lo[k].z, lo[k].w);
+        const int32_t pos = atomicAdd(&s_cur[unit_bucket(l, hi[k].x, A.hkv, A.qhead)], 1);
         dst[2 * (int64_t)pos] = lo[k];
         dst[2 * (int64_t)pos + 1] = hi[k];
       }
@@ -1414,10 +1435,13 @@ inline bool unit_sort_needed(const sa_index* idx, const BuildArgs& a) {
          a.block_size <= kMfmaMaxBlock;
 }
 
-// The sort's two launches; a grid of fewer workgroups than units.
+// The sort's two launches: a workgroup for every kSortThreads *
+// kSortUnitsPerThread units, 4 to kSortGrid of them in steps of 4.
 inline void launch_unit_sort(const sa_index* idx, const IndexPtrs& P, const BuildArgs& a, hipStream_t s) {
-  int64_t g = (idx->max_units + 1023) / 1024;
-  g = g < 1 ? 1 : (g > kSortGrid ? kSortGrid : g);
+  constexpr int64_t per = (int64_t)kSortThreads * kSortUnitsPerThread;
+  int64_t g = (idx->max_units + per - 1) / per;
+  g = (g + 3) / 4 * 4;
+  g = g < 4 ? 4 : (g > kSortGrid ? kSortGrid : g);
   hipLaunchKernelGGL(k_unit_count, dim3((unsigned)g), dim3(kSortThreads), 0, s, P, a);
   hipLaunchKernelGGL(k_unit_place, dim3((unsigned)g), dim3(kSortThreads), 0, s, P, a);
 }

@@ -79,7 +79,7 @@ struct ScratchLayout {
   size_t agg;        // HeadAgg [hkv]     per-head totals published by the fused build
   size_t chunk_agg;  // ChunkAgg [hkv * scan_chunks(nbs)]  per-chunk sums of the slot scan
   size_t units_sorted;  // Unit [max_units]  the MFMA units, largest first (unit sort)
-  size_t sort_hist;  // int32 [kSortHistInts]: the unit sort's counts, counter, totals and group offsets
+  size_t sort_hist;  // int32 [kSortHistInts]: the unit sort's counts, counter and group offsets
   size_t end;
 };
 
@@ -97,16 +97,15 @@ struct alignas(64) HeadAgg {
 // group for each XCD; its size bucket counts 32-row tiles, largest first
 // (units hold at most 2048 rows = 64 tiles). The sort array holds the
 // per-(bucket, workgroup) counts, then offsets [kSortBuckets * kSortGrid];
-// the workgroups' counter [1]; the buckets' totals [kSortBuckets]; and what
-// the forward reads [kSortGroups + 2]: whether the list is in groups, then
-// the groups' first units (kSortGroups + 1 offsets).
-constexpr int kSortGrid = 256;
+// the workgroups' counter [1]; and what the forward reads [kSortGroups +
+// 2]: whether the list is in groups, then the groups' first units
+// (kSortGroups + 1 offsets).
+constexpr int kSortGrid = 64;
 constexpr int kSortSizes = 64;
 constexpr int kSortGroups = 8;
 constexpr int kSortBuckets = kSortSizes * kSortGroups;
 constexpr int kSortHistCounter = kSortBuckets * kSortGrid;
-constexpr int kSortHistTotals = kSortHistCounter + 1;
-constexpr int kSortHistInfo = kSortHistTotals + kSortBuckets;
+constexpr int kSortHistInfo = kSortHistCounter + 1;
 constexpr int kSortHistInts = kSortHistInfo + kSortGroups + 2;
 
 // Slots scanned by one workgroup of the multi-kernel build.
