@@ -119,6 +119,79 @@ __device__ inline floatx4 zero4() {
   z[0] = z[1] = z[2] = z[3] = 0.f;
   return z;
 }
+
+// bf16 pages on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, the fused
+// decode forward): the K and V words enter the products as stored, and each
+// fp32 operand is written as a sum of bf16 terms by repeated truncation (q
+// three terms, which carry its 24 significand bits; p two terms, within
+// 2^-16 of it). A product of two bf16 values is exact in fp32 and the
+// products accumulate in fp32.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ inline float bf16_trunc(float x) { return __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
+// bf16 words of two values packed low half first
+__device__ inline uint32_t bf16_pack(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+__device__ inline bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, uintx4{a, b, c, d});
+}
+// The q row in the B-operand layout (q[i]: d = 32 (i >> 1) + 8g + 4 (i & 1)
+// .. +3) as three bf16 terms; word 4t + m of term k holds d = 32t + 8g + 2m
+// and 2m + 1, the elements of the K words they meet.
+__device__ inline void split_q_bf16(const floatx4 (&q)[8], uint32_t (&qw)[3][16]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float x0 = q[2 * t + (m >> 1)][2 * (m & 1)], x1 = q[2 * t + (m >> 1)][2 * (m & 1) + 1];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float h0 = bf16_trunc(x0), h1 = bf16_trunc(x1);
+        qw[k][4 * t + m] = bf16_pack(h0, h1);
+        x0 -= h0;
+        x1 -= h1;
+      }
+    }
+}
+// Scores of a K piece of bf16 words, S^T = K . Q^T: lane (li, g), reg r holds
+// key 4g + r of the piece against row li. Element e of lane group g stands
+// for d = 32t + 8g + e on both operands.
+__device__ inline floatx4 scores_bf16(const PieceT<kKvBf16>& kp, const uint32_t (&qw)[3][16]) {
+  floatx4 s0 = zero4(), s1 = zero4(), s2 = zero4();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bf16x8 kw = as_bf16x8(kp.x[2 * t].x, kp.x[2 * t].y, kp.x[2 * t + 1].x, kp.x[2 * t + 1].y);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        kw, as_bf16x8(qw[0][4 * t], qw[0][4 * t + 1], qw[0][4 * t + 2], qw[0][4 * t + 3]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        kw, as_bf16x8(qw[1][4 * t], qw[1][4 * t + 1], qw[1][4 * t + 2], qw[1][4 * t + 3]), s1, 0, 0, 0);
+    s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        kw, as_bf16x8(qw[2][4 * t], qw[2][4 * t + 1], qw[2][4 * t + 2], qw[2][4 * t + 3]), s2, 0, 0, 0);
+  }
+  return s0 + (s1 + s2);
+}
+// O^T += V^T . P^T for a V piece of bf16 words (row i of block db: d = 8i +
+// db), p[r] the probability of key 4g + r for row li. Element e of lane
+// group g stands for key 4g + (e & 3): p's high term for e < 4, its low
+// term for e >= 4, V's word twice. `fresh`: the products start the sums.
+__device__ inline void pv_bf16(const PieceT<kKvBf16>& vp, const float (&p)[4], floatx4 (&oacc)[8], bool fresh) {
+  float lo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lo[r] = p[r] - bf16_trunc(p[r]);
+  const bf16x8 pw = as_bf16x8(bf16_pack(p[0], p[1]), bf16_pack(p[2], p[3]), bf16_pack(lo[0], lo[1]),
+                              bf16_pack(lo[2], lo[3]));
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    // V[key 4g + r][8li + db]: half (db & 1) of word (db >> 1) & 1 of group 2r + (db >> 2)
+    uint32_t w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = (db & 2) ? vp.x[2 * r + (db >> 2)].y : vp.x[2 * r + (db >> 2)].x;
+    const uint32_t v01 = (db & 1) ? (w[0] >> 16) | (w[1] & 0xffff0000u) : (w[0] & 0xffffu) | (w[1] << 16);
+    const uint32_t v23 = (db & 1) ? (w[2] >> 16) | (w[3] & 0xffff0000u) : (w[2] & 0xffffu) | (w[3] << 16);
+    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v01, v23, v01, v23), pw,
+                                                       fresh ? zero4() : oacc[db], 0, 0, 0);
+  }
+}
 __device__ inline int32_t unit_keys(const Unit& U, int32_t block_size) {
   const int64_t start = (int64_t)U.blk * block_size;
   int64_t end = start + block_size;
@@ -290,6 +363,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     floatx4 oacc[8];
     float m_row = -INFINITY, l_row = 0.f;
     int32_t pre_rec = 0, pre_page = 0, pre_qi = 0;
+    uint32_t qw[KVF == kKvBf16 ? 3 : 1][16];      // bf16 pages: this unit's q as bf16 terms
 
     auto step = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
@@ -312,17 +386,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
         if constexpr (k < NCH) {
           // ---- scores of piece k: S^T = K . Q^T
-          floatx4 sa0 = zero4(), sa1 = zero4();
+          floatx4 s;                      // lane (li, g), reg r: key 16k + 4g + r, row li
+          if constexpr (KVF == kKvBf16) {
+            if constexpr (k == 0) split_q_bf16(qreg, qw);
+            s = scores_bf16(cur, qw);
+          } else {
+            floatx4 sa0 = zero4(), sa1 = zero4();
 #pragma unroll
-          for (int t = 0; t < 8; t += 2) {
+            for (int t = 0; t < 8; t += 2) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t, c), qreg[t][c], sa0, 0, 0, 0);
-              sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t + 1, c), qreg[t + 1][c], sa1,
-                                                         0, 0, 0);
+              for (int c = 0; c < 4; ++c) {
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t, c), qreg[t][c], sa0, 0, 0, 0);
+                sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t + 1, c), qreg[t + 1][c], sa1,
+                                                           0, 0, 0);
+              }
             }
+            s = sa0 + sa1;
           }
-          const floatx4 s = sa0 + sa1;    // lane (li, g), reg r: key 16k + 4g + r, row li
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kPiece * k + 4 * g + r;
@@ -355,13 +435,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         } else {
           // ---- O^T += V^T . P^T for piece c (row i of block db: d = 8i + db)
           constexpr int c = k - NCH;
+          if constexpr (KVF == kKvBf16) {
+            pv_bf16(cur, sreg[c], oacc, c == 0);
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 4; ++r) {
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-              const floatx4 acc = (c == 0 && r == 0) ? zero4() : oacc[db];
-              oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, 2 * r + (db >> 2), db & 3),
-                                                              sreg[c][r], acc, 0, 0, 0);
+              for (int db = 0; db < 8; ++db) {
+                const floatx4 acc = (c == 0 && r == 0) ? zero4() : oacc[db];
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, 2 * r + (db >> 2), db & 3),
+                                                                sreg[c][r], acc, 0, 0, 0);
+              }
             }
           }
         }
@@ -578,6 +662,10 @@ __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int i = 0; i < 8; ++i) qreg[i] = *(gfloatx4*)(src + 32 * (i >> 1) + 4 * (i & 1));
   }
+  // bf16 pages: the q row as three bf16 terms; word 4t + m of term k holds
+  // d = 32t + 8g + 2m and 2m + 1, the elements of the K words it meets
+  uint32_t qw[KVF == kKvBf16 ? 3 : 1][16];
+  if constexpr (KVF == kKvBf16) split_q_bf16(qreg, qw);
   block_meta(0, 0);
   Piece bufA, bufB;
   load_piece(IC<0>{}, 0, n_blk > 0, bufA);
@@ -614,17 +702,22 @@ __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_e
         else load_piece(IC<0>{}, ks1, more, nxt);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (j < NCH) {
-          floatx4 sa0 = zero4(), sa1 = zero4();
+          floatx4 s;                      // lane (li, g), reg r: key 16j + 4g + r, row li
+          if constexpr (KVF == kKvBf16) {
+            s = scores_bf16(cur, qw);
+          } else {
+            floatx4 sa0 = zero4(), sa1 = zero4();
 #pragma unroll
-          for (int t = 0; t < 8; t += 2) {
+            for (int t = 0; t < 8; t += 2) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t, c), qreg[t][c], sa0, 0, 0, 0);
-              sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t + 1, c), qreg[t + 1][c], sa1,
-                                                         0, 0, 0);
+              for (int c = 0; c < 4; ++c) {
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t, c), qreg[t][c], sa0, 0, 0, 0);
+                sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, t + 1, c), qreg[t + 1][c], sa1,
+                                                           0, 0, 0);
+              }
             }
+            s = sa0 + sa1;
           }
-          const floatx4 s = sa0 + sa1;    // lane (li, g), reg r: key 16j + 4g + r, row li
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kPiece * j + 4 * g + r;
@@ -662,12 +755,16 @@ __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_e
           }
         } else {
           constexpr int c = j - NCH;
+          if constexpr (KVF == kKvBf16) {
+            pv_bf16(cur, sreg[c], oacc, false);
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < 4; ++r) {
 #pragma unroll
-            for (int db = 0; db < 8; ++db)
-              oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, 2 * r + (db >> 2), db & 3),
-                                                              sreg[c][r], oacc[db], 0, 0, 0);
+              for (int db = 0; db < 8; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv_elem(cur, 2 * r + (db >> 2), db & 3),
+                                                                sreg[c][r], oacc[db], 0, 0, 0);
+            }
           }
         }
       }
