@@ -56,7 +56,8 @@ def parse():
                         "or with 256-key blocks (the chunked MFMA kernel's geometries)")
     p.add_argument("--rotate", type=int, default=4, help="independent input batches cycled")
     p.add_argument("--kv-dtype", default="f32", choices=["f32", "bf16", "fp16"],
-                   help="storage of the K/V pages (16-bit: sa_forward_kv16, fp32 arithmetic)")
+                   help="storage of the K/V pages (16-bit: sa_forward_kv16, or "
+                        "sa_forward_combine_kv16 for decode-shaped batches)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target wall time of the oracle leg (all its worker processes)")
@@ -286,15 +287,15 @@ def main():
         w = s["w"]
         sa.sa_combine(s["idx"], s["o"], s["m"], s["l"], w.hq, w.head_dim, s["out"], s["lse"])
 
-    fused = (not args.two_pass and not kv16 and base.tq == base.batch and
+    fused = (not args.two_pass and base.tq == base.batch and
              sa.fused_fits(base.hq, base.hkv, base.head_dim, base.block_size, base.page_size,
                            base.topk))
 
     def forward_combine(s):
         w = s["w"]
-        sa.sa_forward_combine(s["idx"], s["sel"], s["q"], k, v, s["bt"], s["cu"], s["used"], w.hq,
-                              w.hkv, w.head_dim, w.block_size, w.page_size, w.softmax_scale,
-                              w.causal, s["out"], s["lse"])
+        fc = sa.sa_forward_combine_kv16 if kv16 else sa.sa_forward_combine
+        fc(s["idx"], s["sel"], s["q"], k, v, s["bt"], s["cu"], s["used"], w.hq, w.hkv,
+           w.head_dim, w.block_size, w.page_size, w.softmax_scale, w.causal, s["out"], s["lse"])
 
     def step(s):
         # what sa_attention runs: the build, then the fused forward + combine for

@@ -97,6 +97,8 @@ def _declare(lib):
         "sa_combine": [idxp, vp, vp, vp, i32, i32, vp, vp, vp],
         "sa_forward_combine": [idxp, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, vp, i32, i32, i32,
                                i32, i32, c_float, i32, vp, vp, vp],
+        "sa_forward_combine_kv16": [idxp, vp, i64, vp, i64, vp, i64, vp, i64, i32, vp, vp, vp, i32,
+                                    i32, i32, i32, i32, c_float, i32, vp, vp, vp],
         "sa_attention_workspace_bytes": [i64, i32, i32, i32, i32, i32, i32, i32, i32,
                                          POINTER(c_size_t)],
         "sa_attention": [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64,
@@ -327,6 +329,37 @@ def sa_forward_combine(index: Index, selected, q, k_pages, v_pages, block_tables
     return out, lse
 
 
+def sa_forward_combine_kv16(index: Index, selected, q, k_pages, v_pages, block_tables,
+                            cu_seqlens_q, used_kv_lens, hq, hkv, head_dim, block_size, page_size,
+                            softmax_scale, causal, out=None, lse=None, with_lse=True):
+    """sa_forward_combine with K/V pages stored as bfloat16 or float16 tensors
+    (the format follows their dtype; both must match): returns (out, lse)."""
+    _check_head_dims(q, k_pages, v_pages)
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        if not isinstance(t, torch.Tensor) or t.dtype not in _KV16_FORMATS:
+            raise TypeError(f"{name} must be a bfloat16 or float16 tensor")
+    if k_pages.dtype != v_pages.dtype:
+        raise TypeError("k_pages and v_pages must share one dtype")
+    dev = q.device
+    tq = index.c.tq
+    if out is None:
+        out = torch.empty((tq, hq, head_dim), dtype=torch.float32, device=dev)
+    if lse is None and with_lse:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=dev)
+    st = lib().sa_forward_combine_kv16(
+        ctypes.byref(index.c), _ptr(selected, torch.int32, "selected"), selected.numel(),
+        _ptr(q, torch.float32, "q"), q.numel(),
+        _ptr(k_pages, k_pages.dtype, "k_pages"), k_pages.numel(),
+        _ptr(v_pages, v_pages.dtype, "v_pages"), v_pages.numel(), _KV16_FORMATS[k_pages.dtype],
+        _ptr(block_tables, torch.int32, "block_tables"),
+        _ptr(cu_seqlens_q, torch.int64, "cu_seqlens_q"),
+        _ptr(used_kv_lens, torch.int32, "used_kv_lens"),
+        hq, hkv, head_dim, block_size, page_size, float(softmax_scale), int(bool(causal)),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), _stream(dev))
+    _check(st)
+    return out, lse
+
+
 def fused_fits(hq, hkv, head_dim, block_size, page_size, topk):
     """Whether sa_forward_combine takes this geometry (include/sa.h)."""
     return head_dim == 128 and block_size <= 64 and hq // hkv <= 16 and topk <= 512
@@ -482,6 +515,7 @@ def index_arrays(index: Index, info: dict | None = None) -> dict:
 __all__ = [
     "SaError", "SaIndex", "Index", "Workspace", "lib", "sa_index_plan", "sa_build_index",
     "sa_index_status", "sa_forward", "sa_forward_kv16", "sa_combine", "sa_forward_combine",
+    "sa_forward_combine_kv16",
     "fused_fits", "sa_attention",
     "SA_KV_F32", "SA_KV_BF16", "SA_KV_F16",
     "sa_attention_workspace_bytes", "sa_attention_noalloc", "SA_NOALLOC_SCRATCH_BYTES",

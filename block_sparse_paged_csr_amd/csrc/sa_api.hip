@@ -471,17 +471,22 @@ sa_status sa_combine(const sa_index* idx, const float* o_partial, const float* m
   return ok();
 }
 
-sa_status sa_forward_combine(const sa_index* idx, const int32_t* selected, int64_t selected_len,
-                             const float* q, int64_t q_len, const float* k_pages, int64_t k_len,
-                             const float* v_pages, int64_t v_len, const int32_t* block_tables,
-                             const int64_t* cu_seqlens_q, const int32_t* used_kv_lens,
-                             int32_t hq, int32_t hkv, int32_t head_dim, int32_t block_size,
-                             int32_t page_size, float softmax_scale, int32_t causal, float* out,
-                             float* lse, hipStream_t stream) {
+namespace {
+
+// sa_forward_combine's checks (sa_forward's, then the selections and the
+// fused geometry) and launch, for fp32 or 16-bit pages
+sa_status forward_combine_impl(const sa_index* idx, const int32_t* selected, int64_t selected_len,
+                               const float* q, int64_t q_len, const void* k_pages, int64_t k_len,
+                               const void* v_pages, int64_t v_len, bool kv16, int32_t kv_format,
+                               const int32_t* block_tables, const int64_t* cu_seqlens_q,
+                               const int32_t* used_kv_lens, int32_t hq, int32_t hkv,
+                               int32_t head_dim, int32_t block_size, int32_t page_size,
+                               float softmax_scale, int32_t causal, float* out, float* lse,
+                               hipStream_t stream) {
   sa::FwdArgs a{};
   sa_status st = forward_checks(idx, q, q_len, k_pages, k_len, v_pages, v_len, block_tables,
                                 cu_seqlens_q, used_kv_lens, hq, hkv, head_dim, block_size,
-                                page_size, softmax_scale, causal, false, SA_KV_F32, nullptr,
+                                page_size, softmax_scale, causal, kv16, kv_format, nullptr,
                                 nullptr, nullptr, &a);
   if (st != SA_OK) return st;
   const int64_t want_sel = idx->tq * (int64_t)idx->hkv * idx->topk;
@@ -493,6 +498,36 @@ sa_status sa_forward_combine(const sa_index* idx, const int32_t* selected, int64
   hipError_t e = sa::launch_forward_fused(idx, a, selected, out, lse, stream);
   if (e != hipSuccess) return runtime_error(e, "fused forward launch");
   return ok();
+}
+
+}  // namespace
+
+sa_status sa_forward_combine(const sa_index* idx, const int32_t* selected, int64_t selected_len,
+                             const float* q, int64_t q_len, const float* k_pages, int64_t k_len,
+                             const float* v_pages, int64_t v_len, const int32_t* block_tables,
+                             const int64_t* cu_seqlens_q, const int32_t* used_kv_lens,
+                             int32_t hq, int32_t hkv, int32_t head_dim, int32_t block_size,
+                             int32_t page_size, float softmax_scale, int32_t causal, float* out,
+                             float* lse, hipStream_t stream) {
+  return forward_combine_impl(idx, selected, selected_len, q, q_len, k_pages, k_len, v_pages,
+                              v_len, false, SA_KV_F32, block_tables, cu_seqlens_q, used_kv_lens,
+                              hq, hkv, head_dim, block_size, page_size, softmax_scale, causal,
+                              out, lse, stream);
+}
+
+sa_status sa_forward_combine_kv16(const sa_index* idx, const int32_t* selected,
+                                  int64_t selected_len, const float* q, int64_t q_len,
+                                  const uint16_t* k_pages, int64_t k_len,
+                                  const uint16_t* v_pages, int64_t v_len, int32_t kv_format,
+                                  const int32_t* block_tables, const int64_t* cu_seqlens_q,
+                                  const int32_t* used_kv_lens, int32_t hq, int32_t hkv,
+                                  int32_t head_dim, int32_t block_size, int32_t page_size,
+                                  float softmax_scale, int32_t causal, float* out, float* lse,
+                                  hipStream_t stream) {
+  return forward_combine_impl(idx, selected, selected_len, q, q_len, k_pages, k_len, v_pages,
+                              v_len, true, kv_format, block_tables, cu_seqlens_q, used_kv_lens,
+                              hq, hkv, head_dim, block_size, page_size, softmax_scale, causal,
+                              out, lse, stream);
 }
 
 sa_status sa_attention_workspace_bytes(int64_t tq, int32_t hkv, int32_t topk, int32_t batch,

@@ -199,9 +199,13 @@ sa_status sa_forward(const sa_index* idx,
                      float* o_partial, float* m_partial, float* l_partial,
                      hipStream_t stream);
 
-/* Storage formats of K/V pages for sa_forward_kv16. The pages define fp32
- * pages only; 16-bit storage is converted exactly to fp32 where it is used,
- * so the arithmetic and its tolerance are the fp32 path's on the stored
+/* Storage formats of K/V pages for sa_forward_kv16 and
+ * sa_forward_combine_kv16. The pages define fp32 pages only. 16-bit storage
+ * is converted exactly to fp32 where it is used, except that bf16 pages of
+ * the one-wave kernels (head_dim 128, blocks of at most 64 keys, units of at
+ * most 16 rows, and the fused forward) are multiplied on the bf16 matrix
+ * cores as stored, with q written as three bf16 terms and the probabilities
+ * as two; either way the tolerance is the fp32 path's on the stored
  * values. */
 typedef enum sa_kv_format {
   SA_KV_F32 = 0,   /* float32 (sa_forward) */
@@ -265,6 +269,25 @@ sa_status sa_forward_combine(const sa_index* idx,
                              int32_t block_size, int32_t page_size,
                              float softmax_scale, int32_t causal,
                              float* out, float* lse, hipStream_t stream);
+
+/* sa_forward_combine_kv16: sa_forward_combine with K/V pages stored as
+ * 16-bit words (`kv_format` SA_KV_BF16 or SA_KV_F16; k_len / v_len count
+ * elements), as sa_forward_kv16 takes them. Every other argument, what is
+ * written and the host checks are sa_forward_combine's, with UNSUPPORTED
+ * "kv_format" for another format after sa_forward's SHAPE checks (its place
+ * in sa_forward_kv16). */
+sa_status sa_forward_combine_kv16(const sa_index* idx,
+                                  const int32_t* selected, int64_t selected_len,
+                                  const float* q, int64_t q_len,
+                                  const uint16_t* k_pages, int64_t k_len,
+                                  const uint16_t* v_pages, int64_t v_len,
+                                  int32_t kv_format,
+                                  const int32_t* block_tables, const int64_t* cu_seqlens_q,
+                                  const int32_t* used_kv_lens,
+                                  int32_t hq, int32_t hkv, int32_t head_dim,
+                                  int32_t block_size, int32_t page_size,
+                                  float softmax_scale, int32_t causal,
+                                  float* out, float* lse, hipStream_t stream);
 
 /* sa_attention_workspace_bytes: bytes of the workspace that sa_attention
  * needs: the index buffer plus the worst-case partials, 256-B aligned. */

@@ -220,3 +220,32 @@ def test_kv16_shape_checks_come_first():
                              None, hkv * qhead, hkv, d, bs, ps, 0.1, 1, ctypes.c_void_p(16),
                              ctypes.c_void_p(16), ctypes.c_void_p(16), None)
     assert sa.STATUS_NAMES[st] == "ShapeMismatch"
+
+
+def _fused_kv16_call(idx, sel_len, q_len, d, bs, ps, hq, hkv, fmt):
+    lib = sa.lib()
+    n = 4 * hkv * ps * d
+    return lib.sa_forward_combine_kv16(
+        ctypes.byref(idx.c), ctypes.c_void_p(16), sel_len, ctypes.c_void_p(16), q_len,
+        ctypes.c_void_p(16), n, ctypes.c_void_p(16), n, fmt, ctypes.c_void_p(16),
+        ctypes.c_void_p(16), None, hq, hkv, d, bs, ps, 0.1, 1, ctypes.c_void_p(16),
+        ctypes.c_void_p(16), None)
+
+
+@pytest.mark.parametrize("case", ["q", "kv_format"])
+def test_fused_kv16_host_checks_in_order(case):
+    # sa_forward's shape checks, then the format, before any device access
+    # (the selections and the fused geometry come after the device check:
+    # tested on the GPU)
+    hkv, ps, d, qhead, topk, tq, bs = 2, 16, 128, 4, 2, 4, 64
+    hq = hkv * qhead
+    idx = sa.sa_index_plan(tq, hkv, topk, 1, 16, bs, ps, hq, d, 4)
+    idx.c.buffer = 4096
+    q_len = 5 if case == "q" else tq * hq * d
+    fmt = 3 if case == "kv_format" else sa.SA_KV_BF16
+    st = _fused_kv16_call(idx, tq * hkv * topk, q_len, d, bs, ps, hq, hkv, fmt)
+    det = sa.SaErrorDetail()
+    sa.lib().sa_last_error(ctypes.byref(det))
+    want = {"q": ("ShapeMismatch", "q"), "kv_format": ("Unsupported", "kv_format")}
+    assert sa.STATUS_NAMES[st] == want[case][0]
+    assert det.what.decode().startswith(want[case][1])

@@ -128,6 +128,65 @@ def test_decode_workload_kv16(fmt):
     print(f"[gpu case] kv16 decode {fmt}: O rel err {err:.3e}", flush=True)
 
 
+# The fused forward + combine on 16-bit pages (sa_forward_combine_kv16):
+# decode-like batches (one or two queries a sequence, empty sequences) against
+# the oracle on the decoded pages and against the two-pass 16-bit path; with
+# fp16 pages (exact conversion) bitwise the fused fp32 path on the decoded
+# values.
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+@pytest.mark.parametrize("seed", range(6))
+def test_fused_forward_combine_kv16(fmt, seed):
+    ps, ppb = [(16, 4), (16, 1), (8, 2), (4, 4), (16, 3), (32, 2)][seed]
+    w = W.make_random(4600 + seed, batch=1 + seed % 7, qo_max=[1, 2][seed % 2], kv_max=400,
+                      hkv=1 + seed % 3, qhead=[1, 2, 4, 8, 16][seed % 5], head_dim=128,
+                      page_size=ps, pages_per_block=ppb, topk=1 + seed % 9,
+                      causal=bool(seed % 3))
+    print(f"[gpu case] fused kv16 {fmt} seed={seed} tq={w.tq} bs={w.block_size}", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, fmt)
+    idx = run_index(w, d)
+    out, lse = sa.sa_forward_combine_kv16(idx, d["sel"], d["q"], kt, vt, *_fwd_args(w, d))
+    kd, vd = oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt)
+    _check(w, kd, vd, out, lse)
+    o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+    out2, lse2 = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    assert max_rel_err(out.cpu().numpy(), out2.cpu().numpy())[0] <= 1e-5
+    fin = torch.isfinite(lse2)
+    assert torch.equal(fin, torch.isfinite(lse))
+    if fin.any():
+        assert (lse[fin] - lse2[fin]).abs().max().item() <= 1e-5
+    if fmt == "fp16":
+        out3, lse3 = sa.sa_forward_combine(idx, d["sel"], d["q"], torch.from_numpy(kd).cuda(),
+                                           torch.from_numpy(vd).cuda(), *_fwd_args(w, d))
+        assert torch.equal(out3, out) and torch.equal(lse3, lse)
+
+
+def test_fused_kv16_rejects_geometry_and_selections():
+    w = W.make_random(4650, batch=2, qo_max=1, kv_max=200, hkv=1, qhead=2, head_dim=64,
+                      page_size=16, pages_per_block=2, topk=3)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, "bf16")
+    idx = run_index(w, d)
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_forward_combine_kv16(idx, d["sel"], d["q"], kt, vt, *_fwd_args(w, d))
+    assert ei.value.kind == "Unsupported"
+    with pytest.raises(sa.SaError) as ei:
+        sa.sa_forward_combine_kv16(idx, d["sel"][:-1], d["q"], kt, vt, *_fwd_args(w, d))
+    assert (ei.value.kind, ei.value.what) == ("ShapeMismatch", "selected")
+
+
+def test_decode_workload_fused_kv16_bf16():
+    w = W.make_config("decode")
+    print("[gpu case] fused kv16 decode bf16", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, "bf16")
+    idx = run_index(w, d)
+    out, lse = sa.sa_forward_combine_kv16(idx, d["sel"], d["q"], kt, vt, *_fwd_args(w, d))
+    torch.cuda.synchronize()
+    err = _check(w, oracle.decode_kv16(k, "bf16"), oracle.decode_kv16(v, "bf16"), out, lse)
+    print(f"[gpu case] fused kv16 decode bf16: O rel err {err:.3e}", flush=True)
+
+
 def test_ragged_workload_bf16_sampled():
     w = W.make_config("ragged")
     print("[gpu case] kv16 ragged bf16", flush=True)
