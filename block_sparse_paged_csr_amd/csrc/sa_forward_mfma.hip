@@ -496,6 +496,118 @@ __device__ __forceinline__ void tile_pv16(const uint16_t* sv, const floatx16 (&s
   }
 }
 
+// bf16 pages on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16): the K and
+// V words enter the products as stored, and each fp32 operand is written as
+// a sum of bf16 terms by repeated truncation (q three terms, which carry its
+// 24 significand bits; p two, within 2^-16 of it). A product of two bf16
+// values is exact in fp32, and the products accumulate in fp32.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int uintx4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float bf16_trunc(float x) { return __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(bf16x8, uintx4v{a, b, c, d});
+}
+
+// S^T = K . Q^T with bf16 K words: step p takes chunk half*8 + p of the lane's
+// key row (d = half*64 + 8p .. +7, the k slots of the lane's half) and the
+// same d of q, split into three terms at the step.
+template <int NKB>
+__device__ __forceinline__ void tile_scores_bf16(const uint16_t* sk, const float4 (&qr)[16], int lr, int half,
+                                                 floatx16 (&sacc)[NKB]) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
+  uint4 kc[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) kc[kb] = *reinterpret_cast<const uint4*>(&sk[swz16(kb * 32 + lr, half * 8)]);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    uint4 kn[NKB];
+    if (p < 7) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        kn[kb] = *reinterpret_cast<const uint4*>(&sk[swz16(kb * 32 + lr, half * 8 + p + 1)]);
+    }
+    float x[8] = {qr[2 * p].x, qr[2 * p].y, qr[2 * p].z, qr[2 * p].w,
+                  qr[2 * p + 1].x, qr[2 * p + 1].y, qr[2 * p + 1].z, qr[2 * p + 1].w};
+    uint32_t w[3][4];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float h0 = bf16_trunc(x[2 * m]), h1 = bf16_trunc(x[2 * m + 1]);
+        w[t][m] = bf16_pack(h0, h1);
+        x[2 * m] -= h0;
+        x[2 * m + 1] -= h1;
+      }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const bf16x8 k = as_bf16x8(kc[kb].x, kc[kb].y, kc[kb].z, kc[kb].w);
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, as_bf16x8(w[t][0], w[t][1], w[t][2], w[t][3]),
+                                                           sacc[kb], 0, 0, 0);
+    }
+    if (p < 7) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
+    }
+  }
+}
+
+// O^T = V^T . P^T with bf16 V words. Step (kb, u) takes the lane's
+// accumulators 8u .. 8u + 7 of block kb: element e stands for key kb*32 +
+// 16u + 8(e/4) + 4half + e%4 on both operands (p, split into two terms, and
+// the V words of those keys at the lane's words 4 phi(lr) .. +3, as in
+// tile_pv16, so tile_store16 writes the result).
+template <int NKB>
+__device__ __forceinline__ void tile_pv_bf16(const uint16_t* sv, const floatx16 (&sacc)[NKB], int lr, int half,
+                                             floatx16 (&oacc)[4]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = zero16();
+  const int word = pv16_word(lr);
+  auto read_v = [&](int kb, int u, uint2 (&dst)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      dst[e] = *reinterpret_cast<const uint2*>(&sv[(kb * 32 + 16 * u + 8 * (e >> 2) + 4 * half + (e & 3)) * 128 + word]);
+  };
+  uint2 vc[8];
+  read_v(0, 0, vc);
+#pragma unroll
+  for (int st = 0; st < 2 * NKB; ++st) {
+    const int kb = st >> 1, u = st & 1;
+    uint2 vn[8];
+    if (st + 1 < 2 * NKB) read_v((st + 1) >> 1, (st + 1) & 1, vn);
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float a = sacc[kb][8 * u + 2 * m], b = sacc[kb][8 * u + 2 * m + 1];
+      ph[m] = bf16_pack(a, b);
+      pl[m] = bf16_pack(a - bf16_trunc(a), b - bf16_trunc(b));
+    }
+    const bf16x8 phi = as_bf16x8(ph[0], ph[1], ph[2], ph[3]), plo = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      // word db of key e's four: half db & 1 of .x (db < 2) or .y
+      uint32_t a[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w0 = db < 2 ? vc[2 * m].x : vc[2 * m].y, w1 = db < 2 ? vc[2 * m + 1].x : vc[2 * m + 1].y;
+        a[m] = (db & 1) ? (w0 >> 16) | (w1 & 0xffff0000u) : (w0 & 0xffffu) | (w1 << 16);
+      }
+      const bf16x8 v = as_bf16x8(a[0], a[1], a[2], a[3]);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, phi, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, plo, oacc[db], 0, 0, 0);
+    }
+    if (st + 1 < 2 * NKB) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vc[e] = vn[e];
+    }
+  }
+}
+
 // Accumulator i = 4g + c of block db holds d = 4 phi(8g + 4half + c) + db =
 // 32g + 8c + 4half + db of row `row`.
 __device__ __forceinline__ void tile_store16(const FwdArgs& A, int64_t row0, int32_t row, int half,
@@ -898,6 +1010,7 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
       floatx16 sacc[NKB];
       if constexpr (kF32) tile_scores<NKB>(s_k, qr, lr, half, sacc);
+      else if constexpr (KVF == SA_KV_BF16) tile_scores_bf16<NKB>(reinterpret_cast<const uint16_t*>(s_k), qr, lr, half, sacc);
       else tile_scores16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, lr, half, sacc);
       // ---- the first half of the next q rows (all of them for a 16-row tile)
       bool nq16 = false;
@@ -907,6 +1020,7 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       tile_softmax<NKB, true>(sacc, full, s_valid[j & 1], half, kmaxh, c2, mb2, sum);
       floatx16 oacc[kD / 32];
       if constexpr (kF32) tile_pv<NKB>(s_v, sacc, lr, half, oacc);
+      else if constexpr (KVF == SA_KV_BF16) tile_pv_bf16<NKB>(reinterpret_cast<const uint16_t*>(s_v), sacc, lr, half, oacc);
       else tile_pv16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), sacc, lr, half, oacc);
       // the second half, before the stores (a wait for a load also waits
       // for every store issued before it)

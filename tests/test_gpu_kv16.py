@@ -9,10 +9,11 @@ On the same index, the 16-bit forward and the fp32 forward on the decoded
 values give bitwise identical partials where the kernel converts each word
 exactly to fp32 (same arithmetic on the same fp32 operands). The one-wave
 kernel (head_dim 128, blocks of at most 64 keys, at most 16 rows a unit)
-instead runs bf16 pages on the bf16 matrix cores, q as three bf16 terms and
-the probabilities p as two: there the partials match the fp32 path's to
-within the low term that p's split drops (below 2^-16 p a key), bounded
-per row by 2^-16 * l * max|V|.
+and the 32-row tiles of the direct-to-LDS MFMA kernel (blocks of 65..128
+keys) instead run bf16 pages on the bf16 matrix cores, q as three bf16
+terms and the probabilities p as two: there the partials match the fp32
+path's to within the low term that p's split drops (below 2^-16 p a key),
+bounded per row by 2^-16 * l * max|V|.
 """
 import numpy as np
 import pytest
@@ -36,6 +37,27 @@ def _pages16(w, fmt, device="cuda"):
     kt = torch.from_numpy(k.view(np.int16)).to(device).view(TORCH16[fmt])
     vt = torch.from_numpy(v.view(np.int16)).to(device).view(TORCH16[fmt])
     return k, v, kt, vt
+
+
+def _assert_partials_match_fp32_path(fmt, rows, vdec, p16, p32):
+    """fp16 pages: bitwise the fp32 path's partials on the decoded pages.
+    bf16 pages: the scores carry q's 24 bits (three terms), so m and l agree
+    to fp32 rounding; o differs by at most the dropped part of p's two-term
+    split, below 2^-16 p for each key, so |o16 - o32| <= 2^-16 * l * max|V|
+    on every row (4x for the scores' own rounding)."""
+    o16, m16, l16 = (x[:rows] for x in p16)
+    o32, m32, l32 = (x[:rows] for x in p32)
+    if fmt == "fp16":
+        assert torch.equal(o16, o32) and torch.equal(m16, m32) and torch.equal(l16, l32)
+        return
+    o16, m16, l16, o32, m32, l32 = (x.cpu().double() for x in (o16, m16, l16, o32, m32, l32))
+    fin = torch.isfinite(m32)
+    assert torch.equal(fin, torch.isfinite(m16))
+    if fin.any():
+        assert (m16[fin] - m32[fin]).abs().max().item() <= 1e-5 * max(1.0, m32[fin].abs().max().item())
+    assert ((l16 - l32).abs() <= 1e-5 * l32.abs() + 1e-30).all()
+    bound = 4 * 2.0 ** -16 * l32 * float(np.abs(vdec).max())
+    assert ((o16 - o32).abs() <= bound[:, None] + 1e-30).all()
 
 
 def _fwd_args(w, d):
@@ -94,24 +116,8 @@ def test_kv16_partials_equal_fp32_path_on_decoded_pages(fmt, seed):
     vd = torch.from_numpy(oracle.decode_kv16(v, fmt)).cuda()
     o32, m32, l32 = sa.sa_forward(idx, d["q"], kd, vd, *_fwd_args(w, d))
     rows = sa.sa_index_status(idx)["total_edges"] * (w.hq // w.hkv)
-    if fmt == "fp16":
-        assert torch.equal(o16[:rows], o32[:rows])
-        assert torch.equal(m16[:rows], m32[:rows])
-        assert torch.equal(l16[:rows], l32[:rows])
-        return
-    # bf16 on the bf16 matrix cores: the scores carry q's 24 bits (three
-    # terms), so m and l agree to fp32 rounding; o differs by at most the
-    # dropped part of p's two-term split, below 2^-16 p for each key, so
-    # |o16 - o32| <= 2^-16 * l * max|V| on every row (4x for the scores'
-    # own rounding)
-    o16, m16, l16 = (x[:rows].cpu().double() for x in (o16, m16, l16))
-    o32, m32, l32 = (x[:rows].cpu().double() for x in (o32, m32, l32))
-    fin = torch.isfinite(m32)
-    assert torch.equal(fin, torch.isfinite(m16))
-    assert (m16[fin] - m32[fin]).abs().max().item() <= 1e-5 * max(1.0, m32[fin].abs().max().item())
-    assert ((l16 - l32).abs() <= 1e-5 * l32.abs() + 1e-30).all()
-    bound = 4 * 2.0 ** -16 * l32 * float(np.abs(oracle.decode_kv16(v, fmt)).max())
-    assert ((o16 - o32).abs() <= bound[:, None] + 1e-30).all()
+    _assert_partials_match_fp32_path(fmt, rows, oracle.decode_kv16(v, fmt), (o16, m16, l16),
+                                     (o32, m32, l32))
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp16"])
@@ -231,12 +237,12 @@ def test_other_kernels_kv16(fmt, case):
     out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
     kd, vd = oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt)
     _check(w, kd, vd, out, lse)
-    # and bitwise the fp32 path's partials on the decoded pages
+    # and the fp32 path's partials on the decoded pages (bitwise where the
+    # words are converted exactly)
     o32, m32, l32 = sa.sa_forward(idx, d["q"], torch.from_numpy(kd).cuda(),
                                   torch.from_numpy(vd).cuda(), *_fwd_args(w, d))
     rows = sa.sa_index_status(idx)["total_edges"] * (w.hq // w.hkv)
-    assert torch.equal(o[:rows], o32[:rows]) and torch.equal(m[:rows], m32[:rows])
-    assert torch.equal(l[:rows], l32[:rows])
+    _assert_partials_match_fp32_path(fmt, rows, vd, (o, m, l), (o32, m32, l32))
 
 
 def test_prefill_workload_bf16_sampled():
