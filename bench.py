@@ -41,7 +41,8 @@ sys.path.insert(0, ROOT)
 METRIC = "selected-block attention edges/s + effective TFLOP/s and HBM GB/s % of peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
-DEFAULT_CONFIG = "skewed"      # the largest workload (BASELINE configs: skewed long-context)
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+DEFAULT_CONFIG = "skewed"      # the largest workload that fits one GPU: skewed long-context
 
 
 def parse():
@@ -440,13 +441,16 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32", fused=False
     small, mfma = forward_kernels(w, fused, kv_dtype)
     if kv_dtype != "f32":
         small = small.replace(">", f", {kv_dtype}>")
-    ridge = FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    # bf16 pages run their main tiles on the bf16 matrix pipes: their peak
+    # (and ridge) is the bf16 one, against the algorithmic flops
+    mfma_peak = BF16_MFMA_PEAK_TFLOPS if kv_dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if fwd_flops / fwd_bytes < ridge:
         achieved, peak, unit, bound = fwd_bytes / fwd_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
         kernels = small if mfma is None else f"{small} + {mfma}"
         dominant = small
     else:
-        achieved, peak, unit, bound = fwd_flops / fwd_s / 1e12, FP32_MFMA_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        achieved, peak, unit, bound = fwd_flops / fwd_s / 1e12, mfma_peak, "TFLOP/s", "mfma"
         kernels = small if mfma is None else f"{mfma} + {small}"
         dominant = small if mfma is None else mfma
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
