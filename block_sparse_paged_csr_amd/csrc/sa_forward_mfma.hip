@@ -676,6 +676,85 @@ __device__ __forceinline__ void tile16_pv16(const uint16_t* sv, const float (&s)
   }
 }
 
+// 16-row tiles with bf16 words on v_mfma_f32_16x16x32_bf16. Scores: step t
+// (of four) takes K words d = 32t + 4g .. +3 and 32t + 16 + 4g .. +3 of the
+// lane's key row and q at the same d (q[2t], q[2t + 1]), split into three
+// terms once a step for all chunks.
+template <int NCH>
+__device__ __forceinline__ void tile16_scores_bf16(const uint16_t* sk, const float4 (&qr)[16], int li, int g,
+                                                   float (&s)[NCH][4]) {
+  floatx4 acc[NCH];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) acc[ch] = zero4v();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float x[8] = {qr[2 * t].x, qr[2 * t].y, qr[2 * t].z, qr[2 * t].w,
+                  qr[2 * t + 1].x, qr[2 * t + 1].y, qr[2 * t + 1].z, qr[2 * t + 1].w};
+    uint32_t w[3][4];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float h0 = bf16_trunc(x[2 * m]), h1 = bf16_trunc(x[2 * m + 1]);
+        w[k][m] = bf16_pack(h0, h1);
+        x[2 * m] -= h0;
+        x[2 * m + 1] -= h1;
+      }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int row = 16 * ch + li;
+      const uint2 wa = *reinterpret_cast<const uint2*>(&sk[swz16(row, 4 * t + (g >> 1)) + 4 * (g & 1)]);
+      const uint2 wb = *reinterpret_cast<const uint2*>(&sk[swz16(row, 4 * t + 2 + (g >> 1)) + 4 * (g & 1)]);
+      const bf16x8 kw = as_bf16x8(wa.x, wa.y, wb.x, wb.y);
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        acc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw, as_bf16x8(w[k][0], w[k][1], w[k][2], w[k][3]),
+                                                          acc[ch], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[ch][r] = acc[ch][r];
+}
+
+// O^T += V^T . P^T, 16-row tiles with bf16 words: element e of lane group g
+// stands for key 16ch + 4g + (e & 3), p's high term for e < 4 and its low
+// term for e >= 4 (V's word twice); output row i of block db stands for d =
+// 4i + (db & 3) + 64 (db >> 2), as in tile16_pv16.
+template <int NCH>
+__device__ __forceinline__ void tile16_pv_bf16(const uint16_t* sv, const float (&s)[NCH][4], int li, int g,
+                                               floatx4 (&oacc)[8]) {
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    uint2 w0[4], w1[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * ch + 4 * g + r;
+      w0[r] = *reinterpret_cast<const uint2*>(&sv[row * 128 + 4 * li]);
+      w1[r] = *reinterpret_cast<const uint2*>(&sv[row * 128 + 64 + 4 * li]);
+    }
+    float lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lo[r] = s[ch][r] - bf16_trunc(s[ch][r]);
+    const bf16x8 pw = as_bf16x8(bf16_pack(s[ch][0], s[ch][1]), bf16_pack(s[ch][2], s[ch][3]),
+                                bf16_pack(lo[0], lo[1]), bf16_pack(lo[2], lo[3]));
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      uint32_t wr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint2 x = db < 4 ? w0[r] : w1[r];
+        wr[r] = (db & 2) ? x.y : x.x;
+      }
+      const uint32_t v01 = (db & 1) ? (wr[0] >> 16) | (wr[1] & 0xffff0000u) : (wr[0] & 0xffffu) | (wr[1] << 16);
+      const uint32_t v23 = (db & 1) ? (wr[2] >> 16) | (wr[3] & 0xffff0000u) : (wr[2] & 0xffffu) | (wr[3] << 16);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v01, v23, v01, v23), pw,
+                                                         ch == 0 ? zero4v() : oacc[db], 0, 0, 0);
+    }
+  }
+}
+
 // A unit's rows in 16-row quanta, dealt to the four SIMDs of the workgroup in
 // near-equal contiguous shares (the unit ends when its largest share does).
 // A share of q quanta is q / 2 32-row tiles and, for odd q, one 16-row tile
@@ -1040,6 +1119,7 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
       float s16[2 * NKB][4];
       if constexpr (kF32) tile16_scores<2 * NKB>(s_k, qr, li, gq, s16);
+      else if constexpr (KVF == SA_KV_BF16) tile16_scores_bf16<2 * NKB>(reinterpret_cast<const uint16_t*>(s_k), qr, li, gq, s16);
       else tile16_scores16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, li, gq, s16);
       bool nq16 = false;
       const bool nq = next_q(sh.n32, nq16);
@@ -1048,6 +1128,7 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       tile16_softmax<2 * NKB>(s16, full, s_valid[j & 1], gq, kmax, c2, mb2, sum);
       floatx4 o16[8];
       if constexpr (kF32) tile16_pv<2 * NKB>(s_v, s16, li, gq, o16);
+      else if constexpr (KVF == SA_KV_BF16) tile16_pv_bf16<2 * NKB>(reinterpret_cast<const uint16_t*>(s_v), s16, li, gq, o16);
       else tile16_pv16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), s16, li, gq, o16);
       if (nq && !nq16) load_q_rest(qp, qr);
       if (row_ok) tile16_store(A, row0, row, gq, o16, mb2, sum);
