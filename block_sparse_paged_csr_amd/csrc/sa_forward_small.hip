@@ -120,66 +120,106 @@ __device__ inline floatx4 zero4() {
   return z;
 }
 
-// bf16 pages on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, the fused
-// decode forward): the K and V words enter the products as stored, and each
-// fp32 operand is written as a sum of bf16 terms by repeated truncation (q
-// three terms, which carry its 24 significand bits; p two terms, within
-// 2^-16 of it). A product of two bf16 values is exact in fp32 and the
-// products accumulate in fp32.
+// 16-bit pages on the 16-bit matrix cores (v_mfma_f32_16x16x32_bf16 / _f16):
+// the K and V words enter the products as stored, and each fp32 operand is
+// written as a sum of terms of the pages' format by repeated rounding toward
+// zero (q three terms, which carry its 24 significand bits; p two, within
+// 2^-16 of it). A product of two such terms is exact in fp32, and the
+// products accumulate in fp32. fp16 terms have a narrow range: a q row is
+// first scaled by a power of two 2^sx that brings its largest element into
+// [2^14, 2^15), and the scores take 2^-sx back in the factor that scales
+// them (exactly: a power of two). p lies in [0, 1].
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 __device__ inline float bf16_trunc(float x) { return __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
-// bf16 words of two values packed low half first
-__device__ inline uint32_t bf16_pack(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+// The word of the high terms of (x0, x1), low half first; x0 and x1 keep the
+// remainders (exact in fp32).
+template <int KVF>
+__device__ inline uint32_t split_pair(float& x0, float& x1) {
+  if constexpr (KVF == kKvBf16) {
+    const float h0 = bf16_trunc(x0), h1 = bf16_trunc(x1);
+    x0 -= h0;
+    x1 -= h1;
+    return (__float_as_uint(h0) >> 16) | (__float_as_uint(h1) & 0xffff0000u);
+  } else {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+    x0 -= (float)h[0];
+    x1 -= (float)h[1];
+    return __builtin_bit_cast(uint32_t, h);
+  }
 }
-__device__ inline bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return __builtin_bit_cast(bf16x8, uintx4{a, b, c, d});
+// D += A . B on 16x16x32 with 8 elements of the format a lane in each operand
+template <int KVF>
+__device__ inline floatx4 mfma16x16x32(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t b0,
+                                      uint32_t b1, uint32_t b2, uint32_t b3, floatx4 c) {
+  if constexpr (KVF == kKvBf16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, uintx4{a0, a1, a2, a3}),
+                                                   __builtin_bit_cast(bf16x8, uintx4{b0, b1, b2, b3}), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, uintx4{a0, a1, a2, a3}),
+                                                  __builtin_bit_cast(halfx8, uintx4{b0, b1, b2, b3}), c, 0, 0, 0);
 }
 // The q row in the B-operand layout (q[i]: d = 32 (i >> 1) + 8g + 4 (i & 1)
-// .. +3) as three bf16 terms; word 4t + m of term k holds d = 32t + 8g + 2m
-// and 2m + 1, the elements of the K words they meet.
-__device__ inline void split_q_bf16(const floatx4 (&q)[8], uint32_t (&qw)[3][16]) {
+// .. +3; lanes li, li + 16, li + 32, li + 48 hold row li) as three terms;
+// word 4t + m of term k holds d = 32t + 8g + 2m and 2m + 1, the elements of
+// the K words they meet. Returns the factor of the row's raw scores:
+// `scale` (bf16), or `scale` * 2^-sx (fp16, q scaled by 2^sx).
+template <int KVF>
+__device__ inline float split_q16(const floatx4 (&q)[8], uint32_t (&qw)[3][16], float scale) {
+  int sx = 0;
+  if constexpr (KVF == kKvF16) {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(q[i][c]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (mx > 0.f && mx <= 3.0e38f) {
+      int e;
+      (void)frexpf(mx, &e);                   // mx = f * 2^e, f in [0.5, 1)
+      sx = 15 - e;
+      sx = sx < -120 ? -120 : (sx > 120 ? 120 : sx);
+    }
+  }
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       float x0 = q[2 * t + (m >> 1)][2 * (m & 1)], x1 = q[2 * t + (m >> 1)][2 * (m & 1) + 1];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const float h0 = bf16_trunc(x0), h1 = bf16_trunc(x1);
-        qw[k][4 * t + m] = bf16_pack(h0, h1);
-        x0 -= h0;
-        x1 -= h1;
+      if constexpr (KVF == kKvF16) {
+        x0 = ldexpf(x0, sx);
+        x1 = ldexpf(x1, sx);
       }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) qw[k][4 * t + m] = split_pair<KVF>(x0, x1);
     }
+  return KVF == kKvF16 ? ldexpf(scale, -sx) : scale;
 }
-// Scores of a K piece of bf16 words, S^T = K . Q^T: lane (li, g), reg r holds
-// key 4g + r of the piece against row li. Element e of lane group g stands
-// for d = 32t + 8g + e on both operands.
-__device__ inline floatx4 scores_bf16(const PieceT<kKvBf16>& kp, const uint32_t (&qw)[3][16]) {
+// Raw scores of a K piece of 16-bit words, S^T = K . Q^T: lane (li, g), reg r
+// holds key 4g + r of the piece against row li. Element e of lane group g
+// stands for d = 32t + 8g + e on both operands.
+template <int KVF>
+__device__ inline floatx4 scores16(const PieceT<KVF>& kp, const uint32_t (&qw)[3][16]) {
   floatx4 s0 = zero4(), s1 = zero4(), s2 = zero4();
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const bf16x8 kw = as_bf16x8(kp.x[2 * t].x, kp.x[2 * t].y, kp.x[2 * t + 1].x, kp.x[2 * t + 1].y);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-        kw, as_bf16x8(qw[0][4 * t], qw[0][4 * t + 1], qw[0][4 * t + 2], qw[0][4 * t + 3]), s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-        kw, as_bf16x8(qw[1][4 * t], qw[1][4 * t + 1], qw[1][4 * t + 2], qw[1][4 * t + 3]), s1, 0, 0, 0);
-    s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-        kw, as_bf16x8(qw[2][4 * t], qw[2][4 * t + 1], qw[2][4 * t + 2], qw[2][4 * t + 3]), s2, 0, 0, 0);
+    const uint32_t k0 = kp.x[2 * t].x, k1 = kp.x[2 * t].y, k2 = kp.x[2 * t + 1].x, k3 = kp.x[2 * t + 1].y;
+    s0 = mfma16x16x32<KVF>(k0, k1, k2, k3, qw[0][4 * t], qw[0][4 * t + 1], qw[0][4 * t + 2], qw[0][4 * t + 3], s0);
+    s1 = mfma16x16x32<KVF>(k0, k1, k2, k3, qw[1][4 * t], qw[1][4 * t + 1], qw[1][4 * t + 2], qw[1][4 * t + 3], s1);
+    s2 = mfma16x16x32<KVF>(k0, k1, k2, k3, qw[2][4 * t], qw[2][4 * t + 1], qw[2][4 * t + 2], qw[2][4 * t + 3], s2);
   }
   return s0 + (s1 + s2);
 }
-// O^T += V^T . P^T for a V piece of bf16 words (row i of block db: d = 8i +
+// O^T += V^T . P^T for a V piece of 16-bit words (row i of block db: d = 8i +
 // db), p[r] the probability of key 4g + r for row li. Element e of lane
 // group g stands for key 4g + (e & 3): p's high term for e < 4, its low
 // term for e >= 4, V's word twice. `fresh`: the products start the sums.
-__device__ inline void pv_bf16(const PieceT<kKvBf16>& vp, const float (&p)[4], floatx4 (&oacc)[8], bool fresh) {
-  float lo[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) lo[r] = p[r] - bf16_trunc(p[r]);
-  const bf16x8 pw = as_bf16x8(bf16_pack(p[0], p[1]), bf16_pack(p[2], p[3]), bf16_pack(lo[0], lo[1]),
-                              bf16_pack(lo[2], lo[3]));
+template <int KVF>
+__device__ inline void pv16(const PieceT<KVF>& vp, const float (&p)[4], floatx4 (&oacc)[8], bool fresh) {
+  float x0 = p[0], x1 = p[1], x2 = p[2], x3 = p[3];
+  const uint32_t h01 = split_pair<KVF>(x0, x1), h23 = split_pair<KVF>(x2, x3);
+  const uint32_t l01 = split_pair<KVF>(x0, x1), l23 = split_pair<KVF>(x2, x3);
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     // V[key 4g + r][8li + db]: half (db & 1) of word (db >> 1) & 1 of group 2r + (db >> 2)
@@ -188,8 +228,7 @@ __device__ inline void pv_bf16(const PieceT<kKvBf16>& vp, const float (&p)[4], f
     for (int r = 0; r < 4; ++r) w[r] = (db & 2) ? vp.x[2 * r + (db >> 2)].y : vp.x[2 * r + (db >> 2)].x;
     const uint32_t v01 = (db & 1) ? (w[0] >> 16) | (w[1] & 0xffff0000u) : (w[0] & 0xffffu) | (w[1] << 16);
     const uint32_t v23 = (db & 1) ? (w[2] >> 16) | (w[3] & 0xffff0000u) : (w[2] & 0xffffu) | (w[3] << 16);
-    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v01, v23, v01, v23), pw,
-                                                       fresh ? zero4() : oacc[db], 0, 0, 0);
+    oacc[db] = mfma16x16x32<KVF>(v01, v23, v01, v23, h01, h23, l01, l23, fresh ? zero4() : oacc[db]);
   }
 }
 __device__ inline int32_t unit_keys(const Unit& U, int32_t block_size) {
@@ -363,7 +402,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     floatx4 oacc[8];
     float m_row = -INFINITY, l_row = 0.f;
     int32_t pre_rec = 0, pre_page = 0, pre_qi = 0;
-    uint32_t qw[KVF == kKvBf16 ? 3 : 1][16];      // bf16 pages: this unit's q as bf16 terms
+    uint32_t qw[KVF != kKvF32 ? 3 : 1][16];      // 16-bit pages: this unit's q as terms of the format
+    float c2q = A.scale_log2;                    // the factor of the raw scores
 
     auto step = [&](auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
@@ -387,9 +427,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         if constexpr (k < NCH) {
           // ---- scores of piece k: S^T = K . Q^T
           floatx4 s;                      // lane (li, g), reg r: key 16k + 4g + r, row li
-          if constexpr (KVF == kKvBf16) {
-            if constexpr (k == 0) split_q_bf16(qreg, qw);
-            s = scores_bf16(cur, qw);
+          if constexpr (KVF != kKvF32) {
+            if constexpr (k == 0) c2q = split_q16<KVF>(qreg, qw, A.scale_log2);
+            s = scores16<KVF>(cur, qw);
           } else {
             floatx4 sa0 = zero4(), sa1 = zero4();
 #pragma unroll
@@ -407,7 +447,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           for (int r = 0; r < 4; ++r) {
             const int key = kPiece * k + 4 * g + r;
             const bool alive = row_ok && ((vm >> key) & 1ull) && key <= kmax;
-            sreg[k][r] = alive ? s[r] * A.scale_log2 : -INFINITY;
+            sreg[k][r] = alive ? s[r] * c2q : -INFINITY;
           }
           if constexpr (k == NCH - 1) {
             // ---- softmax of row li over the whole block (base 2)
@@ -435,8 +475,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         } else {
           // ---- O^T += V^T . P^T for piece c (row i of block db: d = 8i + db)
           constexpr int c = k - NCH;
-          if constexpr (KVF == kKvBf16) {
-            pv_bf16(cur, sreg[c], oacc, c == 0);
+          if constexpr (KVF != kKvF32) {
+            pv16<KVF>(cur, sreg[c], oacc, c == 0);
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -664,8 +704,9 @@ __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_e
   }
   // bf16 pages: the q row as three bf16 terms; word 4t + m of term k holds
   // d = 32t + 8g + 2m and 2m + 1, the elements of the K words it meets
-  uint32_t qw[KVF == kKvBf16 ? 3 : 1][16];
-  if constexpr (KVF == kKvBf16) split_q_bf16(qreg, qw);
+  uint32_t qw[KVF != kKvF32 ? 3 : 1][16];
+  float c2q = A.scale_log2;          // the factor of the raw scores
+  if constexpr (KVF != kKvF32) c2q = split_q16<KVF>(qreg, qw, A.scale_log2);
   block_meta(0, 0);
   Piece bufA, bufB;
   load_piece(IC<0>{}, 0, n_blk > 0, bufA);
@@ -703,8 +744,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_e
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (j < NCH) {
           floatx4 s;                      // lane (li, g), reg r: key 16j + 4g + r, row li
-          if constexpr (KVF == kKvBf16) {
-            s = scores_bf16(cur, qw);
+          if constexpr (KVF != kKvF32) {
+            s = scores16<KVF>(cur, qw);
           } else {
             floatx4 sa0 = zero4(), sa1 = zero4();
 #pragma unroll
@@ -722,7 +763,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_e
           for (int r = 0; r < 4; ++r) {
             const int key = kPiece * j + 4 * g + r;
             const bool alive = row_ok && ((vm >> key) & 1ull) && key <= kmax;
-            sreg[j][r] = alive ? s[r] * A.scale_log2 : -INFINITY;
+            sreg[j][r] = alive ? s[r] * c2q : -INFINITY;
           }
           if constexpr (j == NCH - 1) {
             // ---- the block's maximum joins the running one; rescale O and L
@@ -755,8 +796,8 @@ __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_e
           }
         } else {
           constexpr int c = j - NCH;
-          if constexpr (KVF == kKvBf16) {
-            pv_bf16(cur, sreg[c], oacc, false);
+          if constexpr (KVF != kKvF32) {
+            pv16<KVF>(cur, sreg[c], oacc, false);
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
