@@ -390,133 +390,105 @@ __device__ __forceinline__ void tile16_store(const FwdArgs& A, int64_t row0, int
 // operand read of the 32-row tiles covers one whole row, and its addresses
 // then fold into immediate offsets; the 16-row tiles' reads of rows four
 // apart meet in the same banks, a 2-way conflict, which measured cheaper
-// than forming swizzled V addresses). Each word becomes its exact fp32 value
-// as it enters the matrix cores, in the order the fp32 tiles use, so both
-// formats give the same bits on the same values.
+// than forming swizzled V addresses). The words go to the 16-bit matrix
+// cores as they are (below).
 __device__ __forceinline__ int swz16(int row, int chunk) { return row * 128 + ((chunk ^ (row & 15)) << 3); }
 
-template <int KVF>
-__device__ __forceinline__ float4 cvt4(uint32_t lo, uint32_t hi) {
-  return make_float4(kv16_to_f32<KVF>(lo & 0xffffu), kv16_to_f32<KVF>(lo >> 16), kv16_to_f32<KVF>(hi & 0xffffu),
-                     kv16_to_f32<KVF>(hi >> 16));
-}
 
-// tile_scores: chunk half*8 + p of the lane's key row holds d = half*64 + 8p .. +7,
-// the operands of steps 2p and 2p + 1.
-template <int NKB, int KVF>
-__device__ __forceinline__ void tile_scores16(const uint16_t* sk, const float4 (&qr)[16], int lr, int half,
-                                              floatx16 (&sacc)[NKB]) {
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
-  uint4 kc[NKB];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) kc[kb] = *reinterpret_cast<const uint4*>(&sk[swz16(kb * 32 + lr, half * 8)]);
-  __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    uint4 kn[NKB];
-    if (p < 7) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        kn[kb] = *reinterpret_cast<const uint4*>(&sk[swz16(kb * 32 + lr, half * 8 + p + 1)]);
-    }
-    // the step's operands converted first, then its products (each
-    // accumulator takes them in the fp32 tiles' order)
-    float4 klo[NKB], khi[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      klo[kb] = cvt4<KVF>(kc[kb].x, kc[kb].y);
-      khi[kb] = cvt4<KVF>(kc[kb].z, kc[kb].w);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x0002, 8 * NKB, 0);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const float4 q = qr[2 * p + sub];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float4 k = sub == 0 ? klo[kb] : khi[kb];
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.x, q.x, sacc[kb], 0, 0, 0);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.y, q.y, sacc[kb], 0, 0, 0);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.z, q.z, sacc[kb], 0, 0, 0);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k.w, q.w, sacc[kb], 0, 0, 0);
-      }
-    }
-    if (p < 7) __builtin_amdgcn_sched_group_barrier(0x0100, NKB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x0008, 8 * NKB, 0);
-    if (p < 7) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
-    }
-  }
-}
 
-// tile_pv: lane lr reads words 4 phi(lr) .. + 3 of a key row, with
-// phi(8g + 4h + c) = 8g + 2c + h (g, c < 4, h < 2), so output row m of MFMA
-// block db stands for d = 4 phi(m) + db: the rows that lanes lr and lr + 32
-// hold side by side are adjacent d, and each store of tile_store16 writes 32
-// contiguous bytes of a row, as the fp32 tiles' stores do.
-__device__ __forceinline__ int pv16_word(int lr) { return 4 * (8 * (lr >> 3) + 2 * (lr & 3) + ((lr >> 2) & 1)); }
-template <int NKB, int KVF>
-__device__ __forceinline__ void tile_pv16(const uint16_t* sv, const floatx16 (&sacc)[NKB], int lr, int half,
-                                          floatx16 (&oacc)[4]) {
-#pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = zero16();
-  uint2 vc[2];
-  auto read_v = [&](int r0, uint2 (&dst)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = r0 + j, kb = r / 16, rr = r % 16;
-      const int key = kb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4);
-      dst[j] = *reinterpret_cast<const uint2*>(&sv[key * 128 + pv16_word(lr)]);
-    }
-  };
-  read_v(0, vc);
-  __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
-#pragma unroll
-  for (int r0 = 0; r0 < 16 * NKB; r0 += 2) {
-    uint2 vn[2];
-    if (r0 + 2 < 16 * NKB) read_v(r0 + 2, vn);
-    const float4 v0 = cvt4<KVF>(vc[0].x, vc[0].y), v1 = cvt4<KVF>(vc[1].x, vc[1].y);
-    __builtin_amdgcn_sched_group_barrier(0x0002, 8, 0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float4 v = j == 0 ? v0 : v1;
-      const float p = sacc[(r0 + j) / 16][(r0 + j) % 16];
-      oacc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.x, p, oacc[0], 0, 0, 0);
-      oacc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.y, p, oacc[1], 0, 0, 0);
-      oacc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.z, p, oacc[2], 0, 0, 0);
-      oacc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(v.w, p, oacc[3], 0, 0, 0);
-    }
-    if (r0 + 2 < 16 * NKB) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x0008, 8, 0);
-    if (r0 + 2 < 16 * NKB) {
-      vc[0] = vn[0];
-      vc[1] = vn[1];
-    }
-  }
-}
 
-// bf16 pages on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16): the K and
-// V words enter the products as stored, and each fp32 operand is written as
-// a sum of bf16 terms by repeated truncation (q three terms, which carry its
-// 24 significand bits; p two, within 2^-16 of it). A product of two bf16
-// values is exact in fp32, and the products accumulate in fp32.
+// 16-bit pages on the 16-bit matrix cores (v_mfma_f32_32x32x16_bf16 / _f16
+// and the 16x16x32 forms): the K and V words enter the products as stored,
+// and each fp32 operand is written as a sum of terms of the pages' format by
+// repeated rounding toward zero (q three terms, which carry its 24
+// significand bits; p two, within 2^-16 of it). A product of two such terms
+// is exact in fp32, and the products accumulate in fp32. fp16 terms have a
+// narrow range: a tile's q row is first scaled by a power of two 2^sx that
+// brings its largest element into [2^14, 2^15), and the row's score factor
+// takes 2^-sx back (exactly: a power of two). p lies in [0, 1].
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef unsigned int uintx4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float bf16_trunc(float x) { return __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
-__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+// The word of the high terms of (x0, x1), low half first; x0 and x1 keep the
+// remainders (exact in fp32).
+template <int KVF>
+__device__ __forceinline__ uint32_t split_pair(float& x0, float& x1) {
+  if constexpr (KVF == SA_KV_BF16) {
+    const float h0 = __uint_as_float(__float_as_uint(x0) & 0xffff0000u);
+    const float h1 = __uint_as_float(__float_as_uint(x1) & 0xffff0000u);
+    x0 -= h0;
+    x1 -= h1;
+    return (__float_as_uint(h0) >> 16) | (__float_as_uint(h1) & 0xffff0000u);
+  } else {
+    const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+    x0 -= (float)h[0];
+    x1 -= (float)h[1];
+    return __builtin_bit_cast(uint32_t, h);
+  }
 }
-__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return __builtin_bit_cast(bf16x8, uintx4v{a, b, c, d});
+template <int KVF>
+__device__ __forceinline__ floatx16 mfma32x32x16(uintx4v a, uintx4v b, const floatx16& c) {
+  if constexpr (KVF == SA_KV_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c,
+                                                  0, 0, 0);
+}
+template <int KVF>
+__device__ __forceinline__ floatx4 mfma16x16x32(uintx4v a, uintx4v b, const floatx4& c) {
+  if constexpr (KVF == SA_KV_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, b), c,
+                                                  0, 0, 0);
+}
+// The power of two 2^sx that fp16 terms take the q row in (0 for bf16): a
+// 32-row tile holds the row in lanes lr and lr + 32 (qr[0..15]), a 16-row
+// tile in lanes li + 16g (qr[0..7]).
+template <int KVF, bool k16>
+__device__ __forceinline__ int q_row_exp(const float4 (&qr)[16]) {
+  if constexpr (KVF != SA_KV_F16) {
+    return 0;
+  } else {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < (k16 ? 8 : 16); ++i)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(qr[i].x), fabsf(qr[i].y)), fmaxf(fabsf(qr[i].z), fabsf(qr[i].w))));
+    if (k16) mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    int sx = 0;
+    if (mx > 0.f && mx <= 3.0e38f) {
+      int e;
+      (void)frexpf(mx, &e);                     // mx = f * 2^e, f in [0.5, 1)
+      sx = 15 - e;
+      sx = sx < -120 ? -120 : (sx > 120 ? 120 : sx);
+    }
+    return sx;
+  }
+}
+// q values (x0..x7) as three terms of the format, words m of term t
+template <int KVF>
+__device__ __forceinline__ void split_q8(float (&x)[8], int sx, uint32_t (&w)[3][4]) {
+  if constexpr (KVF == SA_KV_F16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = ldexpf(x[e], sx);
+  }
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[t][m] = split_pair<KVF>(x[2 * m], x[2 * m + 1]);
 }
 
-// S^T = K . Q^T with bf16 K words: step p takes chunk half*8 + p of the lane's
-// key row (d = half*64 + 8p .. +7, the k slots of the lane's half) and the
-// same d of q, split into three terms at the step.
-template <int NKB>
-__device__ __forceinline__ void tile_scores_bf16(const uint16_t* sk, const float4 (&qr)[16], int lr, int half,
-                                                 floatx16 (&sacc)[NKB]) {
+// S^T = K . Q^T with 16-bit K words: step p takes chunk half*8 + p of the
+// lane's key row (d = half*64 + 8p .. +7, the k slots of the lane's half) and
+// the same d of q, split into three terms at the step. Returns the row's
+// score factor (c2, times 2^-sx for fp16).
+template <int NKB, int KVF>
+__device__ __forceinline__ float tile_scores_m16(const uint16_t* sk, const float4 (&qr)[16], int lr, int half,
+                                                 floatx16 (&sacc)[NKB], float c2) {
+  const int sx = q_row_exp<KVF, false>(qr);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) sacc[kb] = zero16();
   uint4 kc[NKB];
@@ -533,38 +505,36 @@ __device__ __forceinline__ void tile_scores_bf16(const uint16_t* sk, const float
     float x[8] = {qr[2 * p].x, qr[2 * p].y, qr[2 * p].z, qr[2 * p].w,
                   qr[2 * p + 1].x, qr[2 * p + 1].y, qr[2 * p + 1].z, qr[2 * p + 1].w};
     uint32_t w[3][4];
-#pragma unroll
-    for (int t = 0; t < 3; ++t)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float h0 = bf16_trunc(x[2 * m]), h1 = bf16_trunc(x[2 * m + 1]);
-        w[t][m] = bf16_pack(h0, h1);
-        x[2 * m] -= h0;
-        x[2 * m + 1] -= h1;
-      }
+    split_q8<KVF>(x, sx, w);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 k = as_bf16x8(kc[kb].x, kc[kb].y, kc[kb].z, kc[kb].w);
+      const uintx4v k{kc[kb].x, kc[kb].y, kc[kb].z, kc[kb].w};
 #pragma unroll
       for (int t = 0; t < 3; ++t)
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, as_bf16x8(w[t][0], w[t][1], w[t][2], w[t][3]),
-                                                           sacc[kb], 0, 0, 0);
+        sacc[kb] = mfma32x32x16<KVF>(k, uintx4v{w[t][0], w[t][1], w[t][2], w[t][3]}, sacc[kb]);
     }
     if (p < 7) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) kc[kb] = kn[kb];
     }
   }
+  return KVF == SA_KV_F16 ? ldexpf(c2, -sx) : c2;
 }
 
-// O^T = V^T . P^T with bf16 V words. Step (kb, u) takes the lane's
+// tile_pv: lane lr reads words 4 phi(lr) .. + 3 of a key row, with
+// phi(8g + 4h + c) = 8g + 2c + h (g, c < 4, h < 2), so output row m of MFMA
+// block db stands for d = 4 phi(m) + db: the rows that lanes lr and lr + 32
+// hold side by side are adjacent d, and each store of tile_store16 writes 32
+// contiguous bytes of a row, as the fp32 tiles' stores do.
+__device__ __forceinline__ int pv16_word(int lr) { return 4 * (8 * (lr >> 3) + 2 * (lr & 3) + ((lr >> 2) & 1)); }
+
+// O^T = V^T . P^T with 16-bit V words. Step (kb, u) takes the lane's
 // accumulators 8u .. 8u + 7 of block kb: element e stands for key kb*32 +
 // 16u + 8(e/4) + 4half + e%4 on both operands (p, split into two terms, and
-// the V words of those keys at the lane's words 4 phi(lr) .. +3, as in
-// tile_pv16, so tile_store16 writes the result).
-template <int NKB>
-__device__ __forceinline__ void tile_pv_bf16(const uint16_t* sv, const floatx16 (&sacc)[NKB], int lr, int half,
-                                             floatx16 (&oacc)[4]) {
+// the V words of those keys at the lane's words 4 phi(lr) .. +3).
+template <int NKB, int KVF>
+__device__ __forceinline__ void tile_pv_m16(const uint16_t* sv, const floatx16 (&sacc)[NKB], int lr, int half,
+                                            floatx16 (&oacc)[4]) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = zero16();
   const int word = pv16_word(lr);
@@ -583,11 +553,11 @@ __device__ __forceinline__ void tile_pv_bf16(const uint16_t* sv, const floatx16 
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const float a = sacc[kb][8 * u + 2 * m], b = sacc[kb][8 * u + 2 * m + 1];
-      ph[m] = bf16_pack(a, b);
-      pl[m] = bf16_pack(a - bf16_trunc(a), b - bf16_trunc(b));
+      float a = sacc[kb][8 * u + 2 * m], b = sacc[kb][8 * u + 2 * m + 1];
+      ph[m] = split_pair<KVF>(a, b);
+      pl[m] = split_pair<KVF>(a, b);
     }
-    const bf16x8 phi = as_bf16x8(ph[0], ph[1], ph[2], ph[3]), plo = as_bf16x8(pl[0], pl[1], pl[2], pl[3]);
+    const uintx4v phi{ph[0], ph[1], ph[2], ph[3]}, plo{pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       // word db of key e's four: half db & 1 of .x (db < 2) or .y
@@ -597,9 +567,9 @@ __device__ __forceinline__ void tile_pv_bf16(const uint16_t* sv, const floatx16 
         const uint32_t w0 = db < 2 ? vc[2 * m].x : vc[2 * m].y, w1 = db < 2 ? vc[2 * m + 1].x : vc[2 * m + 1].y;
         a[m] = (db & 1) ? (w0 >> 16) | (w1 & 0xffff0000u) : (w0 & 0xffffu) | (w1 << 16);
       }
-      const bf16x8 v = as_bf16x8(a[0], a[1], a[2], a[3]);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, phi, oacc[db], 0, 0, 0);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, plo, oacc[db], 0, 0, 0);
+      const uintx4v v{a[0], a[1], a[2], a[3]};
+      oacc[db] = mfma32x32x16<KVF>(v, phi, oacc[db]);
+      oacc[db] = mfma32x32x16<KVF>(v, plo, oacc[db]);
     }
     if (st + 1 < 2 * NKB) {
 #pragma unroll
@@ -625,64 +595,16 @@ __device__ __forceinline__ void tile_store16(const FwdArgs& A, int64_t row0, int
   }
 }
 
-// 16-row tiles: K words d = 16t + 4g .. +3 and V words 4li .. 4li + 3 (and + 64)
-// of their key rows, the fp32 tiles' operands.
-template <int NCH, int KVF>
-__device__ __forceinline__ void tile16_scores16(const uint16_t* sk, const float4 (&qr)[16], int li, int g,
-                                                float (&s)[NCH][4]) {
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    floatx4 sa0 = zero4v(), sa1 = zero4v();
-    const int row = 16 * ch + li;
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-      const uint2 wa = *reinterpret_cast<const uint2*>(&sk[swz16(row, 2 * t + (g >> 1)) + 4 * (g & 1)]);
-      const uint2 wb = *reinterpret_cast<const uint2*>(&sk[swz16(row, 2 * (t + 1) + (g >> 1)) + 4 * (g & 1)]);
-      const float4 ka = cvt4<KVF>(wa.x, wa.y), kb = cvt4<KVF>(wb.x, wb.y);
-      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.x, qr[t].x, sa0, 0, 0, 0);
-      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.x, qr[t + 1].x, sa1, 0, 0, 0);
-      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.y, qr[t].y, sa0, 0, 0, 0);
-      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.y, qr[t + 1].y, sa1, 0, 0, 0);
-      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.z, qr[t].z, sa0, 0, 0, 0);
-      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.z, qr[t + 1].z, sa1, 0, 0, 0);
-      sa0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka.w, qr[t].w, sa0, 0, 0, 0);
-      sa1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kb.w, qr[t + 1].w, sa1, 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);   // bound how far LDS reads run ahead
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[ch][r] = sa0[r] + sa1[r];
-  }
-}
 
-template <int NCH, int KVF>
-__device__ __forceinline__ void tile16_pv16(const uint16_t* sv, const float (&s)[NCH][4], int li, int g,
-                                            floatx4 (&oacc)[8]) {
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * ch + 4 * g + r;
-      const uint2 w0 = *reinterpret_cast<const uint2*>(&sv[row * 128 + 4 * li]);
-      const uint2 w1 = *reinterpret_cast<const uint2*>(&sv[row * 128 + 64 + 4 * li]);
-      const float4 a = cvt4<KVF>(w0.x, w0.y), b = cvt4<KVF>(w1.x, w1.y);
-      const float v0[4] = {a.x, a.y, a.z, a.w}, v1[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const floatx4 acc = (ch == 0 && r == 0) ? zero4v() : oacc[db];
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(db < 4 ? v0[db & 3] : v1[db & 3], s[ch][r], acc, 0, 0, 0);
-      }
-      if (r & 1) __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-}
 
-// 16-row tiles with bf16 words on v_mfma_f32_16x16x32_bf16. Scores: step t
-// (of four) takes K words d = 32t + 4g .. +3 and 32t + 16 + 4g .. +3 of the
+// 16-row tiles with 16-bit words on the 16x16x32 form. Scores: step t (of
+// four) takes K words d = 32t + 4g .. +3 and 32t + 16 + 4g .. +3 of the
 // lane's key row and q at the same d (q[2t], q[2t + 1]), split into three
-// terms once a step for all chunks.
-template <int NCH>
-__device__ __forceinline__ void tile16_scores_bf16(const uint16_t* sk, const float4 (&qr)[16], int li, int g,
-                                                   float (&s)[NCH][4]) {
+// terms once a step for all chunks. Returns the row's score factor.
+template <int NCH, int KVF>
+__device__ __forceinline__ float tile16_scores_m16(const uint16_t* sk, const float4 (&qr)[16], int li, int g,
+                                                   float (&s)[NCH][4], float c2) {
+  const int sx = q_row_exp<KVF, true>(qr);
   floatx4 acc[NCH];
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) acc[ch] = zero4v();
@@ -691,40 +613,31 @@ __device__ __forceinline__ void tile16_scores_bf16(const uint16_t* sk, const flo
     float x[8] = {qr[2 * t].x, qr[2 * t].y, qr[2 * t].z, qr[2 * t].w,
                   qr[2 * t + 1].x, qr[2 * t + 1].y, qr[2 * t + 1].z, qr[2 * t + 1].w};
     uint32_t w[3][4];
-#pragma unroll
-    for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float h0 = bf16_trunc(x[2 * m]), h1 = bf16_trunc(x[2 * m + 1]);
-        w[k][m] = bf16_pack(h0, h1);
-        x[2 * m] -= h0;
-        x[2 * m + 1] -= h1;
-      }
+    split_q8<KVF>(x, sx, w);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int row = 16 * ch + li;
       const uint2 wa = *reinterpret_cast<const uint2*>(&sk[swz16(row, 4 * t + (g >> 1)) + 4 * (g & 1)]);
       const uint2 wb = *reinterpret_cast<const uint2*>(&sk[swz16(row, 4 * t + 2 + (g >> 1)) + 4 * (g & 1)]);
-      const bf16x8 kw = as_bf16x8(wa.x, wa.y, wb.x, wb.y);
+      const uintx4v kw{wa.x, wa.y, wb.x, wb.y};
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
-        acc[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw, as_bf16x8(w[k][0], w[k][1], w[k][2], w[k][3]),
-                                                          acc[ch], 0, 0, 0);
+      for (int k = 0; k < 3; ++k) acc[ch] = mfma16x16x32<KVF>(kw, uintx4v{w[k][0], w[k][1], w[k][2], w[k][3]}, acc[ch]);
     }
   }
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[ch][r] = acc[ch][r];
+  return KVF == SA_KV_F16 ? ldexpf(c2, -sx) : c2;
 }
 
-// O^T += V^T . P^T, 16-row tiles with bf16 words: element e of lane group g
-// stands for key 16ch + 4g + (e & 3), p's high term for e < 4 and its low
+// O^T += V^T . P^T, 16-row tiles with 16-bit words: element e of lane group
+// g stands for key 16ch + 4g + (e & 3), p's high term for e < 4 and its low
 // term for e >= 4 (V's word twice); output row i of block db stands for d =
-// 4i + (db & 3) + 64 (db >> 2), as in tile16_pv16.
-template <int NCH>
-__device__ __forceinline__ void tile16_pv_bf16(const uint16_t* sv, const float (&s)[NCH][4], int li, int g,
-                                               floatx4 (&oacc)[8]) {
+// 4i + (db & 3) + 64 (db >> 2).
+template <int NCH, int KVF>
+__device__ __forceinline__ void tile16_pv_m16(const uint16_t* sv, const float (&s)[NCH][4], int li, int g,
+                                              floatx4 (&oacc)[8]) {
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
     uint2 w0[4], w1[4];
@@ -734,11 +647,10 @@ __device__ __forceinline__ void tile16_pv_bf16(const uint16_t* sv, const float (
       w0[r] = *reinterpret_cast<const uint2*>(&sv[row * 128 + 4 * li]);
       w1[r] = *reinterpret_cast<const uint2*>(&sv[row * 128 + 64 + 4 * li]);
     }
-    float lo[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lo[r] = s[ch][r] - bf16_trunc(s[ch][r]);
-    const bf16x8 pw = as_bf16x8(bf16_pack(s[ch][0], s[ch][1]), bf16_pack(s[ch][2], s[ch][3]),
-                                bf16_pack(lo[0], lo[1]), bf16_pack(lo[2], lo[3]));
+    float x0 = s[ch][0], x1 = s[ch][1], x2 = s[ch][2], x3 = s[ch][3];
+    const uint32_t h01 = split_pair<KVF>(x0, x1), h23 = split_pair<KVF>(x2, x3);
+    const uint32_t l01 = split_pair<KVF>(x0, x1), l23 = split_pair<KVF>(x2, x3);
+    const uintx4v pw{h01, h23, l01, l23};
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       uint32_t wr[4];
@@ -749,8 +661,7 @@ __device__ __forceinline__ void tile16_pv_bf16(const uint16_t* sv, const float (
       }
       const uint32_t v01 = (db & 1) ? (wr[0] >> 16) | (wr[1] & 0xffff0000u) : (wr[0] & 0xffffu) | (wr[1] << 16);
       const uint32_t v23 = (db & 1) ? (wr[2] >> 16) | (wr[3] & 0xffff0000u) : (wr[2] & 0xffffu) | (wr[3] << 16);
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v01, v23, v01, v23), pw,
-                                                         ch == 0 ? zero4v() : oacc[db], 0, 0, 0);
+      oacc[db] = mfma16x16x32<KVF>(uintx4v{v01, v23, v01, v23}, pw, ch == 0 ? zero4v() : oacc[db]);
     }
   }
 }
@@ -1088,19 +999,18 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       const int32_t kmaxh = (int32_t)(klim < -1 ? -1 : klim) - 4 * half;
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
       floatx16 sacc[NKB];
+      float c2t = c2;                  // the row's score factor
       if constexpr (kF32) tile_scores<NKB>(s_k, qr, lr, half, sacc);
-      else if constexpr (KVF == SA_KV_BF16) tile_scores_bf16<NKB>(reinterpret_cast<const uint16_t*>(s_k), qr, lr, half, sacc);
-      else tile_scores16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, lr, half, sacc);
+      else c2t = tile_scores_m16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, lr, half, sacc, c2);
       // ---- the first half of the next q rows (all of them for a 16-row tile)
       bool nq16 = false;
       const bool nq = next_q(p, nq16);
       if (nq) load_q_first(qp, nq16, qr);
       float mb2, sum;
-      tile_softmax<NKB, true>(sacc, full, s_valid[j & 1], half, kmaxh, c2, mb2, sum);
+      tile_softmax<NKB, true>(sacc, full, s_valid[j & 1], half, kmaxh, c2t, mb2, sum);
       floatx16 oacc[kD / 32];
       if constexpr (kF32) tile_pv<NKB>(s_v, sacc, lr, half, oacc);
-      else if constexpr (KVF == SA_KV_BF16) tile_pv_bf16<NKB>(reinterpret_cast<const uint16_t*>(s_v), sacc, lr, half, oacc);
-      else tile_pv16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), sacc, lr, half, oacc);
+      else tile_pv_m16<NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), sacc, lr, half, oacc);
       // the second half, before the stores (a wait for a load also waits
       // for every store issued before it)
       if (nq && !nq16) load_q_rest(qp, qr);
@@ -1118,18 +1028,17 @@ __global__ __launch_bounds__(512) void k_fwd_mfma_dma(IndexPtrs P, FwdArgs A) {
       const int32_t kmax = (int32_t)(klim < -1 ? -1 : klim);
       const bool full = __all(!row_ok || klim >= kKeys - 1) && all_rows;
       float s16[2 * NKB][4];
+      float c2t = c2;                  // the row's score factor
       if constexpr (kF32) tile16_scores<2 * NKB>(s_k, qr, li, gq, s16);
-      else if constexpr (KVF == SA_KV_BF16) tile16_scores_bf16<2 * NKB>(reinterpret_cast<const uint16_t*>(s_k), qr, li, gq, s16);
-      else tile16_scores16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, li, gq, s16);
+      else c2t = tile16_scores_m16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_k), qr, li, gq, s16, c2);
       bool nq16 = false;
       const bool nq = next_q(sh.n32, nq16);
       if (nq) load_q_first(qp, nq16, qr);
       float mb2, sum;
-      tile16_softmax<2 * NKB>(s16, full, s_valid[j & 1], gq, kmax, c2, mb2, sum);
+      tile16_softmax<2 * NKB>(s16, full, s_valid[j & 1], gq, kmax, c2t, mb2, sum);
       floatx4 o16[8];
       if constexpr (kF32) tile16_pv<2 * NKB>(s_v, s16, li, gq, o16);
-      else if constexpr (KVF == SA_KV_BF16) tile16_pv_bf16<2 * NKB>(reinterpret_cast<const uint16_t*>(s_v), s16, li, gq, o16);
-      else tile16_pv16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), s16, li, gq, o16);
+      else tile16_pv_m16<2 * NKB, KVF>(reinterpret_cast<const uint16_t*>(s_v), s16, li, gq, o16);
       if (nq && !nq16) load_q_rest(qp, qr);
       if (row_ok) tile16_store(A, row0, row, gq, o16, mb2, sum);
     }

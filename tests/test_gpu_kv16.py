@@ -9,10 +9,10 @@ On the same index, the 16-bit forward and the fp32 forward on the decoded
 values give bitwise identical partials where the kernel converts each word
 exactly to fp32 (same arithmetic on the same fp32 operands). The one-wave
 and fused kernels (head_dim 128, blocks of at most 64 keys, at most 16
-rows a unit) instead run both formats on the 16-bit matrix cores, and the
-direct-to-LDS MFMA kernel (blocks of 65..128 keys) runs bf16 there: q as
-three terms of the format (fp16: after a power-of-two row scale) and the
-probabilities p as two. There the partials match the fp32 path's to
+rows a unit) and the direct-to-LDS MFMA kernel (blocks of 65..128 keys)
+instead run both formats on the 16-bit matrix cores: q as three terms of
+the format (fp16: after a power-of-two row scale) and the probabilities p
+as two. There the partials match the fp32 path's to
 within the low part that p's split drops (below 2^-16 p a key), bounded
 per row by 2^-16 * l * max|V|.
 """
@@ -246,8 +246,10 @@ def test_other_kernels_kv16(fmt, case):
     o32, m32, l32 = sa.sa_forward(idx, d["q"], torch.from_numpy(kd).cuda(),
                                   torch.from_numpy(vd).cuda(), *_fwd_args(w, d))
     rows = sa.sa_index_status(idx)["total_edges"] * (w.hq // w.hkv)
-    # (fp16 words convert exactly in these kernels)
-    _assert_partials_match_fp32_path(fmt, rows, vd, (o, m, l), (o32, m32, l32), exact=fmt == "fp16")
+    # (fp16 words convert exactly in these kernels, but for the direct-to-LDS
+    # MFMA kernel's: head_dim 128, blocks of 65..128 keys)
+    exact = fmt == "fp16" and not (w.head_dim == 128 and 64 < w.block_size <= 128)
+    _assert_partials_match_fp32_path(fmt, rows, vd, (o, m, l), (o32, m32, l32), exact=exact)
 
 
 def test_prefill_workload_bf16_sampled():
