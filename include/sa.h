@@ -200,13 +200,13 @@ sa_status sa_forward(const sa_index* idx,
                      hipStream_t stream);
 
 /* Storage formats of K/V pages for sa_forward_kv16 and
- * sa_forward_combine_kv16. The pages define fp32 pages only. 16-bit storage
- * is converted exactly to fp32 where it is used, except that bf16 pages of
- * the one-wave kernels (head_dim 128, blocks of at most 64 keys, units of at
- * most 16 rows, and the fused forward) are multiplied on the bf16 matrix
- * cores as stored, with q written as three bf16 terms and the probabilities
- * as two; either way the tolerance is the fp32 path's on the stored
- * values. */
+ * sa_forward_combine_kv16. The pages define fp32 pages only. Where head_dim
+ * is 128 and blocks hold at most 128 keys (the one-wave, fused and
+ * direct-to-LDS kernels) the 16-bit words are multiplied on the 16-bit
+ * matrix cores as stored, with q written as three terms of the format (fp16:
+ * after a power-of-two scale of its row) and the probabilities as two;
+ * elsewhere each word is converted exactly to fp32. Either way the
+ * tolerance is the fp32 path's on the stored values. */
 typedef enum sa_kv_format {
   SA_KV_F32 = 0,   /* float32 (sa_forward) */
   SA_KV_BF16 = 1,  /* bfloat16: the top 16 bits of an IEEE binary32 */
