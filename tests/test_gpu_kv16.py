@@ -197,6 +197,40 @@ def test_decode_workload_fused_kv16_bf16():
     print(f"[gpu case] fused kv16 decode bf16: O rel err {err:.3e}", flush=True)
 
 
+# The 16-bit matrix-core paths split q into terms of the format; fp16 terms
+# need q's rows scaled by a power of two first. q far above fp16's range
+# (x 2e4: elements past 65504) and far below its normal range (x 1e-3:
+# many elements under 2^-14), with K scaled the other way so that the
+# scores stay of order one, against the oracle on the one-wave, fused and
+# direct-to-LDS kernels.
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+@pytest.mark.parametrize("scales", [(2e4, 5e-5), (1e-3, 1e3)])
+@pytest.mark.parametrize("kernel", ["small", "fused", "mfma"])
+def test_kv16_q_far_from_unit_range(fmt, scales, kernel):
+    kernels = ["small", "fused", "mfma"]
+    geo = {"small": dict(qo_max=12, page_size=16, pages_per_block=4, qhead=8),
+           "fused": dict(qo_max=1, page_size=16, pages_per_block=2, qhead=4),
+           "mfma": dict(qo_max=60, page_size=32, pages_per_block=4, qhead=8)}[kernel]
+    q_scale, k_scale = scales
+    w = W.make_random(4700 + 2 * kernels.index(kernel) + int(q_scale > 1), batch=3, kv_max=600,
+                      hkv=2, head_dim=128, topk=4, causal=True, **geo)
+    w.q = (w.q.astype(np.float64) * q_scale).astype(np.float32)
+    w.k_pages = (w.k_pages.astype(np.float64) * k_scale).astype(np.float32)
+    print(f"[gpu case] kv16 q range {fmt} q x{q_scale:g} k x{k_scale:g} {kernel} tq={w.tq} "
+          f"bs={w.block_size}", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, fmt)
+    idx = run_index(w, d)
+    n_mfma = sa.sa_index_status(idx)["num_units_mfma"]
+    assert (n_mfma > 0) == (kernel == "mfma"), n_mfma
+    if kernel == "fused":
+        out, lse = sa.sa_forward_combine_kv16(idx, d["sel"], d["q"], kt, vt, *_fwd_args(w, d))
+    else:
+        o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+        out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    _check(w, oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt), out, lse)
+
+
 def test_ragged_workload_bf16_sampled():
     w = W.make_config("ragged")
     print("[gpu case] kv16 ragged bf16", flush=True)
