@@ -21,6 +21,8 @@
 //   O^T[d, row] += V[key, d] * P[row, key]  output row i of MFMA block db stands for
 //                                           d = 8i + db
 // Every d is taken once on both sides, so the sums are those of the method.
+// With 16-bit pages the pieces keep their words, and the products run on the
+// 16-bit matrix cores (v_mfma_f32_16x16x32_bf16 / _f16, helpers below).
 // Latency: the next piece (the next unit's first K piece at the end of a unit)
 // is in flight while a piece computes, and the next unit's query rows load
 // during the V pieces. Unit metadata runs further ahead through small per-wave
@@ -69,7 +71,7 @@ struct WaveLds {
 };
 
 // K/V storage formats: fp32 as the pages define them, or 16-bit storage
-// (bf16 / IEEE fp16) converted exactly to fp32 where it is used.
+// (bf16 / IEEE fp16), multiplied as stored on the 16-bit matrix cores.
 enum KvFormat : int { kKvF32 = SA_KV_F32, kKvBf16 = SA_KV_BF16, kKvF16 = SA_KV_F16 };
 
 typedef const __attribute__((address_space(1))) uint16_t gu16;
@@ -95,18 +97,8 @@ struct PieceT<kKvF16> {
   uintx2 x[8];
 };
 
-// Element c of group i as fp32 (exact for every format).
-template <int KVF>
-__device__ inline float kv_elem(const PieceT<KVF>& pc, int i, int c) {
-  if constexpr (KVF == kKvF32) {
-    return pc.x[i][c];
-  } else {
-    const uint32_t w = c < 2 ? pc.x[i].x : pc.x[i].y;
-    const uint32_t h = (c & 1) ? (w >> 16) : (w & 0xffffu);
-    if constexpr (KVF == kKvBf16) return __uint_as_float(h << 16);
-    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-  }
-}
+// Element c of group i of an fp32 piece.
+__device__ inline float kv_elem(const PieceT<kKvF32>& pc, int i, int c) { return pc.x[i][c]; }
 
 template <int N>
 using IC = std::integral_constant<int, N>;
