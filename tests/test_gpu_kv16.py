@@ -231,6 +231,46 @@ def test_kv16_q_far_from_unit_range(fmt, scales, kernel):
     _check(w, oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt), out, lse)
 
 
+# Rows of one tile at very different scales (each q row times 10^u, u
+# uniform in [-3, 4]): every row takes its own power of two on the fp16 path.
+# Large rows give near-hard softmaxes with lse up to ~1e4, so lse is compared
+# relative to its size; O to 1e-4 of max|O| as everywhere.
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+@pytest.mark.parametrize("kernel", ["small", "fused", "mfma"])
+def test_kv16_q_rows_of_mixed_scale(fmt, kernel):
+    kernels = ["small", "fused", "mfma"]
+    geo = {"small": dict(qo_max=12, page_size=16, pages_per_block=4, qhead=8),
+           "fused": dict(qo_max=1, page_size=16, pages_per_block=2, qhead=4),
+           "mfma": dict(qo_max=60, page_size=32, pages_per_block=4, qhead=8)}[kernel]
+    w = W.make_random(4720 + kernels.index(kernel), batch=3, kv_max=600, hkv=2, head_dim=128,
+                      topk=4, causal=True, **geo)
+    rng = np.random.default_rng(4730 + kernels.index(kernel))
+    row_scale = 10.0 ** rng.uniform(-3.0, 4.0, size=w.q.shape[:2])
+    w.q = (w.q.astype(np.float64) * row_scale[:, :, None]).astype(np.float32)
+    print(f"[gpu case] kv16 mixed row scales {fmt} {kernel} tq={w.tq} bs={w.block_size}", flush=True)
+    d = dev_inputs(w)
+    k, v, kt, vt = _pages16(w, fmt)
+    idx = run_index(w, d)
+    n_mfma = sa.sa_index_status(idx)["num_units_mfma"]
+    assert (n_mfma > 0) == (kernel == "mfma"), n_mfma
+    if kernel == "fused":
+        out, lse = sa.sa_forward_combine_kv16(idx, d["sel"], d["q"], kt, vt, *_fwd_args(w, d))
+    else:
+        o, m, l = sa.sa_forward_kv16(idx, d["q"], kt, vt, *_fwd_args(w, d))
+        out, lse = sa.sa_combine(idx, o, m, l, w.hq, w.head_dim)
+    ref_o, ref_lse = oracle.attention_qo_ref(
+        w.q, oracle.decode_kv16(k, fmt), oracle.decode_kv16(v, fmt), w.selected, w.block_tables,
+        w.cu_seqlens_q, w.used_kv_lens, w.hq, w.hkv, w.head_dim, w.block_size, w.page_size,
+        w.softmax_scale, w.causal)
+    got_o = out.cpu().numpy().astype(np.float64)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert max_rel_err(got_o, ref_o)[0] <= TOL_O
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(got_lse))
+    if fin.any():
+        assert (np.abs(got_lse[fin] - ref_lse[fin]) <= TOL_LSE + 1e-6 * np.abs(ref_lse[fin])).all()
+
+
 def test_ragged_workload_bf16_sampled():
     w = W.make_config("ragged")
     print("[gpu case] kv16 ragged bf16", flush=True)
