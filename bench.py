@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "selected-block attention edges/s + effective TFLOP/s and HBM GB/s % of peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix
 DEFAULT_CONFIG = "skewed"      # the largest workload that fits one GPU: skewed long-context
 
 
@@ -381,7 +381,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the matrix operands' type: fp32, or the pages' 16-bit format (q and
+        # the probabilities as sums of its terms, fp32 accumulation)
+        "dtype": "f32" if args.kv_dtype == "f32" else args.kv_dtype,
         "data": "synthetic",
         "config": {**base.describe(), "kv_dtype": args.kv_dtype,
                    "edges_per_batch": int(np.mean([p["edges"] for p in per])),
@@ -441,9 +443,10 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32", fused=False
     small, mfma = forward_kernels(w, fused, kv_dtype)
     if kv_dtype != "f32":
         small = small.replace(">", f", {kv_dtype}>")
-    # bf16 pages run their main tiles on the bf16 matrix pipes: their peak
-    # (and ridge) is the bf16 one, against the algorithmic flops
-    mfma_peak = BF16_MFMA_PEAK_TFLOPS if kv_dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    # 16-bit pages run their main tiles on the 16-bit matrix pipes (bf16 and
+    # fp16 share one dense peak): that peak (and ridge), against the
+    # algorithmic flops
+    mfma_peak = BF16_MFMA_PEAK_TFLOPS if kv_dtype in ("bf16", "fp16") else FP32_MFMA_PEAK_TFLOPS
     ridge = mfma_peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if fwd_flops / fwd_bytes < ridge:
         achieved, peak, unit, bound = fwd_bytes / fwd_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
