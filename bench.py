@@ -451,7 +451,8 @@ def forward_roofline(w, fwd_bytes, fwd_flops, fwd_s, kv_dtype="f32", fused=False
     if fwd_flops / fwd_bytes < ridge:
         achieved, peak, unit, bound = fwd_bytes / fwd_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
         kernels = small if mfma is None else f"{small} + {mfma}"
-        dominant = small
+        # where an MFMA kernel runs, it takes nearly all of the forward's time
+        dominant = small if mfma is None else mfma
     else:
         achieved, peak, unit, bound = fwd_flops / fwd_s / 1e12, mfma_peak, "TFLOP/s", "mfma"
         kernels = small if mfma is None else f"{mfma} + {small}"
